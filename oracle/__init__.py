@@ -1,0 +1,182 @@
+"""CPU oracle for canonical reduction and canonical inclusive scan.
+
+TEST INFRASTRUCTURE.  This package is the slow, literal statement of what the
+GPU library computes, and is used only to check it: by the tests, by the
+package's smoke check and by the benchmark's CPU-baseline leg.  The GPU path
+never imports it, and it imports nothing from the GPU path.
+
+Two independent implementations live here:
+
+* ``canon_oracle.c`` (numeric, loaded through ctypes): the pairwise tree PW is
+  evaluated literally bottom-up, the two-stage reduction gathers the lanes
+  i mod L explicitly, and scans either evaluate one prefix from scratch
+  (``scan_prefix``) or every prefix with the shift-reduce stack (``scan``).
+* ``symbolic.py`` (pure Python): builds the expression tree itself from a
+  different formulation (split at the largest power of two below n), prints it
+  and evaluates it in exact IEEE arithmetic of the requested type.
+
+The semantics follow the canonical-reduce README (sections "P4016R0 —
+Canonical Parallel Reduction" and "P4229R0 — Canonical Parallel Scan").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = [os.path.join(_HERE, "canon_oracle.c"), os.path.join(_HERE, "canon_oracle_body.h")]
+
+POLICIES = {"pairwise": 0, "iterated_pairwise": 1, "block_dyadic": 2}
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = _SO + ".tmp"
+    cmd = ["gcc", *CFLAGS, "-o", tmp, os.path.join(_HERE, "canon_oracle.c")]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        S = ctypes.c_size_t
+        U = ctypes.c_uint32
+        I = ctypes.c_int
+        for sfx, ct in (("f64", ctypes.c_double), ("f32", ctypes.c_float)):
+            f = getattr(L, f"oracle_pw_{sfx}"); f.argtypes = [P, S, P]; f.restype = I
+            f = getattr(L, f"oracle_lane_values_{sfx}"); f.argtypes = [P, S, U, P]; f.restype = S
+            f = getattr(L, f"oracle_cr_{sfx}"); f.argtypes = [P, S, U, P]; f.restype = I
+            f = getattr(L, f"oracle_reduce_{sfx}"); f.argtypes = [P, S, U, ct]; f.restype = ct
+            f = getattr(L, f"oracle_scan_prefix_{sfx}"); f.argtypes = [P, S, I, U, P]; f.restype = I
+            f = getattr(L, f"oracle_scan_{sfx}"); f.argtypes = [P, P, S, I, U]; f.restype = I
+            f = getattr(L, f"oracle_reduce_rows_{sfx}"); f.argtypes = [P, S, S, S, U, ct, P]; f.restype = None
+            f = getattr(L, f"oracle_scan_rows_{sfx}"); f.argtypes = [P, S, P, S, S, S, I, U]; f.restype = I
+        _lib = L
+    return _lib
+
+
+def _sfx(a: np.ndarray) -> str:
+    if a.dtype == np.float64:
+        return "f64"
+    if a.dtype == np.float32:
+        return "f32"
+    raise TypeError(f"oracle supports float64/float32, got {a.dtype}")
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.ndim != 1:
+        a = a.reshape(-1)
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def pw(s: np.ndarray):
+    """PW(s) as a numpy scalar of s's dtype, or None for an empty sequence."""
+    s = _c(s)
+    out = np.zeros(1, s.dtype)
+    ok = getattr(lib(), f"oracle_pw_{_sfx(s)}")(_ptr(s), s.size, _ptr(out))
+    return out[0] if ok else None
+
+
+def lane_values(x: np.ndarray, L: int) -> np.ndarray:
+    """[PW(lane 0), ..., PW(lane m-1)], m = min(n, L)."""
+    x = _c(x)
+    out = np.zeros(max(min(x.size, L), 1), x.dtype)
+    m = getattr(lib(), f"oracle_lane_values_{_sfx(x)}")(_ptr(x), x.size, L, _ptr(out))
+    return out[:m]
+
+
+def cr(x: np.ndarray, L: int):
+    """CR_L(x) (the two-stage expression without init), or None if empty."""
+    x = _c(x)
+    out = np.zeros(1, x.dtype)
+    ok = getattr(lib(), f"oracle_cr_{_sfx(x)}")(_ptr(x), x.size, L, _ptr(out))
+    return out[0] if ok else None
+
+
+def reduce(x: np.ndarray, L: int, init=0.0):
+    """init + CR_L(x); init when x is empty.  Returns a numpy scalar."""
+    x = _c(x)
+    f = getattr(lib(), f"oracle_reduce_{_sfx(x)}")
+    return x.dtype.type(f(_ptr(x), x.size, L, x.dtype.type(init)))
+
+
+def _policy(policy) -> int:
+    return POLICIES[policy] if isinstance(policy, str) else int(policy)
+
+
+def _check_param(policy: int, param: int) -> None:
+    if policy in (1, 2) and param < 1:
+        raise ValueError("iterated_pairwise / block_dyadic need param >= 1")
+
+
+def scan_prefix(x: np.ndarray, i: int, policy, param: int = 0):
+    """Value of the policy's expression on x[0..i], evaluated from scratch."""
+    x = _c(x)
+    p = _policy(policy)
+    _check_param(p, param)
+    out = np.zeros(1, x.dtype)
+    ok = getattr(lib(), f"oracle_scan_prefix_{_sfx(x)}")(_ptr(x), i, p, param, _ptr(out))
+    if not ok:
+        raise ValueError("bad scan arguments")
+    return out[0]
+
+
+def scan(x: np.ndarray, policy, param: int = 0) -> np.ndarray:
+    """Every prefix of x under the policy (streaming shift-reduce form)."""
+    x = _c(x)
+    p = _policy(policy)
+    _check_param(p, param)
+    y = np.empty_like(x)
+    ok = getattr(lib(), f"oracle_scan_{_sfx(x)}")(_ptr(x), _ptr(y), x.size, p, param)
+    if not ok:
+        raise ValueError("bad scan arguments")
+    return y
+
+
+def reduce_rows(X: np.ndarray, L: int, init=0.0, cols: int | None = None) -> np.ndarray:
+    """Per-row reduce of a 2-D array (rows are independent sequences).
+
+    ``cols`` may be smaller than X.shape[1]; X.shape[1] is then the row pitch.
+    """
+    X = np.ascontiguousarray(X)
+    rows, ld = X.shape
+    cols = ld if cols is None else cols
+    out = np.empty(rows, X.dtype)
+    getattr(lib(), f"oracle_reduce_rows_{_sfx(X)}")(
+        _ptr(X), rows, cols, ld, L, X.dtype.type(init), _ptr(out))
+    return out
+
+
+def scan_rows(X: np.ndarray, policy, param: int = 0, cols: int | None = None) -> np.ndarray:
+    """Per-row scan of a 2-D array; entries past ``cols`` in a row are left 0."""
+    X = np.ascontiguousarray(X)
+    rows, ld = X.shape
+    cols = ld if cols is None else cols
+    p = _policy(policy)
+    _check_param(p, param)
+    Y = np.zeros_like(X)
+    ok = getattr(lib(), f"oracle_scan_rows_{_sfx(X)}")(
+        _ptr(X), ld, _ptr(Y), ld, rows, cols, p, param)
+    if not ok:
+        raise ValueError("bad scan arguments")
+    return Y
