@@ -1,0 +1,155 @@
+/*
+ * canon.h — canonical (reproducible) parallel reduction and inclusive scan on
+ * AMD MI355X (gfx950).  C ABI of libcanon.
+ *
+ * What is computed (canonical-reduce README: "P4016R0 — Canonical Parallel
+ * Reduction" > "Key Design Points"; "P4229R0 — Canonical Parallel Scan" >
+ * "Summary" and "Key Design Points"):
+ *
+ *   PW(s)            the iterative pairwise tree over a sequence s: pair
+ *                    neighbours (s0+s1)(s2+s3)..., carry an odd trailing
+ *                    element up unchanged, repeat until one value is left.
+ *   CR_L(x[0..n))    element i goes to lane i mod L; each lane is reduced by
+ *                    PW in index order; the lane values are combined by PW in
+ *                    lane order.  Lanes that hold no element (n < L) take no
+ *                    part.
+ *   reduce           init + CR_L(x): init is combined once, on the left, after
+ *                    the tree; the result is init itself when n == 0.
+ *   scan<E>(x)[i]    the value of expression E over the prefix x[0..i]:
+ *                      CANON_PAIRWISE           E = PW
+ *                      CANON_ITERATED_PAIRWISE  E = CR_L, L = param
+ *                      CANON_BLOCK_DYADIC       E(n) = PW(PW(block 0), ...,
+ *                                               PW(block q-1)) + PW(tail),
+ *                                               n = qB + t, 0 <= t < B,
+ *                                               B = param (a power of two);
+ *                                               an empty part is left out.
+ *                    Hence scan<E>(x)[n-1] == reduce<E>(x[0..n)) bit for bit.
+ *
+ * The results are bit-identical for every input of a given (n, L) or
+ * (policy, param), whatever the launch shape, GPU or run: the library
+ * evaluates exactly the expression above (IEEE-754 binary64 / binary32
+ * additions, round to nearest even, no contraction into FMA, subnormals
+ * kept).  Only NaN payloads are not specified.
+ *
+ * Conventions for every entry point:
+ *   - Array arguments (x, y, out, ws) are DEVICE pointers on the current HIP
+ *     device.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Work is enqueued on `stream` and the call returns at once.
+ *   - Elements are contiguous (the row functions take a row pitch `ld` in
+ *     elements).  Any element alignment is accepted; 16-byte aligned data
+ *     with a 16-byte aligned row pitch takes the fastest path.
+ *   - The caller owns every buffer.  `ws` is scratch device memory of at
+ *     least the size returned by the matching *_workspace_bytes function
+ *     (which may be 0; ws may then be NULL).  It must be 256-byte aligned.
+ *     Its contents on entry are ignored and on exit unspecified; calls that
+ *     may run concurrently must not share a workspace.
+ *   - Argument errors are detected before anything is enqueued and return
+ *     CANON_EINVAL (bad pointer / size / parameter), CANON_EUNSUPPORTED
+ *     (parameter beyond the supported range) or CANON_EWORKSPACE (workspace
+ *     too small or misaligned).  A failed launch returns CANON_EHIP and
+ *     keeps the HIP error code for canon_last_hip_error().  Device faults
+ *     surface at the caller's next synchronisation.  The library never
+ *     prints and holds no device memory between calls.
+ */
+#ifndef CANON_H
+#define CANON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CANON_ABI_VERSION 1
+
+/* Largest lane count L for reduce and iterated_pairwise, and largest block
+ * size B for block_dyadic.  Larger values return CANON_EUNSUPPORTED. */
+#define CANON_MAX_L 65536u
+#define CANON_MAX_B 65536u
+
+typedef enum {
+    CANON_OK = 0,
+    CANON_EINVAL = 1,
+    CANON_EUNSUPPORTED = 2,
+    CANON_EWORKSPACE = 3,
+    CANON_EHIP = 4
+} canon_status_t;
+
+typedef enum {
+    CANON_PAIRWISE = 0,          /* param must be 0 or 1 */
+    CANON_ITERATED_PAIRWISE = 1, /* param = L, 1 <= L <= CANON_MAX_L */
+    CANON_BLOCK_DYADIC = 2       /* param = B, power of two, 1 <= B <= CANON_MAX_B */
+} canon_policy_t;
+
+/* ABI version of the loaded library (CANON_ABI_VERSION). */
+int canon_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* canon_status_str(int status);
+
+/* HIP error code of the last CANON_EHIP returned on this thread (0 if none). */
+int canon_last_hip_error(void);
+
+/* ---------------------------------------------------------------- reduce */
+/* out[0] = init + CR_L(x[0..n)), or init when n == 0.
+ *   x     device, n elements (may be NULL when n == 0)
+ *   L     lane count, 1 <= L <= CANON_MAX_L
+ *   out   device, one element; written on `stream`
+ * Source: P4016R0 "Key Design Points" (lanes i mod L, pairwise tree per lane,
+ * lanes combined by the same rule, op(init, R)). */
+size_t canon_reduce_workspace_bytes(size_t n, uint32_t L, size_t elem_size);
+canon_status_t canon_reduce_f64(const double* x, size_t n, uint32_t L, double init, double* out,
+                                void* ws, size_t ws_bytes, void* stream);
+canon_status_t canon_reduce_f32(const float* x, size_t n, uint32_t L, float init, float* out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Row-batched reduce: row r is the sequence x[r*ldx + 0 .. r*ldx + cols);
+ * out[r] = init + CR_L(row r) (init when cols == 0).
+ *   x     device, rows x ldx elements (ldx >= cols)
+ *   out   device, `rows` elements */
+size_t canon_reduce_rows_workspace_bytes(size_t rows, size_t cols, uint32_t L, size_t elem_size);
+canon_status_t canon_reduce_rows_f64(const double* x, size_t rows, size_t cols, size_t ldx,
+                                     uint32_t L, double init, double* out, void* ws,
+                                     size_t ws_bytes, void* stream);
+canon_status_t canon_reduce_rows_f32(const float* x, size_t rows, size_t cols, size_t ldx,
+                                     uint32_t L, float init, float* out, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ scan */
+/* y[i] = value of the policy's expression over x[0..i], for i < n.
+ * Source: P4229R0 "Summary" (policies) and "Key Design Points" (reduce
+ * observes the root, scan observes the prefixes).
+ *   x, y  device, n elements each; y == x (in place) is allowed, any other
+ *         overlap is undefined. */
+size_t canon_scan_workspace_bytes(size_t n, int policy, uint32_t param, size_t elem_size);
+canon_status_t canon_scan_f64(const double* x, double* y, size_t n, int policy, uint32_t param,
+                              void* ws, size_t ws_bytes, void* stream);
+canon_status_t canon_scan_f32(const float* x, float* y, size_t n, int policy, uint32_t param,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Row-batched scan: every row is an independent sequence of `cols` elements;
+ * y[r*ldy + i] = scan<E>(row r)[i].  ldx, ldy >= cols; y == x with ldy == ldx
+ * is allowed. */
+size_t canon_scan_rows_workspace_bytes(size_t rows, size_t cols, int policy, uint32_t param,
+                                       size_t elem_size);
+canon_status_t canon_scan_rows_f64(const double* x, size_t ldx, double* y, size_t ldy,
+                                   size_t rows, size_t cols, int policy, uint32_t param,
+                                   void* ws, size_t ws_bytes, void* stream);
+canon_status_t canon_scan_rows_f32(const float* x, size_t ldx, float* y, size_t ldy,
+                                   size_t rows, size_t cols, int policy, uint32_t param,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* -------------------------------------------------------------- checking */
+/* The single-pass scans wait on values published by earlier workgroups with
+ * a bounded spin; if a bound is ever exceeded the kernel stops waiting,
+ * records a nonzero word at the start of the workspace and finishes (the
+ * output is then invalid).  This call copies that word to *err_out and
+ * synchronises `stream`.  0 means no error. */
+canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CANON_H */

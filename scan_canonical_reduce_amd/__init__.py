@@ -1,0 +1,227 @@
+"""Python binding of libcanon: canonical reduce and scan on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libcanon.so`` (built in-tree by ``scan_canonical_reduce_amd.build``);
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: if the library is missing or a tensor is not on the GPU the calls
+raise.
+
+The C ABI is declared in ``include/canon.h``; the functions here have the
+same names without the ``canon_`` prefix:
+
+    reduce(x, L, init)                 -> 0-d tensor, init + CR_L(x)
+    scan(x, policy, param=0)           -> tensor of prefix values
+    reduce_rows(X, L, init)            -> 1-d tensor, one value per row
+    scan_rows(X, policy, param=0)      -> tensor shaped like X
+
+``policy`` is "pairwise", "iterated_pairwise" (param = L) or "block_dyadic"
+(param = B, a power of two).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcanon.so")
+
+POLICIES = {"pairwise": 0, "iterated_pairwise": 1, "block_dyadic": 2}
+STATUS = {0: "CANON_OK", 1: "CANON_EINVAL", 2: "CANON_EUNSUPPORTED", 3: "CANON_EWORKSPACE",
+          4: "CANON_EHIP"}
+
+EXPORTS = [
+    "canon_abi_version", "canon_status_str", "canon_last_hip_error",
+    "canon_reduce_workspace_bytes", "canon_reduce_f64", "canon_reduce_f32",
+    "canon_reduce_rows_workspace_bytes", "canon_reduce_rows_f64", "canon_reduce_rows_f32",
+    "canon_scan_workspace_bytes", "canon_scan_f64", "canon_scan_f32",
+    "canon_scan_rows_workspace_bytes", "canon_scan_rows_f64", "canon_scan_rows_f32",
+    "canon_workspace_error",
+]
+
+_lib = None
+
+
+class CanonError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcanon.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise CanonError(f"{LIB_PATH} is missing: build it with "
+                         "`python -m scan_canonical_reduce_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, U, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int
+    D, F = ctypes.c_double, ctypes.c_float
+    L.canon_abi_version.restype = I
+    L.canon_status_str.argtypes = [I]
+    L.canon_status_str.restype = ctypes.c_char_p
+    L.canon_last_hip_error.restype = I
+    L.canon_reduce_workspace_bytes.argtypes = [S, U, S]
+    L.canon_reduce_workspace_bytes.restype = S
+    L.canon_reduce_f64.argtypes = [P, S, U, D, P, P, S, P]
+    L.canon_reduce_f32.argtypes = [P, S, U, F, P, P, S, P]
+    L.canon_reduce_rows_workspace_bytes.argtypes = [S, S, U, S]
+    L.canon_reduce_rows_workspace_bytes.restype = S
+    L.canon_reduce_rows_f64.argtypes = [P, S, S, S, U, D, P, P, S, P]
+    L.canon_reduce_rows_f32.argtypes = [P, S, S, S, U, F, P, P, S, P]
+    L.canon_scan_workspace_bytes.argtypes = [S, I, U, S]
+    L.canon_scan_workspace_bytes.restype = S
+    L.canon_scan_f64.argtypes = [P, P, S, I, U, P, S, P]
+    L.canon_scan_f32.argtypes = [P, P, S, I, U, P, S, P]
+    L.canon_scan_rows_workspace_bytes.argtypes = [S, S, I, U, S]
+    L.canon_scan_rows_workspace_bytes.restype = S
+    L.canon_scan_rows_f64.argtypes = [P, S, P, S, S, S, I, U, P, S, P]
+    L.canon_scan_rows_f32.argtypes = [P, S, P, S, S, S, I, U, P, S, P]
+    L.canon_workspace_error.argtypes = [P, ctypes.POINTER(U), P]
+    for name in EXPORTS:
+        if name not in ("canon_abi_version", "canon_status_str", "canon_last_hip_error") and \
+                not name.endswith("workspace_bytes"):
+            getattr(L, name).restype = I
+    if L.canon_abi_version() != 1:
+        raise CanonError("libcanon ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status == 0:
+        return
+    msg = lib().canon_status_str(status).decode()
+    if status == 4:
+        msg += f" (hip error {lib().canon_last_hip_error()})"
+    if status in (1, 2, 3):
+        raise ValueError(f"{what}: {msg}")
+    raise CanonError(f"{what}: {msg}")
+
+
+def _sfx(t: torch.Tensor) -> str:
+    if t.dtype == torch.float64:
+        return "f64"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"canonical reduce/scan take float64 or float32, not {t.dtype}")
+
+
+def _need_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (no CPU path)")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _policy(p) -> int:
+    if isinstance(p, str):
+        return POLICIES[p]
+    return int(p)
+
+
+def _ws(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def reduce_workspace_bytes(n: int, L: int, elem_size: int) -> int:
+    return lib().canon_reduce_workspace_bytes(n, L, elem_size)
+
+
+def scan_workspace_bytes(n: int, policy, param: int, elem_size: int) -> int:
+    return lib().canon_scan_workspace_bytes(n, _policy(policy), param, elem_size)
+
+
+def reduce(x: torch.Tensor, L: int, init: float = 0.0, out: torch.Tensor | None = None,
+           ws: torch.Tensor | None = None) -> torch.Tensor:
+    """init + CR_L(x) as a 0-d tensor on x's device (init when x is empty)."""
+    _need_gpu(x)
+    if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
+        raise ValueError("reduce takes a contiguous 1-d tensor")
+    sfx = _sfx(x)
+    if out is None:
+        out = torch.empty((), dtype=x.dtype, device=x.device)
+    nb = lib().canon_reduce_workspace_bytes(x.numel(), L, x.element_size())
+    w = _ws(nb, x.device, ws)
+    st = getattr(lib(), f"canon_reduce_{sfx}")(
+        _ptr(x), x.numel(), L, float(init), out.data_ptr(), _ptr(w), nb if w is None else w.numel(),
+        _stream())
+    _check(st, "reduce")
+    return out
+
+
+def scan(x: torch.Tensor, policy="pairwise", param: int = 0, out: torch.Tensor | None = None,
+         ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Prefix values of the policy's expression; out may be x (in place)."""
+    _need_gpu(x)
+    if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
+        raise ValueError("scan takes a contiguous 1-d tensor")
+    sfx = _sfx(x)
+    if out is None:
+        out = torch.empty_like(x)
+    p = _policy(policy)
+    nb = lib().canon_scan_workspace_bytes(x.numel(), p, param, x.element_size())
+    w = _ws(nb, x.device, ws)
+    st = getattr(lib(), f"canon_scan_{sfx}")(
+        _ptr(x), out.data_ptr(), x.numel(), p, param, _ptr(w), nb if w is None else w.numel(),
+        _stream())
+    _check(st, "scan")
+    return out
+
+
+def _rows_view(X: torch.Tensor):
+    if X.dim() != 2 or (X.numel() > 0 and X.stride(1) != 1):
+        raise ValueError("row functions take a 2-d tensor with unit column stride")
+    rows, cols = X.shape
+    ld = X.stride(0) if rows > 1 else max(cols, 1)
+    return rows, cols, ld
+
+
+def reduce_rows(X: torch.Tensor, L: int, init: float = 0.0,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """One canonical reduce per row of a 2-d tensor."""
+    _need_gpu(X)
+    sfx = _sfx(X)
+    rows, cols, ld = _rows_view(X)
+    if out is None:
+        out = torch.empty(rows, dtype=X.dtype, device=X.device)
+    st = getattr(lib(), f"canon_reduce_rows_{sfx}")(
+        _ptr(X), rows, cols, ld, L, float(init), out.data_ptr(), None, 0, _stream())
+    _check(st, "reduce_rows")
+    return out
+
+
+def scan_rows(X: torch.Tensor, policy="pairwise", param: int = 0,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """One canonical scan per row of a 2-d tensor."""
+    _need_gpu(X)
+    sfx = _sfx(X)
+    rows, cols, ldx = _rows_view(X)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=X.dtype, device=X.device)
+    _, _, ldy = _rows_view(out)
+    p = _policy(policy)
+    st = getattr(lib(), f"canon_scan_rows_{sfx}")(
+        _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, None, 0, _stream())
+    _check(st, "scan_rows")
+    return out
+
+
+def workspace_error(ws: torch.Tensor) -> int:
+    """The error word a single-pass scan left in its workspace (synchronises)."""
+    v = ctypes.c_uint32(0)
+    _check(lib().canon_workspace_error(ws.data_ptr(), ctypes.byref(v), _stream()),
+           "workspace_error")
+    return v.value

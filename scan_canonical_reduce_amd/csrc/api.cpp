@@ -1,0 +1,277 @@
+// libcanon C ABI: argument checking, workspace sizing, launch planning.
+//
+// Every entry point validates its arguments before anything is enqueued,
+// then enqueues its kernels on the caller's stream and returns.  The library
+// keeps no device memory and no state between calls, apart from the
+// thread-local HIP error code of the last failed launch.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/canon.h"
+#include "reduce.hpp"
+#include "scan.hpp"
+
+using namespace canon;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr uint64_t kReduceTargetWG = 256;  // one streaming workgroup per MI355X CU
+constexpr size_t kWsAlign = 256;
+
+bool is_pow2(uint64_t v) { return v && !(v & (v - 1)); }
+
+int log2_exact(uint64_t v)
+{
+    int l = 0;
+    while ((1ull << l) < v) ++l;
+    return l;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+canon_status_t hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return CANON_OK;
+    g_last_hip_error = (int)e;
+    return CANON_EHIP;
+}
+
+canon_status_t check_ws(const void* ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0) return CANON_OK;
+    if (ws == nullptr || ws_bytes < need) return CANON_EWORKSPACE;
+    if (((uintptr_t)ws & (kWsAlign - 1)) != 0) return CANON_EWORKSPACE;
+    return CANON_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ------------------------------------------------------------------ reduce
+size_t reduce_ws(uint64_t n, uint32_t L, size_t es)
+{
+    if (L == 0 || L > CANON_MAX_L || (es != 4 && es != 8)) return 0;
+    // the larger of the two possible plans (16-byte aligned input or not)
+    const ReducePlan a = plan_reduce(n, L, es, true, kReduceTargetWG);
+    const ReducePlan b = plan_reduce(n, L, es, false, kReduceTargetWG);
+    uint64_t need = reduce_partials_bytes(a, L, es);
+    const uint64_t nb = reduce_partials_bytes(b, L, es);
+    if (nb > need) need = nb;
+    return need ? round_up(need, kWsAlign) : 0;
+}
+
+template <typename T>
+canon_status_t reduce_impl(const T* x, size_t n, uint32_t L, T init, T* out, void* ws,
+                           size_t ws_bytes, void* stream)
+{
+    if (out == nullptr || L == 0 || (n > 0 && x == nullptr)) return CANON_EINVAL;
+    if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
+    const ReducePlan pl = plan_reduce(n, L, sizeof(T), aligned16(x), kReduceTargetWG);
+    // the documented size (covers either plan), so that a caller who sizes by
+    // canon_reduce_workspace_bytes is never rejected and never overrun
+    if (canon_status_t s = check_ws(ws, ws_bytes, reduce_ws(n, L, sizeof(T)))) return s;
+    return hip_status(launch_reduce<T>(x, n, L, init, out, static_cast<T*>(ws), pl,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+template <typename T>
+canon_status_t reduce_rows_impl(const T* x, size_t rows, size_t cols, size_t ldx, uint32_t L,
+                                T init, T* out, void* ws, size_t ws_bytes, void* stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    if (L == 0 || ldx < cols || (rows > 0 && out == nullptr) ||
+        (rows > 0 && cols > 0 && x == nullptr))
+        return CANON_EINVAL;
+    if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
+    if (rows == 0) return CANON_OK;
+    return hip_status(launch_reduce_rows<T>(x, rows, cols, ldx, L, init, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+// -------------------------------------------------------------------- scan
+canon_status_t check_policy(int policy, uint32_t param)
+{
+    switch (policy) {
+        case CANON_PAIRWISE:
+            return (param <= 1) ? CANON_OK : CANON_EINVAL;
+        case CANON_ITERATED_PAIRWISE:
+            if (param == 0) return CANON_EINVAL;
+            return param <= CANON_MAX_L ? CANON_OK : CANON_EUNSUPPORTED;
+        case CANON_BLOCK_DYADIC:
+            if (param == 0 || !is_pow2(param)) return CANON_EINVAL;
+            return param <= CANON_MAX_B ? CANON_OK : CANON_EUNSUPPORTED;
+        default:
+            return CANON_EINVAL;
+    }
+}
+
+template <typename T>
+ScanLayout scan_layout(uint64_t n, int policy, uint32_t param)
+{
+    (void)policy;
+    (void)param;
+    const uint64_t S = 1ull << scan_tile_log<T>();
+    return make_scan_layout((n + S - 1) / S, 1);
+}
+
+size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
+{
+    if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
+    const ScanLayout lay = es == 8 ? scan_layout<double>(n, policy, param)
+                                   : scan_layout<float>(n, policy, param);
+    return round_up(lay.total_words * 8, kWsAlign);
+}
+
+template <typename T>
+canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param, void* ws,
+                         size_t ws_bytes, void* stream)
+{
+    if (canon_status_t s = check_policy(policy, param)) return s;
+    if (n > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
+    if (n == 0) return CANON_OK;
+    if (policy == CANON_ITERATED_PAIRWISE) return CANON_EUNSUPPORTED;
+    const ScanLayout lay = scan_layout<T>(n, policy, param);
+    if (lay.ntiles > 0xFFFFFFFFull) return CANON_EUNSUPPORTED;
+    if (canon_status_t s = check_ws(ws, ws_bytes, round_up(lay.total_words * 8, kWsAlign)))
+        return s;
+    const bool pairwise = policy == CANON_PAIRWISE;
+    const int b_log = pairwise ? 0 : log2_exact(param);
+    const bool al = aligned16(x) && aligned16(y);
+    return hip_status(launch_scan<T>(x, y, n, pairwise, b_log, al, static_cast<uint64_t*>(ws), lay,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+template <typename T>
+canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t rows, size_t cols,
+                              int policy, uint32_t param, void* ws, size_t ws_bytes, void* stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    if (canon_status_t s = check_policy(policy, param)) return s;
+    if (ldx < cols || ldy < cols) return CANON_EINVAL;
+    if (rows > 0 && cols > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
+    if (rows == 0 || cols == 0) return CANON_OK;
+    if (policy == CANON_ITERATED_PAIRWISE) return CANON_EUNSUPPORTED;
+    const bool pairwise = policy == CANON_PAIRWISE;
+    const int b_log = pairwise ? 0 : log2_exact(param);
+    const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
+                    (ldy * sizeof(T)) % 16 == 0;
+    return hip_status(launch_scan_rows<T>(x, ldx, y, ldy, rows, cols, pairwise, b_log, al,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int canon_abi_version(void) { return CANON_ABI_VERSION; }
+
+const char* canon_status_str(int s)
+{
+    switch (s) {
+        case CANON_OK: return "CANON_OK";
+        case CANON_EINVAL: return "CANON_EINVAL: invalid argument";
+        case CANON_EUNSUPPORTED: return "CANON_EUNSUPPORTED: parameter outside the supported range";
+        case CANON_EWORKSPACE: return "CANON_EWORKSPACE: workspace too small or misaligned";
+        case CANON_EHIP: return "CANON_EHIP: HIP launch failed";
+        default: return "unknown canon status";
+    }
+}
+
+int canon_last_hip_error(void) { return g_last_hip_error; }
+
+size_t canon_reduce_workspace_bytes(size_t n, uint32_t L, size_t elem_size)
+{
+    return reduce_ws(n, L, elem_size);
+}
+
+canon_status_t canon_reduce_f64(const double* x, size_t n, uint32_t L, double init, double* out,
+                                void* ws, size_t ws_bytes, void* stream)
+{
+    return reduce_impl<double>(x, n, L, init, out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_reduce_f32(const float* x, size_t n, uint32_t L, float init, float* out,
+                                void* ws, size_t ws_bytes, void* stream)
+{
+    return reduce_impl<float>(x, n, L, init, out, ws, ws_bytes, stream);
+}
+
+size_t canon_reduce_rows_workspace_bytes(size_t rows, size_t cols, uint32_t L, size_t elem_size)
+{
+    (void)rows;
+    (void)cols;
+    (void)L;
+    (void)elem_size;
+    return 0;
+}
+
+canon_status_t canon_reduce_rows_f64(const double* x, size_t rows, size_t cols, size_t ldx,
+                                     uint32_t L, double init, double* out, void* ws,
+                                     size_t ws_bytes, void* stream)
+{
+    return reduce_rows_impl<double>(x, rows, cols, ldx, L, init, out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_reduce_rows_f32(const float* x, size_t rows, size_t cols, size_t ldx,
+                                     uint32_t L, float init, float* out, void* ws,
+                                     size_t ws_bytes, void* stream)
+{
+    return reduce_rows_impl<float>(x, rows, cols, ldx, L, init, out, ws, ws_bytes, stream);
+}
+
+size_t canon_scan_workspace_bytes(size_t n, int policy, uint32_t param, size_t elem_size)
+{
+    return scan_ws(n, policy, param, elem_size);
+}
+
+canon_status_t canon_scan_f64(const double* x, double* y, size_t n, int policy, uint32_t param,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_impl<double>(x, y, n, policy, param, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_f32(const float* x, float* y, size_t n, int policy, uint32_t param,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_impl<float>(x, y, n, policy, param, ws, ws_bytes, stream);
+}
+
+size_t canon_scan_rows_workspace_bytes(size_t rows, size_t cols, int policy, uint32_t param,
+                                       size_t elem_size)
+{
+    (void)rows;
+    (void)cols;
+    (void)policy;
+    (void)param;
+    (void)elem_size;
+    return 0;
+}
+
+canon_status_t canon_scan_rows_f64(const double* x, size_t ldx, double* y, size_t ldy,
+                                   size_t rows, size_t cols, int policy, uint32_t param,
+                                   void* ws, size_t ws_bytes, void* stream)
+{
+    return scan_rows_impl<double>(x, ldx, y, ldy, rows, cols, policy, param, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_rows_f32(const float* x, size_t ldx, float* y, size_t ldy, size_t rows,
+                                   size_t cols, int policy, uint32_t param, void* ws,
+                                   size_t ws_bytes, void* stream)
+{
+    return scan_rows_impl<float>(x, ldx, y, ldy, rows, cols, policy, param, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream)
+{
+    if (ws == nullptr || err_out == nullptr) return CANON_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(err_out, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return hip_status(e);
+}
+
+}  // extern "C"

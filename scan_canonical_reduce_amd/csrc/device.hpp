@@ -1,0 +1,239 @@
+// Device-side helpers shared by the libcanon kernels (gfx950, wave64).
+//
+// Everything here is plain data movement: 16-byte loads and stores, wave64
+// cross-lane moves, and agent-scope atomics for the scan's published values.
+// The only arithmetic the kernels perform on data is IEEE addition, always
+// written as (left + right) with `left` covering the lower input indices.
+//
+// "Absent" values are represented by -0.0: x + (-0.0) == x for every x
+// (including +0.0, -0.0, infinities and NaN), and -0.0 + -0.0 == -0.0, so
+// padding a sequence with trailing -0.0 never changes its pairwise value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace canon {
+
+constexpr int kWave = 64;
+
+template <typename T> struct Elem;
+template <> struct Elem<double> {
+    using bits_t = uint64_t;
+    static constexpr int E = 2;     // elements per 16-byte vector
+    static constexpr int LOGE = 1;
+    typedef double vec_t __attribute__((ext_vector_type(2)));
+};
+template <> struct Elem<float> {
+    using bits_t = uint32_t;
+    static constexpr int E = 4;
+    static constexpr int LOGE = 2;
+    typedef float vec_t __attribute__((ext_vector_type(4)));
+};
+
+template <typename T> __device__ __forceinline__ T neg_zero() { return T(-0.0); }
+
+// ---------------------------------------------------------------- 16-byte I/O
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* p, T (&v)[Elem<T>::E])
+{
+    using V = typename Elem<T>::vec_t;
+    V x = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+#pragma unroll
+    for (int e = 0; e < Elem<T>::E; ++e) v[e] = x[e];
+}
+
+template <typename T>
+__device__ __forceinline__ void store_vec(T* p, const T (&v)[Elem<T>::E])
+{
+    using V = typename Elem<T>::vec_t;
+    V x;
+#pragma unroll
+    for (int e = 0; e < Elem<T>::E; ++e) x[e] = v[e];
+    __builtin_nontemporal_store(x, reinterpret_cast<V*>(p));
+}
+
+// ------------------------------------------------------- wave64 lane moves
+// ds_swizzle in bit mode: source lane = ((lane & AND) | OR) ^ XOR within each
+// group of 32 lanes.  PAT = AND | OR << 5 | XOR << 10.
+template <int PAT>
+__device__ __forceinline__ uint32_t swz32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, PAT);
+}
+
+template <int PAT>
+__device__ __forceinline__ double swz(double v)
+{
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    uint32_t lo = swz32<PAT>((uint32_t)b), hi = swz32<PAT>((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int PAT>
+__device__ __forceinline__ float swz(float v)
+{
+    return __builtin_bit_cast(float, swz32<PAT>(__builtin_bit_cast(uint32_t, v)));
+}
+
+__device__ __forceinline__ double readlane(double v, int lane)
+{
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float readlane(float v, int lane)
+{
+    return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_readlane(
+                                         (int)__builtin_bit_cast(uint32_t, v), lane));
+}
+
+// Value of `v` held by lane (lane ^ MASK), MASK a power of two below 64.
+template <int MASK, typename T>
+__device__ __forceinline__ T shfl_xor(T v)
+{
+    static_assert(MASK > 0 && MASK < 64 && (MASK & (MASK - 1)) == 0, "xor mask");
+    if constexpr (MASK < 32) {
+        return swz<0x1F | (MASK << 10)>(v);
+    } else {
+        const int addr = (int)((__lane_id() ^ 32u) << 2);
+        if constexpr (sizeof(T) == 8) {
+            uint64_t b = __builtin_bit_cast(uint64_t, v);
+            uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)b);
+            uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(b >> 32));
+            return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+        } else {
+            return __builtin_bit_cast(
+                T, (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)__builtin_bit_cast(uint32_t, v)));
+        }
+    }
+}
+
+// Value of `v` held by the last lane of the lower half of this lane's aligned
+// group of 2*H lanes: lane ((lane & ~(2H-1)) | (H-1)).  H in {1,...,32}.
+template <int H, typename T>
+__device__ __forceinline__ T from_lower_half_end(T v)
+{
+    static_assert(H >= 1 && H <= 32 && (H & (H - 1)) == 0, "half size");
+    if constexpr (H < 32) {
+        constexpr int AND = 0x1F & ~(2 * H - 1);
+        constexpr int OR = H - 1;
+        return swz<AND | (OR << 5)>(v);
+    } else {
+        return readlane(v, 31);
+    }
+}
+
+// ----------------------------------------------- published 64-bit words
+// Values published between workgroups of one kernel are single 64-bit words,
+// stored and polled with agent-scope relaxed atomics: the word itself says
+// whether it is ready, so no ordering with other memory is needed.
+//   f64: the value's bits; "not ready" is a signalling-NaN pattern that no
+//        addition can produce (published values are canonicalised first).
+//   f32: the value's bits in the low half and 1 in the high half; "not
+//        ready" is 0.
+constexpr uint64_t kNotReady64 = 0x7FF4DEADBEEF0001ull;
+constexpr uint64_t kNotReady32 = 0ull;
+constexpr uint32_t kErrSpin = 1u;
+constexpr long kSpinLimit = 1l << 20;
+
+template <typename T> __device__ __forceinline__ uint64_t not_ready_word()
+{
+    return sizeof(T) == 8 ? kNotReady64 : kNotReady32;
+}
+
+__device__ __forceinline__ uint64_t pack_word(double v)
+{
+    return __builtin_bit_cast(uint64_t, __builtin_canonicalize(v));
+}
+__device__ __forceinline__ uint64_t pack_word(float v)
+{
+    return (1ull << 32) | (uint64_t)__builtin_bit_cast(uint32_t, v);
+}
+template <typename T> __device__ __forceinline__ T unpack_word(uint64_t w);
+template <> __device__ __forceinline__ double unpack_word<double>(uint64_t w)
+{
+    return __builtin_bit_cast(double, w);
+}
+template <> __device__ __forceinline__ float unpack_word<float>(uint64_t w)
+{
+    return __builtin_bit_cast(float, (uint32_t)w);
+}
+
+template <typename T>
+__device__ __forceinline__ void publish(uint64_t* slot, T v)
+{
+    __hip_atomic_store(slot, pack_word(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll a published word until it is ready.  The wait is bounded: after
+// kSpinLimit polls, or as soon as another wave has recorded an error, the
+// kernel's error word gets kErrSpin and -0.0 is returned, so that every wave
+// still runs to completion and the host can report the failure.
+template <typename T>
+__device__ __forceinline__ T wait_word(uint64_t* slot, uint32_t* err)
+{
+    const uint64_t nr = not_ready_word<T>();
+    uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    long it = 0;
+    while (w == nr) {
+        ++it;
+        if (it > kSpinLimit ||
+            ((it & 63) == 0 &&
+             __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+            __hip_atomic_fetch_or(err, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return neg_zero<T>();
+        }
+        __builtin_amdgcn_s_sleep(2);
+        w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return unpack_word<T>(w);
+}
+
+// Binary-counter ("shift-reduce") stack of complete pairwise subtrees, one
+// entry per level, each entry a small vector of W values.  push(k, v) adds the
+// k-th (0-based) subtree of equal size; after n pushes, collapse(n) returns
+// the right-to-left combination s_top + ... (s_1 + s_0), i.e. the pairwise
+// value over all pushed items.  k and n are uniform across the wave, so every
+// branch is scalar and every register index static.
+template <typename T, int W, int D>
+struct TreeStack {
+    T s[D + 1][W];
+
+    __device__ __forceinline__ void push(uint64_t k, T (&v)[W])
+    {
+        // merges = number of trailing one bits of k; the merged subtree then
+        // lands at level `merges`.  Static indices only (no break), so the
+        // stack stays in registers.
+        const int merges = __builtin_ctzll(~k);
+#pragma unroll
+        for (int l = 0; l < D; ++l) {
+            if (l < merges) {
+#pragma unroll
+                for (int i = 0; i < W; ++i) v[i] = s[l][i] + v[i];
+            }
+        }
+#pragma unroll
+        for (int l = 0; l <= D; ++l) {
+            const bool here = (l == merges);
+#pragma unroll
+            for (int i = 0; i < W; ++i) s[l][i] = here ? v[i] : s[l][i];
+        }
+    }
+
+    // n pushes; returns -0.0 ("absent") when n == 0.  Requires n <= 2^D.
+    __device__ __forceinline__ void collapse(uint64_t n, T (&out)[W]) const
+    {
+#pragma unroll
+        for (int i = 0; i < W; ++i) out[i] = neg_zero<T>();
+#pragma unroll
+        for (int l = 0; l <= D; ++l) {
+            if ((n >> l) & 1) {
+#pragma unroll
+                for (int i = 0; i < W; ++i) out[i] = s[l][i] + out[i];
+            }
+        }
+    }
+};
+
+}  // namespace canon

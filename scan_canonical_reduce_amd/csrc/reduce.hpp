@@ -1,0 +1,104 @@
+// Launch planning for the reduction kernels (host and device shared constants).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace canon {
+
+constexpr int kReduceThreads = 1024;  // streaming and finishing workgroups
+constexpr int kReduceWaves = kReduceThreads / 64;
+constexpr int kReduceBatch = 8;        // 16-byte vectors per thread per batch
+constexpr int kReduceStackDepth = 10;  // batches per wave <= 2^10
+constexpr int kRowsThreads = 256;      // row-batched workgroups
+constexpr int kMaxLogL = 16;
+constexpr uint64_t kPartialBudget = 1ull << 16;  // partial values (P * Lp) aimed for
+
+struct ReducePlan {
+    bool pow2;       // register path (L = 2^logl, 16-byte aligned input)
+    int logl;        // log2 L (pow2 path)
+    int lp_log;      // log2 of L rounded up to a power of two
+    uint64_t P;      // row ranges (grid.x); partial rows
+    uint64_t slices; // grid.y: column slices (pow2) or lane chunks (general)
+    int rw_log;      // pow2: log2 super-rows per wave
+    int lw_log;      // general: log2 lanes per workgroup chunk
+    int rs_log;      // general: log2 rows per thread segment
+};
+
+inline int ceil_log2(uint64_t v)
+{
+    int l = 0;
+    while ((1ull << l) < v) ++l;
+    return l;
+}
+
+// target_wg: workgroups the streaming kernel aims for (one per CU of MI355X).
+inline ReducePlan plan_reduce(uint64_t n, uint32_t L, size_t elem_size, bool aligned16,
+                              uint64_t target_wg)
+{
+    ReducePlan pl{};
+    pl.lp_log = ceil_log2(L);
+    const uint64_t Lp = 1ull << pl.lp_log;
+    const bool is_pow2 = (Lp == L);
+    pl.pow2 = is_pow2 && aligned16 && pl.lp_log <= kMaxLogL;
+    pl.logl = pl.lp_log;
+    if (n == 0) {
+        pl.P = 0;
+        pl.slices = 1;
+        return pl;
+    }
+    uint64_t budgetP = kPartialBudget / Lp;
+    if (budgetP < 1) budgetP = 1;
+    if (pl.pow2) {
+        const int loge = elem_size == 8 ? 1 : 2;
+        const int log_sr = pl.logl > loge ? pl.logl : loge;
+        const int logc = log_sr - loge;
+        const int log_cw = logc < 6 ? logc : 6;
+        const int logg = 6 - log_cw;
+        const uint64_t GU = (uint64_t)kReduceBatch << logg;
+        pl.slices = 1ull << (logc - log_cw);
+        const uint64_t msr = (n + (1ull << log_sr) - 1) >> log_sr;
+        uint64_t pt = target_wg / pl.slices;
+        if (pt < 1) pt = 1;
+        if (pt > budgetP) pt = budgetP;
+        uint64_t want = (msr + pt * kReduceWaves - 1) / (pt * kReduceWaves);
+        uint64_t rw = GU;
+        while (rw < want) rw *= 2;
+        const uint64_t rw_max = GU << kReduceStackDepth;
+        if (rw > rw_max) rw = rw_max;
+        pl.rw_log = ceil_log2(rw);
+        pl.P = (msr + rw * kReduceWaves - 1) / (rw * kReduceWaves);
+    } else {
+        const uint64_t m = (n + L - 1) / L;
+        const uint64_t LW = Lp < (uint64_t)kReduceThreads ? Lp : (uint64_t)kReduceThreads;
+        pl.lw_log = ceil_log2(LW);
+        const uint64_t S = kReduceThreads / LW;
+        pl.slices = (L + LW - 1) / LW;
+        uint64_t pt = target_wg / pl.slices;
+        if (pt < 1) pt = 1;
+        if (pt > budgetP) pt = budgetP;
+        uint64_t want = (m + pt * S - 1) / (pt * S);
+        uint64_t rs = 1;
+        while (rs < want) rs *= 2;
+        const uint64_t rs_max = 8ull << kReduceStackDepth;
+        if (rs > rs_max) rs = rs_max;
+        pl.rs_log = ceil_log2(rs);
+        pl.P = (m + rs * S - 1) / (rs * S);
+    }
+    return pl;
+}
+
+inline uint64_t reduce_partials_bytes(const ReducePlan& pl, uint32_t L, size_t elem_size)
+{
+    return pl.P * (uint64_t)L * elem_size;
+}
+
+template <typename T>
+hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, T* partial,
+                         const ReducePlan& pl, hipStream_t s);
+
+template <typename T>
+hipError_t launch_reduce_rows(const T* x, uint64_t rows, uint64_t cols, uint64_t ldx, uint32_t L,
+                              T init, T* out, hipStream_t s);
+
+}  // namespace canon

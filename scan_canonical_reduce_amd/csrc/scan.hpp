@@ -1,0 +1,69 @@
+// Launch planning for the scan kernels (host and device shared constants).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace canon {
+
+constexpr int kScanThreads = 256;  // 4 waves
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanVec = 8;        // 16-byte vectors per thread per tile
+constexpr int kGroupLog = 6;       // tile nodes below this level are rebuilt from tile totals
+constexpr int kMaxLevels = 48;
+
+// Workspace layout of a single-pass scan (offsets in 64-bit words).
+//   word 0: error word (low 32 bits); word 1: tile counter (low 32 bits)
+//   [tiles_off, +ntiles): published tile totals (tile-level 0 nodes)
+//   [level_off[k], +ceil(ntiles / 2^k)): published tile-level k nodes, k >= kGroupLog
+// Each published word holds one value (one lane value for the
+// iterated_pairwise scan, whose nodes are vectors of L words).
+struct ScanLayout {
+    uint64_t ntiles;
+    uint64_t width;  // words per node (1, or L for iterated_pairwise)
+    uint64_t tiles_off;
+    uint64_t level_off[kMaxLevels];
+    uint64_t total_words;
+};
+
+inline ScanLayout make_scan_layout(uint64_t ntiles, uint64_t width)
+{
+    ScanLayout l{};
+    l.ntiles = ntiles;
+    l.width = width;
+    l.tiles_off = 32;  // 256 bytes of header
+    uint64_t off = l.tiles_off + ntiles * width;
+    for (int k = 0; k < kMaxLevels; ++k) {
+        l.level_off[k] = off;
+        if (k >= kGroupLog) {
+            uint64_t cnt = (ntiles + (1ull << k) - 1) >> k;
+            off += cnt * width;
+        }
+    }
+    l.total_words = off;
+    return l;
+}
+
+template <typename T>
+constexpr int scan_tile_log()
+{
+    return (sizeof(T) == 8 ? 1 : 2) + 6 + 3 + 2;  // log2(E * 64 * kScanVec * kScanWaves)
+}
+
+template <typename T>
+hipError_t launch_scan(const T* x, T* y, uint64_t n, bool pairwise, int b_log, bool aligned,
+                       uint64_t* ws, const ScanLayout& lay, hipStream_t s);
+
+template <typename T>
+hipError_t launch_scan_rows(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
+                            uint64_t cols, bool pairwise, int b_log, bool aligned, hipStream_t s);
+
+template <typename T>
+hipError_t launch_scan_ip(const T* x, T* y, uint64_t n, uint32_t L, uint64_t* ws,
+                          const ScanLayout& lay, hipStream_t s);
+
+template <typename T>
+hipError_t launch_scan_rows_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
+                               uint64_t cols, uint32_t L, T* ws, hipStream_t s);
+
+}  // namespace canon

@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before it
+enqueues anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "canon.h")
+
+
+@pytest.fixture(scope="module")
+def canon():
+    import scan_canonical_reduce_amd as c
+    if not os.path.exists(c.LIB_PATH):
+        from scan_canonical_reduce_amd import build
+        build.build()
+    return c
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(canon_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_lists_the_binding_exports(canon):
+    assert header_functions() == sorted(canon.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(canon):
+    L = canon.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {canon.LIB_PATH}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_status_strings(canon):
+    L = canon.lib()
+    assert L.canon_abi_version() == 1
+    for s in range(5):
+        assert L.canon_status_str(s).decode().startswith("CANON_")
+    assert L.canon_last_hip_error() == 0
+
+
+def test_workspace_sizes(canon):
+    L = canon.lib()
+    assert L.canon_reduce_workspace_bytes(0, 16, 8) == 0
+    assert L.canon_reduce_workspace_bytes(1 << 20, 0, 8) == 0
+    assert L.canon_reduce_workspace_bytes(1 << 20, 16, 3) == 0
+    w = L.canon_reduce_workspace_bytes(1 << 28, 128, 8)
+    assert w > 0 and w % 256 == 0 and w <= (1 << 16) * 8 + 256
+    # enough room for one partial value per lane and range
+    assert L.canon_reduce_workspace_bytes(1000, 7, 8) >= 7 * 8
+    s = L.canon_scan_workspace_bytes(1 << 27, 2, 256, 8)
+    assert s > 0 and s % 256 == 0
+    assert L.canon_scan_workspace_bytes(1 << 20, 2, 3, 8) == 0  # B not a power of two
+    assert L.canon_scan_workspace_bytes(0, 0, 0, 8) == 0
+
+
+def _call_reduce(L, x, n, lanes, out, ws, wsb):
+    return L.canon_reduce_f64(x, n, lanes, 0.0, out, ws, wsb, None)
+
+
+def test_reduce_argument_errors(canon):
+    L = canon.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call fails validation
+    assert _call_reduce(L, fake, 10, 0, fake, None, 0) == 1       # L = 0
+    assert _call_reduce(L, None, 10, 4, fake, None, 0) == 1       # x NULL with n > 0
+    assert _call_reduce(L, fake, 10, 4, None, None, 0) == 1       # out NULL
+    assert _call_reduce(L, fake, 10, (1 << 16) + 1, fake, None, 0) == 2  # L too large
+    assert _call_reduce(L, fake, 1 << 20, 16, fake, None, 0) == 3  # no workspace
+    need = L.canon_reduce_workspace_bytes(1 << 20, 16, 8)
+    assert _call_reduce(L, fake, 1 << 20, 16, fake, ctypes.c_void_p(0x1000 + 8), need) == 3
+    assert _call_reduce(L, fake, 1 << 20, 16, fake, fake, need - 1) == 3
+    assert L.canon_reduce_rows_f64(fake, 4, 10, 9, 4, 0.0, fake, None, 0, None) == 1  # ld < cols
+    assert L.canon_reduce_rows_f64(fake, 4, 10, 10, 0, 0.0, fake, None, 0, None) == 1
+
+
+def test_scan_argument_errors(canon):
+    L = canon.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.canon_scan_f64(fake, fake, 10, 7, 0, None, 0, None) == 1      # bad policy
+    assert L.canon_scan_f64(fake, fake, 10, 0, 2, None, 0, None) == 1      # pairwise param
+    assert L.canon_scan_f64(fake, fake, 10, 2, 0, None, 0, None) == 1      # B = 0
+    assert L.canon_scan_f64(fake, fake, 10, 2, 12, None, 0, None) == 1     # B not pow2
+    assert L.canon_scan_f64(fake, fake, 10, 2, 1 << 17, None, 0, None) == 2  # B too large
+    assert L.canon_scan_f64(fake, fake, 10, 1, 0, None, 0, None) == 1      # L = 0
+    assert L.canon_scan_f64(fake, fake, 10, 1, (1 << 16) + 1, None, 0, None) == 2
+    assert L.canon_scan_f64(None, fake, 10, 0, 0, None, 0, None) == 1
+    assert L.canon_scan_f64(fake, fake, 1 << 20, 0, 0, None, 0, None) == 3  # no workspace
+    assert L.canon_scan_f64(fake, fake, 0, 0, 0, None, 0, None) == 0       # nothing to do
+    assert L.canon_scan_rows_f64(fake, 5, fake, 10, 3, 10, 0, 0, None, 0, None) == 1
+    assert L.canon_scan_rows_f64(fake, 10, fake, 5, 3, 10, 0, 0, None, 0, None) == 1
+    assert L.canon_workspace_error(None, None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors(canon):
+    import torch
+    x = torch.zeros(8, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        canon.reduce(x, 4)
+    with pytest.raises(ValueError):
+        canon.scan(x, "pairwise")
+    with pytest.raises(TypeError):
+        canon._sfx(torch.zeros(2, dtype=torch.int32))

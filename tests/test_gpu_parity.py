@@ -1,0 +1,216 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle, bit
+for bit (0 ULP; NaN compared by class), on seeded synthetic inputs.
+
+Sizes span several tiles / workgroups and ragged tails; the full-size
+workloads are in test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import assert_bit_exact, to_dev, to_host  # noqa: E402
+
+DT = {np.float64: torch.float64, np.float32: torch.float32}
+
+
+@pytest.fixture(scope="module")
+def canon():
+    import scan_canonical_reduce_amd as c
+    c.lib()
+    assert torch.cuda.is_available()
+    return c
+
+
+def gpu_reduce(canon, x, L, init):
+    r = canon.reduce(to_dev(x), L, init)
+    return to_host(r).reshape(1)
+
+
+# ----------------------------------------------------------------- reduce
+@pytest.mark.parametrize("L", [16, 128])
+@pytest.mark.parametrize("init", [0.0, 0.1, -0.0])
+def test_reduce_1m_uniform(canon, L, init):
+    x = synth.config_input("reduce_1m")
+    assert_bit_exact(gpu_reduce(canon, x, L, init), [oracle.reduce(x, L, init)], f"L={L}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 5, 7, 8, 16, 32, 64, 100, 128, 256, 512, 1024, 3000,
+                               4096, 65536])
+def test_reduce_tails(canon, dtype, L):
+    x = synth.generate(300_000, "mixed_magnitude", 7000 + L, dtype)
+    ns = sorted({0, 1, 2, 3, L - 1, L, L + 1, 2 * L + 3, 1000, 4095, 4096, 4097, 65535, 65536,
+                 65537, 131072 + 77, 300_000} - {-1})
+    for n in ns:
+        if n < 0 or n > x.size:
+            continue
+        xs = x[:n]
+        assert_bit_exact(gpu_reduce(canon, xs, L, 0.1), [oracle.reduce(xs, L, 0.1)],
+                         f"n={n} L={L}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [1, 16, 128, 7])
+def test_reduce_unaligned_input(canon, dtype, L):
+    """A view starting one element in is not 16-byte aligned: other path."""
+    base = synth.generate(200_001, "mixed_magnitude", 88, dtype)
+    xb = to_dev(base)
+    xs = xb[1:]
+    got = to_host(canon.reduce(xs, L, 1.0)).reshape(1)
+    assert_bit_exact(got, [oracle.reduce(base[1:], L, 1.0)], f"L={L}")
+
+
+def test_reduce_negative_zero_and_special_values(canon):
+    for L in (1, 4, 16, 128):
+        for n in (1, 3, 17, 300):
+            x = np.full(n, -0.0)
+            got = gpu_reduce(canon, x, L, -0.0)
+            assert_bit_exact(got, [oracle.reduce(x, L, -0.0)], "all -0")
+            assert np.signbit(got[0])
+    x = synth.generate(5000, "uniform_pm1", 5)
+    x[17] = np.inf
+    x[999] = -np.inf
+    x[2000] = np.nan
+    for L in (1, 16, 100):
+        assert_bit_exact(gpu_reduce(canon, x, L, 0.0), [oracle.reduce(x, L, 0.0)], "nan")
+    x = synth.generate(5000, "uniform_pm1", 6)
+    x[3] = np.inf
+    for L in (1, 16, 100):
+        assert_bit_exact(gpu_reduce(canon, x, L, 0.0), [oracle.reduce(x, L, 0.0)], "inf")
+
+
+def test_reduce_cancellation(canon):
+    x = synth.generate(100_000, "mixed_magnitude", 9)
+    x = np.concatenate([x, -x[::-1]])
+    for L in (1, 16, 128):
+        assert_bit_exact(gpu_reduce(canon, x, L, 0.0), [oracle.reduce(x, L, 0.0)], f"L={L}")
+
+
+def test_reduce_repeatable(canon):
+    x = synth.generate(3_000_001, "mixed_magnitude", 10)
+    xd = to_dev(x)
+    want = oracle.reduce(x, 128, 1.0)
+    for _ in range(20):
+        assert_bit_exact(to_host(canon.reduce(xd, 128, 1.0)).reshape(1), [want], "repeat")
+
+
+# ------------------------------------------------------------ reduce rows
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [1, 3, 16, 128, 300, 1024])
+def test_reduce_rows(canon, dtype, L):
+    rows, ld = 37, 5003
+    X = synth.generate(rows * ld, "uniform_pm1", 11 + L, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for cols in (0, 1, 15, 16, 17, 4096, 5000, 5003):
+        got = to_host(canon.reduce_rows(Xd[:, :cols], L, 0.1))
+        want = oracle.reduce_rows(X, L, 0.1, cols=cols)
+        assert_bit_exact(got, want, f"cols={cols}")
+
+
+def test_reduce_rows_shape_of_workload(canon):
+    rows, cols = 2048, 4096
+    X = synth.generate(rows * cols, "uniform_pm1", 1004).reshape(rows, cols)
+    assert_bit_exact(to_host(canon.reduce_rows(to_dev(X), 16, 0.0)),
+                     oracle.reduce_rows(X, 16, 0.0), "rows")
+
+
+# ------------------------------------------------------------------- scan
+def gpu_scan(canon, x, policy, param):
+    xd = to_dev(x)
+    ws = torch.empty(max(canon.scan_workspace_bytes(x.size, policy, param, x.itemsize), 1),
+                     dtype=torch.uint8, device="cuda")
+    y = canon.scan(xd, policy, param, ws=ws)
+    out = to_host(y)
+    if x.size:
+        assert canon.workspace_error(ws) == 0
+    return out
+
+
+@pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 256)])
+def test_scan_1m_uniform(canon, policy, param):
+    x = synth.config_input("scan_1m")
+    y = gpu_scan(canon, x, policy, param)
+    assert_bit_exact(y, oracle.scan(x, policy, param), policy)
+    # scan back element == canonical reduce of the same expression (GPU reduce)
+    assert_bit_exact(y[-1:], gpu_reduce(canon, x, 1, -0.0), "back == reduce")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 1), ("block_dyadic", 2),
+                                          ("block_dyadic", 4), ("block_dyadic", 16),
+                                          ("block_dyadic", 256), ("block_dyadic", 4096),
+                                          ("block_dyadic", 8192), ("block_dyadic", 65536)])
+def test_scan_tails(canon, dtype, policy, param):
+    S = 4096 if dtype == np.float64 else 8192
+    x = synth.generate(70 * S + 999, "mixed_magnitude", 12, dtype)
+    want_all = oracle.scan(x, policy, param)
+    for n in (1, 2, 3, 17, S - 1, S, S + 1, 3 * S + 5, 64 * S - 1, 64 * S, 64 * S + 1, 65 * S + 17,
+              x.size):
+        y = gpu_scan(canon, x[:n], policy, param)
+        assert_bit_exact(y, want_all[:n], f"n={n}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 16),
+                                          ("block_dyadic", 256)])
+def test_scan_many_tiles(canon, dtype, policy, param):
+    """Enough tiles for published nodes up to tile level 9."""
+    x = synth.generate((1 << 22) + 12345, "mixed_magnitude", 13, dtype)
+    y = gpu_scan(canon, x, policy, param)
+    assert_bit_exact(y, oracle.scan(x, policy, param), policy)
+
+
+def test_scan_in_place_and_unaligned(canon):
+    x = synth.generate(500_001, "mixed_magnitude", 14)
+    for policy, param in (("pairwise", 0), ("block_dyadic", 16)):
+        xd = to_dev(x)
+        canon.scan(xd, policy, param, out=xd)
+        assert_bit_exact(to_host(xd), oracle.scan(x, policy, param), "in place")
+        base = to_dev(x)
+        y = canon.scan(base[1:], policy, param)
+        assert_bit_exact(to_host(y), oracle.scan(x[1:], policy, param), "unaligned")
+
+
+def test_scan_repeatable(canon):
+    x = synth.generate(2_000_003, "mixed_magnitude", 15)
+    want = oracle.scan(x, "block_dyadic", 256)
+    xd = to_dev(x)
+    for _ in range(10):
+        assert_bit_exact(to_host(canon.scan(xd, "block_dyadic", 256)), want, "repeat")
+
+
+def test_scan_special_values(canon):
+    x = synth.generate(100_000, "uniform_pm1", 16)
+    x[:50] = -0.0
+    x[5000] = np.inf
+    x[70000] = np.nan
+    for policy, param in (("pairwise", 0), ("block_dyadic", 16)):
+        assert_bit_exact(gpu_scan(canon, x, policy, param), oracle.scan(x, policy, param), policy)
+
+
+# -------------------------------------------------------------- scan rows
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16),
+                                          ("block_dyadic", 4096)])
+def test_scan_rows(canon, dtype, policy, param):
+    rows, ld = 19, 3 * 8192 + 40
+    X = synth.generate(rows * ld, "mixed_magnitude", 17, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for cols in (1, 16, 4095, 4096, 8193, 3 * 8192 + 33):
+        got = to_host(canon.scan_rows(Xd[:, :cols], policy, param))
+        want = oracle.scan_rows(X, policy, param, cols=cols)[:, :cols]
+        assert_bit_exact(got, want, f"cols={cols}")
+
+
+def test_scan_rows_shape_of_workload(canon):
+    rows, cols = 2048, 4096
+    X = synth.generate(rows * cols, "uniform_pm1", 1004).reshape(rows, cols)
+    got = to_host(canon.scan_rows(to_dev(X), "block_dyadic", 16))
+    assert_bit_exact(got, oracle.scan_rows(X, "block_dyadic", 16), "rows")
+    # per row, the last prefix equals the pairwise reduce of the row (16 | 4096)
+    assert_bit_exact(got[:, -1], oracle.reduce_rows(X, 1, -0.0), "row back == PW(row)")
