@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark: canonical fp64 reduce and scans at N = 2^28 on one MI355X.
+
+One step runs every operation of the hot path once, each over its resident
+synthetic input:
+  reduce          canonical reduce, L = 128, init = 1.0   (N = 2^28 f64)
+  scan_bd256      block_dyadic<256> inclusive scan         (N = 2^28 f64)
+  scan_bd16       block_dyadic<16> inclusive scan          (N = 2^28 f64)
+  scan_pairwise   pairwise inclusive scan                  (N = 2^28 f64)
+  scan_ip128      iterated_pairwise<128> inclusive scan    (N = 2^28 f64)
+  rows_reduce     16384 rows x 4096, L = 16                (f64)
+  rows_scan_bd16  16384 rows x 4096, block_dyadic<16>      (f64)
+value = algorithmic bytes of the step / time of the step (GB/s); reduce
+reads N*8 bytes, a scan reads and writes N*8 bytes each.  Before timing,
+every result is checked bit for bit against the CPU oracle (full reduce,
+sampled scan prefixes evaluated from scratch).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-check]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+N_MAIN = 1 << 28
+ROWS, COLS = 16384, 4096
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle parity gate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of ops to run (profiling)")
+    ap.add_argument("--reps", type=int, default=20, help="per-op timing repetitions")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import scan_canonical_reduce_amd as canon
+    import synth
+
+    canon.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    x_np = synth.config_input("reduce_2e28_f64")  # N = 2^28 mixed magnitude, seed 1003
+    X_np = synth.config_input("rows_16384x4096")
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s "
+        f"sha256(x)={synth.sha256(x_np)[:16]} sha256(X)={synth.sha256(X_np)[:16]}")
+    x = torch.from_numpy(x_np).to(dev)
+    X = torch.from_numpy(X_np).to(dev)
+    y = torch.empty_like(x)
+    Y = torch.empty_like(X)
+    r0 = torch.empty((), dtype=torch.float64, device=dev)
+    rr = torch.empty(ROWS, dtype=torch.float64, device=dev)
+
+    have_ip = canon.scan_workspace_bytes(N_MAIN, "iterated_pairwise", 128, 8) > 0
+    scans = [("scan_bd256", "block_dyadic", 256), ("scan_bd16", "block_dyadic", 16),
+             ("scan_pairwise", "pairwise", 0)]
+    if have_ip:
+        scans.append(("scan_ip128", "iterated_pairwise", 128))
+    ws_bytes = max([canon.reduce_workspace_bytes(N_MAIN, 128, 8)] +
+                   [canon.scan_workspace_bytes(N_MAIN, p, q, 8) for _, p, q in scans])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    ops = {}
+    ops["reduce"] = (lambda: canon.reduce(x, 128, 1.0, out=r0, ws=ws), N_MAIN * 8)
+    for name, p, q in scans:
+        ops[name] = ((lambda p=p, q=q: canon.scan(x, p, q, out=y, ws=ws)), 2 * N_MAIN * 8)
+    ops["rows_reduce"] = (lambda: canon.reduce_rows(X, 16, 0.0, out=rr), ROWS * COLS * 8)
+    ops["rows_scan_bd16"] = (lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y),
+                             2 * ROWS * COLS * 8)
+    if args.only:
+        keep = set(args.only.split(","))
+        ops = {k: v for k, v in ops.items() if k in keep}
+
+    # ------------------------------------------------------- parity gate
+    parity = {}
+    if not args.no_check:
+        import oracle
+        t0 = time.time()
+        rng = np.random.default_rng(2024)
+        probes = np.unique(np.concatenate([[0, 1, 4095, 4096, N_MAIN - 1],
+                                           rng.integers(0, N_MAIN, 3)]))
+        for name, (fn, _) in ops.items():
+            fn()
+            torch.cuda.synchronize()
+            if name == "reduce":
+                want = oracle.reduce(x_np, 128, 1.0)
+                ok = np.float64(r0.item()).tobytes() == np.float64(want).tobytes()
+            elif name == "rows_reduce":
+                want = oracle.reduce_rows(X_np, 16, 0.0)
+                ok = np.array_equal(rr.cpu().numpy().view(np.uint64), want.view(np.uint64))
+            elif name == "rows_scan_bd16":
+                idx = rng.integers(0, ROWS, 64)
+                got = Y[idx].cpu().numpy()
+                want = oracle.scan_rows(X_np[idx], "block_dyadic", 16)
+                ok = np.array_equal(got.view(np.uint64), want.view(np.uint64))
+            else:
+                _, p, q = [s for s in scans if s[0] == name][0]
+                err = canon.workspace_error(ws)
+                got = y[torch.from_numpy(probes).to(dev)].cpu().numpy()
+                want = np.array([oracle.scan_prefix(x_np, int(i), p, q) for i in probes])
+                ok = err == 0 and np.array_equal(got.view(np.uint64), want.view(np.uint64))
+            parity[name] = bool(ok)
+            log(f"[bench] parity {name}: {'PASS' if ok else 'FAIL'}")
+        log(f"[bench] parity gate {time.time() - t0:.1f}s")
+        if not all(parity.values()):
+            print(json.dumps({"error": "parity gate failed", "parity": parity}))
+            sys.exit(1)
+
+    # ------------------------------------------------- per-op timing
+    stream = torch.cuda.current_stream()
+    per_op = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        med = ms[len(ms) // 2]
+        per_op[name] = {"ms_median": med, "ms_p10": ms[len(ms) // 10],
+                        "ms_p90": ms[(9 * len(ms)) // 10], "bytes": nbytes,
+                        "GBps": nbytes / (med * 1e-3) / 1e9,
+                        "pct_hbm_peak": 100.0 * nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] {name:15s} median {med * 1e3:9.1f} us  "
+            f"{per_op[name]['GBps']:8.1f} GB/s  {per_op[name]['pct_hbm_peak']:5.1f}% of peak")
+
+    # ------------------------------------------------------ step timing
+    def step():
+        for fn, _ in ops.values():
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    total_ms = a.elapsed_time(b)
+    ms_step = total_ms / args.steps
+    step_bytes = sum(nb for _, nb in ops.values())
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: the op with the largest share of the step
+    dom = max(per_op, key=lambda k: per_op[k]["ms_median"])
+    d = per_op[dom]
+    roofline = {"bound": "hbm", "achieved": round(d["GBps"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dom}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x_np, X_np)
+
+    out = {
+        "metric": "GB/s and % HBM peak, bit-exact canonical fp64 reduce & scan, N=2^28, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "canonical fp64 reduce (L=128, init=1) and scans "
+                               "(block_dyadic<256>, block_dyadic<16>, pairwise"
+                               + (", iterated_pairwise<128>" if have_ip else "") +
+                               ") over N=2^28 mixed-magnitude doubles, plus 16384x4096 "
+                               "row reduce (L=16) and row scan (block_dyadic<16>)",
+                   "n": N_MAIN, "rows": ROWS, "cols": COLS,
+                   "ops": list(ops.keys())},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "parity": parity,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in per_op.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x_np, X_np):
+    """The oracle (single-threaded C, as it stands) on a bounded sample of the
+    same step: every op over the first 2^26 of the 2^28 elements (the row ops
+    over the first 4096 of 16384 rows)."""
+    import oracle
+    n = 1 << 26
+    xs = x_np[:n]
+    Xs = X_np[:4096]
+    nbytes = 0
+    t0 = time.perf_counter()
+    oracle.reduce(xs, 128, 1.0)
+    nbytes += n * 8
+    for p, q in (("block_dyadic", 256), ("block_dyadic", 16), ("pairwise", 0)):
+        oracle.scan(xs, p, q)
+        nbytes += 2 * n * 8
+    oracle.reduce_rows(Xs, 16, 0.0)
+    nbytes += Xs.size * 8
+    oracle.scan_rows(Xs, "block_dyadic", 16)
+    nbytes += 2 * Xs.size * 8
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "reduce and the block_dyadic<256>, block_dyadic<16> and pairwise scans over "
+                      "the first 2^26 of the 2^28 elements; row reduce and row scan over the "
+                      "first 4096 of 16384 rows",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

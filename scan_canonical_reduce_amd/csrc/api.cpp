@@ -120,6 +120,7 @@ ScanLayout scan_layout(uint64_t n, int policy, uint32_t param)
 size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
+    if (policy == CANON_ITERATED_PAIRWISE) return 0;
     const ScanLayout lay = es == 8 ? scan_layout<double>(n, policy, param)
                                    : scan_layout<float>(n, policy, param);
     return round_up(lay.total_words * 8, kWsAlign);

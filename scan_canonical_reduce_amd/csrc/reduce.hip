@@ -19,6 +19,7 @@
 //   2. a finishing kernel (one workgroup): PW over the partials of each lane
 //      in range order, PW over lanes, then init + R.
 #include "device.hpp"
+#include "launch.hpp"
 #include "reduce.hpp"
 
 namespace canon {
@@ -454,9 +455,11 @@ hipError_t launch_reduce_rows(const T* x, uint64_t rows, uint64_t cols, uint64_t
     int lp_log = 0;
     while ((1ull << lp_log) < L) ++lp_log;
     int lw_log = lp_log < 8 ? lp_log : 8;
-    uint64_t grid = rows < 65536 ? rows : 65536;
-    hipLaunchKernelGGL((k_reduce_rows<T>), dim3((unsigned)grid), dim3(kRowsThreads), 0, s, x, rows,
-                       cols, ldx, L, lw_log, init, out);
+    constexpr auto kern = k_reduce_rows<T>;
+    uint64_t grid = resident_grid<kern>(kRowsThreads);
+    if (grid > rows) grid = rows;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRowsThreads), 0, s, x, rows, cols, ldx, L,
+                       lw_log, init, out);
     return hipGetLastError();
 }
 

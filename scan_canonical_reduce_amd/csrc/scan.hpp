@@ -44,10 +44,20 @@ inline ScanLayout make_scan_layout(uint64_t ntiles, uint64_t width)
     return l;
 }
 
+#ifndef CANON_SCAN_LOGV
+#define CANON_SCAN_LOGV 3
+#endif
+// log2 of the 16-byte vectors each thread of the single-pass scan holds
+template <typename T>
+constexpr int scan_log_v()
+{
+    return CANON_SCAN_LOGV;
+}
+
 template <typename T>
 constexpr int scan_tile_log()
 {
-    return (sizeof(T) == 8 ? 1 : 2) + 6 + 3 + 2;  // log2(E * 64 * kScanVec * kScanWaves)
+    return (sizeof(T) == 8 ? 1 : 2) + 6 + scan_log_v<T>() + 2;  // log2(E * 64 * V * waves)
 }
 
 template <typename T>
