@@ -67,6 +67,9 @@ extern "C" {
  * size B for block_dyadic.  Larger values return CANON_EUNSUPPORTED. */
 #define CANON_MAX_L 65536u
 #define CANON_MAX_B 65536u
+/* Largest lane count L of the iterated_pairwise scan (the per-row lane trees
+ * of a tile are kept in LDS). */
+#define CANON_MAX_IP_L 2048u
 
 typedef enum {
     CANON_OK = 0,
@@ -78,7 +81,7 @@ typedef enum {
 
 typedef enum {
     CANON_PAIRWISE = 0,          /* param must be 0 or 1 */
-    CANON_ITERATED_PAIRWISE = 1, /* param = L, 1 <= L <= CANON_MAX_L */
+    CANON_ITERATED_PAIRWISE = 1, /* param = L, 1 <= L <= CANON_MAX_IP_L */
     CANON_BLOCK_DYADIC = 2       /* param = B, power of two, 1 <= B <= CANON_MAX_B */
 } canon_policy_t;
 
@@ -141,11 +144,12 @@ canon_status_t canon_scan_rows_f32(const float* x, size_t ldx, float* y, size_t 
                                    void* ws, size_t ws_bytes, void* stream);
 
 /* -------------------------------------------------------------- checking */
-/* The single-pass scans wait on values published by earlier workgroups with
- * a bounded spin; if a bound is ever exceeded the kernel stops waiting,
- * records a nonzero word at the start of the workspace and finishes (the
- * output is then invalid).  This call copies that word to *err_out and
- * synchronises `stream`.  0 means no error. */
+/* Every scan workspace begins with a 32-bit error word.  The single-pass
+ * scans (pairwise, block_dyadic) wait on values published by earlier
+ * workgroups with a bounded spin; if a bound is ever exceeded the kernel
+ * stops waiting, records a nonzero error word and finishes (the output is
+ * then invalid).  This call copies the word to *err_out and synchronises
+ * `stream`.  0 means no error. */
 canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream);
 
 #ifdef __cplusplus

@@ -144,6 +144,10 @@ def scan_workspace_bytes(n: int, policy, param: int, elem_size: int) -> int:
     return lib().canon_scan_workspace_bytes(n, _policy(policy), param, elem_size)
 
 
+def scan_rows_workspace_bytes(rows: int, cols: int, policy, param: int, elem_size: int) -> int:
+    return lib().canon_scan_rows_workspace_bytes(rows, cols, _policy(policy), param, elem_size)
+
+
 def reduce(x: torch.Tensor, L: int, init: float = 0.0, out: torch.Tensor | None = None,
            ws: torch.Tensor | None = None) -> torch.Tensor:
     """init + CR_L(x) as a 0-d tensor on x's device (init when x is empty)."""
@@ -204,7 +208,7 @@ def reduce_rows(X: torch.Tensor, L: int, init: float = 0.0,
 
 
 def scan_rows(X: torch.Tensor, policy="pairwise", param: int = 0,
-              out: torch.Tensor | None = None) -> torch.Tensor:
+              out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
     """One canonical scan per row of a 2-d tensor."""
     _need_gpu(X)
     sfx = _sfx(X)
@@ -213,8 +217,11 @@ def scan_rows(X: torch.Tensor, policy="pairwise", param: int = 0,
         out = torch.empty((rows, cols), dtype=X.dtype, device=X.device)
     _, _, ldy = _rows_view(out)
     p = _policy(policy)
+    nb = lib().canon_scan_rows_workspace_bytes(rows, cols, p, param, X.element_size())
+    w = _ws(nb, X.device, ws)
     st = getattr(lib(), f"canon_scan_rows_{sfx}")(
-        _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, None, 0, _stream())
+        _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, _ptr(w),
+        nb if w is None else w.numel(), _stream())
     _check(st, "scan_rows")
     return out
 

@@ -11,6 +11,7 @@
 #include "../../include/canon.h"
 #include "reduce.hpp"
 #include "scan.hpp"
+#include "scan_ip.hpp"
 
 using namespace canon;
 
@@ -99,7 +100,7 @@ canon_status_t check_policy(int policy, uint32_t param)
             return (param <= 1) ? CANON_OK : CANON_EINVAL;
         case CANON_ITERATED_PAIRWISE:
             if (param == 0) return CANON_EINVAL;
-            return param <= CANON_MAX_L ? CANON_OK : CANON_EUNSUPPORTED;
+            return param <= CANON_MAX_IP_L ? CANON_OK : CANON_EUNSUPPORTED;
         case CANON_BLOCK_DYADIC:
             if (param == 0 || !is_pow2(param)) return CANON_EINVAL;
             return param <= CANON_MAX_B ? CANON_OK : CANON_EUNSUPPORTED;
@@ -117,13 +118,32 @@ ScanLayout scan_layout(uint64_t n, int policy, uint32_t param)
     return make_scan_layout((n + S - 1) / S, 1);
 }
 
+// Node storage of an iterated_pairwise scan, after the 256-byte header whose
+// first word is the error word every scan workspace carries.
+template <typename T>
+T* ip_nodes(void* ws)
+{
+    return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + kWsAlign);
+}
+
+// iterated_pairwise with L = 1 is the pairwise expression: CR_1 = PW.
+bool is_ip(int policy, uint32_t param) { return policy == CANON_ITERATED_PAIRWISE && param > 1; }
+
 size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
-    if (policy == CANON_ITERATED_PAIRWISE) return 0;
+    if (is_ip(policy, param))
+        return kWsAlign + round_up(make_ip_layout(1, n, param, es).total * es, kWsAlign);
     const ScanLayout lay = es == 8 ? scan_layout<double>(n, policy, param)
                                    : scan_layout<float>(n, policy, param);
     return round_up(lay.total_words * 8, kWsAlign);
+}
+
+size_t scan_rows_ws(uint64_t rows, uint64_t cols, int policy, uint32_t param, size_t es)
+{
+    if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8)) return 0;
+    if (rows == 0 || cols == 0 || !is_ip(policy, param)) return 0;
+    return kWsAlign + round_up(make_ip_layout(rows, cols, param, es).total * es, kWsAlign);
 }
 
 template <typename T>
@@ -133,12 +153,18 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
     if (canon_status_t s = check_policy(policy, param)) return s;
     if (n > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
     if (n == 0) return CANON_OK;
-    if (policy == CANON_ITERATED_PAIRWISE) return CANON_EUNSUPPORTED;
+    if (is_ip(policy, param)) {
+        const IpLayout ip = make_ip_layout(1, n, param, sizeof(T));
+        if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
+            return s;
+        return hip_status(launch_scan_ip<T>(x, n, y, n, 1, n, static_cast<uint32_t*>(ws),
+                                            ip_nodes<T>(ws), ip, static_cast<hipStream_t>(stream)));
+    }
     const ScanLayout lay = scan_layout<T>(n, policy, param);
     if (lay.ntiles > 0xFFFFFFFFull) return CANON_EUNSUPPORTED;
     if (canon_status_t s = check_ws(ws, ws_bytes, round_up(lay.total_words * 8, kWsAlign)))
         return s;
-    const bool pairwise = policy == CANON_PAIRWISE;
+    const bool pairwise = policy != CANON_BLOCK_DYADIC;  // pairwise, or iterated_pairwise<1>
     const int b_log = pairwise ? 0 : log2_exact(param);
     const bool al = aligned16(x) && aligned16(y);
     return hip_status(launch_scan<T>(x, y, n, pairwise, b_log, al, static_cast<uint64_t*>(ws), lay,
@@ -155,8 +181,16 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
     if (ldx < cols || ldy < cols) return CANON_EINVAL;
     if (rows > 0 && cols > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
     if (rows == 0 || cols == 0) return CANON_OK;
-    if (policy == CANON_ITERATED_PAIRWISE) return CANON_EUNSUPPORTED;
-    const bool pairwise = policy == CANON_PAIRWISE;
+    if (is_ip(policy, param)) {
+        const IpLayout ip = make_ip_layout(rows, cols, param, sizeof(T));
+        if (canon_status_t s =
+                check_ws(ws, ws_bytes, scan_rows_ws(rows, cols, policy, param, sizeof(T))))
+            return s;
+        return hip_status(launch_scan_ip<T>(x, ldx, y, ldy, rows, cols,
+                                            static_cast<uint32_t*>(ws), ip_nodes<T>(ws), ip,
+                                            static_cast<hipStream_t>(stream)));
+    }
+    const bool pairwise = policy != CANON_BLOCK_DYADIC;
     const int b_log = pairwise ? 0 : log2_exact(param);
     const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                     (ldy * sizeof(T)) % 16 == 0;
@@ -244,12 +278,7 @@ canon_status_t canon_scan_f32(const float* x, float* y, size_t n, int policy, ui
 size_t canon_scan_rows_workspace_bytes(size_t rows, size_t cols, int policy, uint32_t param,
                                        size_t elem_size)
 {
-    (void)rows;
-    (void)cols;
-    (void)policy;
-    (void)param;
-    (void)elem_size;
-    return 0;
+    return scan_rows_ws(rows, cols, policy, param, elem_size);
 }
 
 canon_status_t canon_scan_rows_f64(const double* x, size_t ldx, double* y, size_t ldy,

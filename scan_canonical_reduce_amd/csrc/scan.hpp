@@ -68,12 +68,5 @@ template <typename T>
 hipError_t launch_scan_rows(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
                             uint64_t cols, bool pairwise, int b_log, bool aligned, hipStream_t s);
 
-template <typename T>
-hipError_t launch_scan_ip(const T* x, T* y, uint64_t n, uint32_t L, uint64_t* ws,
-                          const ScanLayout& lay, hipStream_t s);
-
-template <typename T>
-hipError_t launch_scan_rows_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
-                               uint64_t cols, uint32_t L, T* ws, hipStream_t s);
 
 }  // namespace canon

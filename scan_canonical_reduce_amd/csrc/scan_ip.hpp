@@ -1,0 +1,72 @@
+// Planning for the iterated_pairwise<L> scan (host and device shared).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace canon {
+
+constexpr int kIpThreads = 256;
+constexpr int kIpMaxRLog = 6;         // at most 64 rows per tile
+constexpr int kIpLevelsPerPass = 4;   // node levels built per launch
+constexpr int kIpMaxLevels = 48;
+constexpr uint64_t kIpMaxGrid = 8192;
+constexpr uint32_t kIpMaxL = 2048;    // largest lane count of the scan
+
+// Geometry of an iterated_pairwise scan over nseg independent segments of
+// `cols` elements (one segment for a plain scan, one per row for the row
+// scan), and the layout of the node arrays in the workspace (in elements):
+// level k holds, per segment, cnt[k] nodes of L values: the complete
+// pairwise trees, lane by lane, over tiles [u 2^k, (u+1) 2^k).
+struct IpLayout {
+    uint32_t L;
+    int lp_log;  // Lp = 2^lp_log >= L
+    int r_log;   // R = 2^r_log rows of L lanes per tile
+    uint64_t nseg;
+    uint64_t tps;  // tiles per segment
+    int levels;    // node levels with at least one node
+    uint64_t cnt[kIpMaxLevels];
+    uint64_t off[kIpMaxLevels];
+    uint64_t total;  // elements of node storage
+};
+
+// LDS budget (elements) for the per-row trees of one tile: (R + 1) * 2 * Lp
+inline uint64_t ip_lds_elems(size_t elem_size) { return elem_size == 8 ? 8192 : 16384; }
+
+inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t elem_size)
+{
+    IpLayout lay{};
+    lay.L = L;
+    int lp = 0;
+    while ((1ull << lp) < L) ++lp;
+    lay.lp_log = lp;
+    const uint64_t Lp = 1ull << lp;
+    int rl = kIpMaxRLog;
+    while (rl > 0 && ((1ull << rl) + 1) * 2 * Lp > ip_lds_elems(elem_size)) --rl;
+    lay.r_log = rl;
+    lay.nseg = nseg;
+    const uint64_t rows = (cols + L - 1) / L;
+    lay.tps = (rows + (1ull << rl) - 1) >> rl;
+    uint64_t off = 0;
+    lay.levels = 0;
+    for (int k = 0; k < kIpMaxLevels; ++k) {
+        lay.cnt[k] = k == 0 ? lay.tps : (lay.tps >> k);
+        lay.off[k] = off;
+        if (lay.cnt[k] > 0) lay.levels = k + 1;
+        off += nseg * lay.cnt[k] * L;
+    }
+    lay.total = off;
+    return lay;
+}
+
+inline size_t ip_lds_bytes(const IpLayout& lay, size_t elem_size)
+{
+    return (size_t)((1ull << lay.r_log) + 1) * 2 * (1ull << lay.lp_log) * elem_size;
+}
+
+template <typename T>
+hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,
+                          uint64_t cols, uint32_t* err, T* nodes, const IpLayout& lay,
+                          hipStream_t s);
+
+}  // namespace canon

@@ -60,6 +60,9 @@ def test_workspace_sizes(canon):
     assert s > 0 and s % 256 == 0
     assert L.canon_scan_workspace_bytes(1 << 20, 2, 3, 8) == 0  # B not a power of two
     assert L.canon_scan_workspace_bytes(0, 0, 0, 8) == 0
+    assert L.canon_scan_workspace_bytes(1 << 20, 1, 128, 8) > 0       # iterated_pairwise nodes
+    assert L.canon_scan_rows_workspace_bytes(16, 4096, 2, 16, 8) == 0  # block_dyadic rows: none
+    assert L.canon_scan_rows_workspace_bytes(16, 4096, 1, 16, 8) > 0
 
 
 def _call_reduce(L, x, n, lanes, out, ws, wsb):
@@ -91,6 +94,9 @@ def test_scan_argument_errors(canon):
     assert L.canon_scan_f64(fake, fake, 10, 2, 1 << 17, None, 0, None) == 2  # B too large
     assert L.canon_scan_f64(fake, fake, 10, 1, 0, None, 0, None) == 1      # L = 0
     assert L.canon_scan_f64(fake, fake, 10, 1, (1 << 16) + 1, None, 0, None) == 2
+    assert L.canon_scan_f64(fake, fake, 10, 1, 4096, None, 0, None) == 2    # L > CANON_MAX_IP_L
+    assert L.canon_scan_f64(fake, fake, 1 << 20, 1, 128, None, 0, None) == 3  # no workspace
+    assert L.canon_scan_rows_f64(fake, 4096, fake, 4096, 8, 4096, 1, 16, None, 0, None) == 3
     assert L.canon_scan_f64(None, fake, 10, 0, 0, None, 0, None) == 1
     assert L.canon_scan_f64(fake, fake, 1 << 20, 0, 0, None, 0, None) == 3  # no workspace
     assert L.canon_scan_f64(fake, fake, 0, 0, 0, None, 0, None) == 0       # nothing to do

@@ -214,3 +214,47 @@ def test_scan_rows_shape_of_workload(canon):
     assert_bit_exact(got, oracle.scan_rows(X, "block_dyadic", 16), "rows")
     # per row, the last prefix equals the pairwise reduce of the row (16 | 4096)
     assert_bit_exact(got[:, -1], oracle.reduce_rows(X, 1, -0.0), "row back == PW(row)")
+
+
+# ------------------------------------------------- iterated_pairwise scan
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 7, 16, 100, 128, 1024, 2048])
+def test_scan_iterated_pairwise(canon, dtype, L):
+    x = synth.generate(200_003, "mixed_magnitude", 300 + L, dtype)
+    want_all = oracle.scan(x[:60_000] if L > 128 else x, "iterated_pairwise", L)
+    for n in (1, 2, L - 1, L, L + 1, 3 * L + 2, 5000, 60_000, x.size):
+        if n <= 0 or n > want_all.size:
+            continue
+        y = gpu_scan(canon, x[:n], "iterated_pairwise", L)
+        assert_bit_exact(y, want_all[:n], f"n={n}")
+        # the last prefix is the canonical reduce with the same L (GPU reduce)
+        assert_bit_exact(y[-1:], gpu_reduce(canon, x[:n], L, -0.0), f"back n={n}")
+
+
+def test_scan_iterated_pairwise_many_tiles(canon):
+    x = synth.generate((1 << 21) + 777, "mixed_magnitude", 401)
+    for L in (16, 128):
+        y = gpu_scan(canon, x, "iterated_pairwise", L)
+        assert_bit_exact(y, oracle.scan(x, "iterated_pairwise", L), f"L={L}")
+
+
+def test_scan_iterated_pairwise_in_place_unaligned(canon):
+    x = synth.generate(100_001, "mixed_magnitude", 402)
+    xd = to_dev(x)
+    canon.scan(xd, "iterated_pairwise", 128, out=xd)
+    assert_bit_exact(to_host(xd), oracle.scan(x, "iterated_pairwise", 128), "in place")
+    base = to_dev(x)
+    y = canon.scan(base[1:], "iterated_pairwise", 7)
+    assert_bit_exact(to_host(y), oracle.scan(x[1:], "iterated_pairwise", 7), "unaligned")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [3, 16, 128])
+def test_scan_rows_iterated_pairwise(canon, dtype, L):
+    rows, ld = 23, 9001
+    X = synth.generate(rows * ld, "mixed_magnitude", 403 + L, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for cols in (1, 17, L, 4096, 9001):
+        got = to_host(canon.scan_rows(Xd[:, :cols], "iterated_pairwise", L))
+        want = oracle.scan_rows(X, "iterated_pairwise", L, cols=cols)[:, :cols]
+        assert_bit_exact(got, want, f"cols={cols}")
