@@ -133,7 +133,12 @@ size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
     if (is_ip(policy, param))
-        return kWsAlign + round_up(make_ip_layout(1, n, param, es).total * es, kWsAlign);
+    {
+        // the larger of the two layouts (register path or LDS path)
+        const uint64_t a = make_ip_layout(1, n, param, es, true).total;
+        const uint64_t b = make_ip_layout(1, n, param, es, false).total;
+        return kWsAlign + round_up((a > b ? a : b) * es, kWsAlign);
+    }
     const ScanLayout lay = es == 8 ? scan_layout<double>(n, policy, param)
                                    : scan_layout<float>(n, policy, param);
     return round_up(lay.total_words * 8, kWsAlign);
@@ -143,7 +148,9 @@ size_t scan_rows_ws(uint64_t rows, uint64_t cols, int policy, uint32_t param, si
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8)) return 0;
     if (rows == 0 || cols == 0 || !is_ip(policy, param)) return 0;
-    return kWsAlign + round_up(make_ip_layout(rows, cols, param, es).total * es, kWsAlign);
+    const uint64_t a = make_ip_layout(rows, cols, param, es, true).total;
+    const uint64_t b = make_ip_layout(rows, cols, param, es, false).total;
+    return kWsAlign + round_up((a > b ? a : b) * es, kWsAlign);
 }
 
 template <typename T>
@@ -154,7 +161,7 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
     if (n > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
     if (n == 0) return CANON_OK;
     if (is_ip(policy, param)) {
-        const IpLayout ip = make_ip_layout(1, n, param, sizeof(T));
+        const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), aligned16(x) && aligned16(y));
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
             return s;
         return hip_status(launch_scan_ip<T>(x, n, y, n, 1, n, static_cast<uint32_t*>(ws),
@@ -182,7 +189,9 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
     if (rows > 0 && cols > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
     if (rows == 0 || cols == 0) return CANON_OK;
     if (is_ip(policy, param)) {
-        const IpLayout ip = make_ip_layout(rows, cols, param, sizeof(T));
+        const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
+                        (ldy * sizeof(T)) % 16 == 0;
+        const IpLayout ip = make_ip_layout(rows, cols, param, sizeof(T), al);
         if (canon_status_t s =
                 check_ws(ws, ws_bytes, scan_rows_ws(rows, cols, policy, param, sizeof(T))))
             return s;

@@ -186,27 +186,342 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan(const T* __restrict__ x,
     }
 }
 
+template <typename T>
+static hipError_t launch_ip_nodes(T* nodes, const IpLayout& lay, hipStream_t s)
+{
+    for (int k0 = 0; k0 + 1 < lay.levels; k0 += kIpLevelsPerPass) {
+        const uint64_t blocks = (lay.cnt[k0] + (1u << kIpLevelsPerPass) - 1) >> kIpLevelsPerPass;
+        const uint64_t nit = lay.nseg * blocks;
+        const unsigned g = (unsigned)(nit < kIpMaxGrid ? nit : kIpMaxGrid);
+        hipLaunchKernelGGL((k_ip_nodes<T>), dim3(g), dim3(kIpThreads), 0, s, nodes, lay, k0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// ============================================================================
+// Fast path: L = 64 * E * RV with RV = 2^LOGRV in {1, ..., 8} (a row is RV
+// wave-wide 16-byte loads), 16-byte aligned rows.  A tile is 32 / RV rows;
+// each thread holds 8 vectors: wave w owns rows w*RW .. w*RW + RW-1
+// (RW = 8 / RV), vector u = row-in-wave u / RV, row-vector q = u % RV, lanes
+// (q * 64 + lane) * E + e.  The lane tree of a row has three kinds of levels:
+// inside a vector (static), across the 64 lanes (xor butterfly), across the
+// RV vectors of the row (in the thread).
+// ============================================================================
+template <typename T, int LOGRV>
+struct IpFast {
+    static constexpr int E = Elem<T>::E;
+    static constexpr int LOGE = Elem<T>::LOGE;
+    static constexpr int RV = 1 << LOGRV;
+    static constexpr int NV = 8;
+    static constexpr int RW = NV / RV;
+    static constexpr int LOGRW = 3 - LOGRV;
+    static constexpr int R = 4 * RW;  // rows per tile
+    static constexpr int L = 64 * E * RV;
+};
+
+// butterfly partner value of `v` held by lane ^ 2^K
+template <int K, typename T>
+__device__ __forceinline__ T xor_lane(T v)
+{
+    return shfl_xor<(1 << K)>(v);
+}
+
+template <typename T, int LOGRV, bool GUARD>
+__device__ __forceinline__ void ipf_load(const T* __restrict__ xs, uint64_t cols, uint64_t row0,
+                                         int w, int lane, T (&a)[8][Elem<T>::E])
+{
+    using F = IpFast<T, LOGRV>;
+#pragma unroll
+    for (int u = 0; u < F::NV; ++u) {
+        const uint64_t row = row0 + (uint64_t)w * F::RW + u / F::RV;
+        const uint64_t gi = row * F::L + (uint64_t)((u % F::RV) * 64 + lane) * F::E;
+        if (!GUARD || gi + F::E <= cols) {
+            load_vec(xs + gi, a[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < F::E; ++e) a[u][e] = gi + e < cols ? xs[gi + e] : neg_zero<T>();
+        }
+    }
+}
+
+// In-wave pairwise prefix down each lane over the wave's RW rows (Sklansky
+// over rows; the upper half receives the end of the lower half).
+template <typename T, int LOGRV>
+__device__ __forceinline__ void ipf_columns_in_wave(T (&a)[8][Elem<T>::E])
+{
+    using F = IpFast<T, LOGRV>;
+#pragma unroll
+    for (int h = 1; h < F::RW; h *= 2)
+#pragma unroll
+        for (int r = 0; r < F::RW; ++r)
+            if (r & h)
+#pragma unroll
+                for (int q = 0; q < F::RV; ++q)
+#pragma unroll
+                    for (int e = 0; e < F::E; ++e)
+                        a[r * F::RV + q][e] = a[((r & ~(2 * h - 1)) + h - 1) * F::RV + q][e] +
+                                              a[r * F::RV + q][e];
+}
+
+// Kernel 1 (fast): tile totals, lane by lane, into node level 0.
+template <typename T, int LOGRV>
+__global__ __launch_bounds__(kIpThreads) void k_ip_totals_fast(const T* __restrict__ x,
+                                                               uint64_t ldx, uint64_t cols,
+                                                               uint32_t* __restrict__ err,
+                                                               T* __restrict__ nodes, IpLayout lay)
+{
+    using F = IpFast<T, LOGRV>;
+    __shared__ T s_tot[4][F::L];
+    if (blockIdx.x == 0 && threadIdx.x == 0) err[0] = 0u;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t items = lay.nseg * lay.tps;
+    for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const uint64_t seg = item / lay.tps, t = item % lay.tps;
+        const T* xs = x + seg * ldx;
+        T a[8][F::E];
+        const uint64_t row0 = t * F::R;
+        if ((row0 + F::R) * F::L <= cols) ipf_load<T, LOGRV, false>(xs, cols, row0, w, lane, a);
+        else ipf_load<T, LOGRV, true>(xs, cols, row0, w, lane, a);
+        // complete tree over the wave's rows, per lane
+#pragma unroll
+        for (int h = 1; h < F::RW; h *= 2)
+#pragma unroll
+            for (int r = 0; r < F::RW; r += 2 * h)
+#pragma unroll
+                for (int q = 0; q < F::RV; ++q)
+#pragma unroll
+                    for (int e = 0; e < F::E; ++e)
+                        a[r * F::RV + q][e] = a[r * F::RV + q][e] + a[(r + h) * F::RV + q][e];
+#pragma unroll
+        for (int q = 0; q < F::RV; ++q)
+#pragma unroll
+            for (int e = 0; e < F::E; ++e) s_tot[w][(q * 64 + lane) * F::E + e] = a[q][e];
+        __syncthreads();
+        T* dst = ip_node(nodes, lay, 0, seg, t);
+        for (int j = threadIdx.x; j < F::L; j += kIpThreads)
+            dst[j] = (s_tot[0][j] + s_tot[1][j]) + (s_tot[2][j] + s_tot[3][j]);
+        __syncthreads();
+    }
+}
+
+// Kernel 3 (fast): the scan.
+template <typename T, int LOGRV>
+__global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict__ x, uint64_t ldx,
+                                                             T* __restrict__ y, uint64_t ldy,
+                                                             uint64_t cols,
+                                                             const T* __restrict__ nodes,
+                                                             IpLayout lay)
+{
+    using F = IpFast<T, LOGRV>;
+    constexpr int E = F::E, RV = F::RV, RW = F::RW;
+    __shared__ T s_row[4][F::L];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t items = lay.nseg * lay.tps;
+
+    for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const uint64_t seg = item / lay.tps, t = item % lay.tps;
+        const T* xs = x + seg * ldx;
+        T* ys = y + seg * ldy;
+        const uint64_t row0 = t * F::R;
+        const bool full = (row0 + F::R) * F::L <= cols;
+        T a[8][E];
+        if (full) ipf_load<T, LOGRV, false>(xs, cols, row0, w, lane, a);
+        else ipf_load<T, LOGRV, true>(xs, cols, row0, w, lane, a);
+
+        // lane prefixes: inside the wave, across the 4 waves, then the nodes
+        // of the earlier tiles (right-nested, lowest level first)
+        ipf_columns_in_wave<T, LOGRV>(a);
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                s_row[w][(q * 64 + lane) * E + e] = a[(RW - 1) * RV + q][e];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int j = (q * 64 + lane) * E + e;
+                const T t0 = s_row[0][j], t1 = s_row[1][j], t2 = s_row[2][j];
+                if (w & 1) {
+                    const T s = (w & 2) ? t2 : t0;
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) a[r * RV + q][e] = s + a[r * RV + q][e];
+                }
+                if (w & 2) {
+                    const T s = t0 + t1;
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) a[r * RV + q][e] = s + a[r * RV + q][e];
+                }
+            }
+        T b[RV][E];
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e) b[q][e] = neg_zero<T>();
+        for (int k = 0; k < lay.levels && (t >> k) != 0; ++k) {
+            if (!((t >> k) & 1)) continue;
+            const T* h = ip_node(nodes, lay, k, seg, (t >> k) - 1);
+#pragma unroll
+            for (int q = 0; q < RV; ++q) {
+                T hv[E];
+                load_vec(h + (q * 64 + lane) * E, hv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) a[r * RV + q][e] = hv[e] + a[r * RV + q][e];
+                    b[q][e] = hv[e] + b[q][e];
+                }
+            }
+        }
+        // the B row of each wave's first row: the A row just above it
+        __syncthreads();  // s_row is reused
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                s_row[w][(q * 64 + lane) * E + e] = a[(RW - 1) * RV + q][e];
+        __syncthreads();
+        if (w > 0) {
+#pragma unroll
+            for (int q = 0; q < RV; ++q)
+#pragma unroll
+                for (int e = 0; e < E; ++e) b[q][e] = s_row[w - 1][(q * 64 + lane) * E + e];
+        }
+
+        // walk every lane up its row's tree.  For row r: A = a[row r],
+        // B = a[row r-1] (b for the wave's first row).  pa[l] / pb[l]: value of
+        // this lane-group's subtree at lane level l for the A / B row.
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            T val[RV][E];
+            T pa[RV], pb[RV];  // subtree values after the in-vector levels
+#pragma unroll
+            for (int q = 0; q < RV; ++q) {
+                const T* A = a[r * RV + q];
+                const T* Bv = (r == 0) ? b[q] : a[(r - 1) * RV + q];
+                // in-vector levels: slot e's sibling at each level
+                T av[E], bv[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    av[e] = A[e];
+                    bv[e] = Bv[e];
+                    val[q][e] = A[e];
+                }
+#pragma unroll
+                for (int h = 1; h < E; h *= 2) {
+                    // subtrees of size h at slots s*h; pair (2i, 2i+1)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int node = e / h, sib = node ^ 1;
+                        val[q][e] = (node & 1) ? av[sib * h] + val[q][e] : val[q][e] + bv[sib * h];
+                    }
+#pragma unroll
+                    for (int i = 0; i < E / (2 * h); ++i) {
+                        av[2 * i * h] = av[2 * i * h] + av[(2 * i + 1) * h];
+                        bv[2 * i * h] = bv[2 * i * h] + bv[(2 * i + 1) * h];
+                    }
+                }
+                pa[q] = av[0];
+                pb[q] = bv[0];
+            }
+            // lane levels
+#define CANON_IP_LANE_LEVEL(K)                                                          \
+    {                                                                                   \
+        const bool right = (lane >> (K)) & 1;                                           \
+        _Pragma("unroll") for (int q = 0; q < RV; ++q)                                  \
+        {                                                                               \
+            const T oa = xor_lane<K>(pa[q]);                                            \
+            const T ob = xor_lane<K>(pb[q]);                                            \
+            _Pragma("unroll") for (int e = 0; e < E; ++e) val[q][e] =                   \
+                right ? (oa + val[q][e]) : (val[q][e] + ob);                            \
+            pa[q] = right ? (oa + pa[q]) : (pa[q] + oa);                                \
+            pb[q] = right ? (ob + pb[q]) : (pb[q] + ob);                                \
+        }                                                                               \
+    }
+            CANON_IP_LANE_LEVEL(0)
+            CANON_IP_LANE_LEVEL(1)
+            CANON_IP_LANE_LEVEL(2)
+            CANON_IP_LANE_LEVEL(3)
+            CANON_IP_LANE_LEVEL(4)
+            CANON_IP_LANE_LEVEL(5)
+#undef CANON_IP_LANE_LEVEL
+            // vector levels (inside the thread)
+#pragma unroll
+            for (int h = 1; h < RV; h *= 2) {
+#pragma unroll
+                for (int q = 0; q < RV; ++q) {
+                    const int node = q / h, sib = node ^ 1;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        val[q][e] = (node & 1) ? pa[sib * h] + val[q][e] : val[q][e] + pb[sib * h];
+                }
+#pragma unroll
+                for (int i = 0; i < RV / (2 * h); ++i) {
+                    pa[2 * i * h] = pa[2 * i * h] + pa[(2 * i + 1) * h];
+                    pb[2 * i * h] = pb[2 * i * h] + pb[(2 * i + 1) * h];
+                }
+            }
+            // store row r
+            const uint64_t row = row0 + (uint64_t)w * RW + r;
+#pragma unroll
+            for (int q = 0; q < RV; ++q) {
+                const uint64_t gi = row * F::L + (uint64_t)(q * 64 + lane) * E;
+                if (full || gi + E <= cols) {
+                    store_vec(ys + gi, val[q]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if (gi + e < cols) ys[gi + e] = val[q][e];
+                }
+            }
+        }
+        __syncthreads();  // s_row is rewritten by the next tile
+    }
+}
+
 // ---------------------------------------------------------------- launcher
+template <typename T, int LOGRV>
+static hipError_t launch_ip_fast(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                                 uint32_t* err, T* nodes, const IpLayout& lay, hipStream_t s)
+{
+    const uint64_t items = lay.nseg * lay.tps;
+    const unsigned grid = (unsigned)(items < kIpMaxGrid ? items : kIpMaxGrid);
+    hipLaunchKernelGGL((k_ip_totals_fast<T, LOGRV>), dim3(grid), dim3(kIpThreads), 0, s, x, ldx,
+                       cols, err, nodes, lay);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_ip_nodes<T>(nodes, lay, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ip_scan_fast<T, LOGRV>), dim3(grid), dim3(kIpThreads), 0, s, x, ldx, y,
+                       ldy, cols, nodes, lay);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,
                           uint64_t cols, uint32_t* err, T* nodes, const IpLayout& lay,
                           hipStream_t s)
 {
     if (nseg == 0 || cols == 0) return hipSuccess;
+    if (lay.fast_logrv >= 0) {
+        switch (lay.fast_logrv) {
+            case 0: return launch_ip_fast<T, 0>(x, ldx, y, ldy, cols, err, nodes, lay, s);
+            case 1: return launch_ip_fast<T, 1>(x, ldx, y, ldy, cols, err, nodes, lay, s);
+            case 2: return launch_ip_fast<T, 2>(x, ldx, y, ldy, cols, err, nodes, lay, s);
+            default: return launch_ip_fast<T, 3>(x, ldx, y, ldy, cols, err, nodes, lay, s);
+        }
+    }
     const uint64_t items = lay.nseg * lay.tps;
     const unsigned grid = (unsigned)(items < kIpMaxGrid ? items : kIpMaxGrid);
     hipLaunchKernelGGL((k_ip_totals<T>), dim3(grid), dim3(kIpThreads), 0, s, x, ldx, cols, err,
                        nodes, lay);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    for (int k0 = 0; k0 + 1 < lay.levels; k0 += kIpLevelsPerPass) {
-        const uint64_t blocks = (lay.cnt[k0] + (1u << kIpLevelsPerPass) - 1) >> kIpLevelsPerPass;
-        const uint64_t nit = lay.nseg * blocks;
-        const unsigned g = (unsigned)(nit < kIpMaxGrid ? nit : kIpMaxGrid);
-        hipLaunchKernelGGL((k_ip_nodes<T>), dim3(g), dim3(kIpThreads), 0, s, nodes, lay, k0);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    e = launch_ip_nodes<T>(nodes, lay, s);
+    if (e != hipSuccess) return e;
     const size_t lds = ip_lds_bytes(lay, sizeof(T));
     hipLaunchKernelGGL((k_ip_scan<T>), dim3(grid), dim3(kIpThreads), lds, s, x, ldx, y, ldy, cols,
                        nodes, lay);

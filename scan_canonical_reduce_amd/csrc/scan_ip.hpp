@@ -28,12 +28,15 @@ struct IpLayout {
     uint64_t cnt[kIpMaxLevels];
     uint64_t off[kIpMaxLevels];
     uint64_t total;  // elements of node storage
+    int fast_logrv;  // >= 0: register path with L = 64 * E * 2^fast_logrv; -1: LDS path
 };
 
 // LDS budget (elements) for the per-row trees of one tile: (R + 1) * 2 * Lp
 inline uint64_t ip_lds_elems(size_t elem_size) { return elem_size == 8 ? 8192 : 16384; }
 
-inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t elem_size)
+// `aligned`: rows start on 16-byte boundaries (x, y and both pitches).
+inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t elem_size,
+                               bool aligned)
 {
     IpLayout lay{};
     lay.L = L;
@@ -41,8 +44,16 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
     while ((1ull << lp) < L) ++lp;
     lay.lp_log = lp;
     const uint64_t Lp = 1ull << lp;
-    int rl = kIpMaxRLog;
-    while (rl > 0 && ((1ull << rl) + 1) * 2 * Lp > ip_lds_elems(elem_size)) --rl;
+    const int loge = elem_size == 8 ? 1 : 2;
+    lay.fast_logrv = -1;
+    int rl;
+    if (aligned && Lp == L && lp >= loge + 6 && lp <= loge + 9) {
+        lay.fast_logrv = lp - loge - 6;
+        rl = 5 - lay.fast_logrv;  // 32 / RV rows per tile
+    } else {
+        rl = kIpMaxRLog;
+        while (rl > 0 && ((1ull << rl) + 1) * 2 * Lp > ip_lds_elems(elem_size)) --rl;
+    }
     lay.r_log = rl;
     lay.nseg = nseg;
     const uint64_t rows = (cols + L - 1) / L;

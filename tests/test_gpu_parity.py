@@ -258,3 +258,16 @@ def test_scan_rows_iterated_pairwise(canon, dtype, L):
         got = to_host(canon.scan_rows(Xd[:, :cols], "iterated_pairwise", L))
         want = oracle.scan_rows(X, "iterated_pairwise", L, cols=cols)[:, :cols]
         assert_bit_exact(got, want, f"cols={cols}")
+
+
+@pytest.mark.parametrize("dtype,L", [(np.float64, 128), (np.float64, 256), (np.float64, 1024),
+                                     (np.float32, 256), (np.float32, 512)])
+def test_scan_rows_iterated_pairwise_aligned_pitch(canon, dtype, L):
+    """Row pitch a multiple of 16 bytes: the register path of the scan."""
+    rows, ld = 9, 40960
+    X = synth.generate(rows * ld, "mixed_magnitude", 410 + L, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for cols in (L, 3 * L + 8, 20000, 40960):
+        got = to_host(canon.scan_rows(Xd[:, :cols], "iterated_pairwise", L))
+        want = oracle.scan_rows(X, "iterated_pairwise", L, cols=cols)[:, :cols]
+        assert_bit_exact(got, want, f"cols={cols}")
