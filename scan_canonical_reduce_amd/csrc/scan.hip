@@ -194,6 +194,7 @@ struct ScanTile {
         if constexpr (LOGV >= 1) vector_level<0>();
         if constexpr (LOGV >= 2) vector_level<1>();
         if constexpr (LOGV >= 3) vector_level<2>();
+        if constexpr (LOGV >= 4) vector_level<3>();
     }
 
     // Wave-level merges (the tile's 4 waves), given the 4 wave totals.

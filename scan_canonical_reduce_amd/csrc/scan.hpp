@@ -44,14 +44,13 @@ inline ScanLayout make_scan_layout(uint64_t ntiles, uint64_t width)
     return l;
 }
 
-#ifndef CANON_SCAN_LOGV
-#define CANON_SCAN_LOGV 3
-#endif
-// log2 of the 16-byte vectors each thread of the single-pass scan holds
+// log2 of the 16-byte vectors each thread of the single-pass scan holds:
+// 128 bytes of the tile per thread (measured best on MI355X: fewer bytes per
+// tile leave each tile's look-back round trip exposed, more spill registers)
 template <typename T>
 constexpr int scan_log_v()
 {
-    return CANON_SCAN_LOGV;
+    return sizeof(T) == 8 ? 3 : 4;
 }
 
 template <typename T>

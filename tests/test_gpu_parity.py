@@ -146,7 +146,7 @@ def test_scan_1m_uniform(canon, policy, param):
                                           ("block_dyadic", 256), ("block_dyadic", 4096),
                                           ("block_dyadic", 8192), ("block_dyadic", 65536)])
 def test_scan_tails(canon, dtype, policy, param):
-    S = 4096 if dtype == np.float64 else 8192
+    S = 4096 if dtype == np.float64 else 16384  # elements per scan tile
     x = synth.generate(70 * S + 999, "mixed_magnitude", 12, dtype)
     want_all = oracle.scan(x, policy, param)
     for n in (1, 2, 3, 17, S - 1, S, S + 1, 3 * S + 5, 64 * S - 1, 64 * S, 64 * S + 1, 65 * S + 17,
@@ -198,10 +198,10 @@ def test_scan_special_values(canon):
 @pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16),
                                           ("block_dyadic", 4096)])
 def test_scan_rows(canon, dtype, policy, param):
-    rows, ld = 19, 3 * 8192 + 40
+    rows, ld = 19, 3 * 16384 + 40
     X = synth.generate(rows * ld, "mixed_magnitude", 17, dtype).reshape(rows, ld)
     Xd = to_dev(X)
-    for cols in (1, 16, 4095, 4096, 8193, 3 * 8192 + 33):
+    for cols in (1, 16, 4095, 4096, 8193, 16385, 3 * 16384 + 33):
         got = to_host(canon.scan_rows(Xd[:, :cols], policy, param))
         want = oracle.scan_rows(X, policy, param, cols=cols)[:, :cols]
         assert_bit_exact(got, want, f"cols={cols}")
