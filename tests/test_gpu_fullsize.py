@@ -1,0 +1,90 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same entry points, same 16-byte aligned resident inputs).
+
+The reduce and every scan are compared element by element with the oracle
+(its streaming form handles every prefix at this size); iterated_pairwise
+at 2^27 is checked on every prefix of the first 2^22 elements, on sampled
+prefixes evaluated from scratch, and through scan/reduce consistency."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import assert_bit_exact, to_dev, to_host  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def canon():
+    import scan_canonical_reduce_amd as c
+    c.lib()
+    return c
+
+
+def _probes(n, k=6, seed=77):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, n // 2, n - 1], rng.integers(0, n, k)]))
+
+
+@pytest.mark.parametrize("name,L,init", [("reduce_1m", 16, 0.0), ("reduce_1m", 128, 0.0),
+                                         ("reduce_2e28_f64", 128, 1.0),
+                                         ("reduce_2e29_f32", 128, 1.0)])
+def test_reduce_full_size(canon, name, L, init):
+    print(f"[fullsize] reduce {name} L={L}", flush=True)
+    x = synth.config_input(name)
+    got = to_host(canon.reduce(to_dev(x), L, init)).reshape(1)
+    assert_bit_exact(got, [oracle.reduce(x, L, init)], name)
+
+
+def test_rows_full_size(canon):
+    print("[fullsize] rows 16384x4096", flush=True)
+    X = synth.config_input("rows_16384x4096")
+    Xd = to_dev(X)
+    assert_bit_exact(to_host(canon.reduce_rows(Xd, 16, 0.0)), oracle.reduce_rows(X, 16, 0.0),
+                     "reduce_rows")
+    Y = to_host(canon.scan_rows(Xd, "block_dyadic", 16))
+    W = oracle.scan_rows(X, "block_dyadic", 16)
+    assert_bit_exact(Y, W, "scan_rows")
+    # 16 divides 4096: each row's last prefix is the pairwise value of the row
+    assert_bit_exact(Y[:, -1], oracle.reduce_rows(X, 1, -0.0), "row back")
+
+
+@pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 256)])
+def test_scan_1m_full(canon, policy, param):
+    print(f"[fullsize] scan_1m {policy}<{param}>", flush=True)
+    x = synth.config_input("scan_1m")
+    y = to_host(canon.scan(to_dev(x), policy, param))
+    assert_bit_exact(y, oracle.scan(x, policy, param), policy)
+    assert_bit_exact(y[-1:], to_host(canon.reduce(to_dev(x), 1, -0.0)).reshape(1), "back")
+
+
+@pytest.mark.parametrize("name,policy,param", [
+    ("scan_2e27_f64", "block_dyadic", 16), ("scan_2e27_f64", "block_dyadic", 256),
+    ("scan_2e28_f32", "block_dyadic", 256)])
+def test_scan_full_size(canon, name, policy, param):
+    print(f"[fullsize] {name} {policy}<{param}>", flush=True)
+    x = synth.config_input(name)
+    xd = to_dev(x)
+    y = canon.scan(xd, policy, param)
+    yh = to_host(y)
+    assert_bit_exact(yh, oracle.scan(x, policy, param), name)
+
+
+@pytest.mark.parametrize("L", [128, 16])
+def test_scan_iterated_pairwise_full_size(canon, L):
+    print(f"[fullsize] scan_2e27_f64 iterated_pairwise<{L}>", flush=True)
+    x = synth.config_input("scan_2e27_f64")
+    xd = to_dev(x)
+    y = canon.scan(xd, "iterated_pairwise", L)
+    head = 1 << 22
+    assert_bit_exact(to_host(y[:head]), oracle.scan(x[:head], "iterated_pairwise", L), "head")
+    idx = _probes(x.size)
+    got = to_host(y[torch.from_numpy(idx).to("cuda")])
+    want = np.array([oracle.scan_prefix(x, int(i), "iterated_pairwise", L) for i in idx])
+    assert_bit_exact(got, want, "probes")
+    back = to_host(canon.reduce(xd, L, -0.0)).reshape(1)
+    assert_bit_exact(to_host(y[-1:]), back, "scan back == reduce (GPU)")
