@@ -15,7 +15,15 @@ reads N*8 bytes, a scan reads and writes N*8 bytes each.  Before timing,
 every result is checked bit for bit against the CPU oracle (full reduce,
 sampled scan prefixes evaluated from scratch).
 
+Inside the timed steps every op is bracketed by HIP events on the stream it
+runs on; the op with the largest mean time is the dominant kernel of the
+roofline object.  Its HBM traffic comes from the rocprofv3 FETCH_SIZE /
+WRITE_SIZE summary under profiles/ when that summary was taken from the
+kernel sources as they are now (their SHA-256 is stored with it), else null.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-check]
+       python bench.py --only copy ...   (a 2 GiB device copy: the reference
+                                          for scaling the PMC byte counters)
 """
 from __future__ import annotations
 
@@ -33,17 +41,58 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 N_MAIN = 1 << 28
 ROWS, COLS = 16384, 4096
+PROFILES = os.path.join(ROOT, "profiles")
+# sources whose kernels the traffic summaries describe
+KERNEL_SOURCES = ["device.hpp", "launch.hpp", "reduce.hpp", "reduce.hip", "scan.hpp",
+                  "scan_tile.hpp", "scan.hip", "scan_rows.hip", "scan_ip.hpp", "scan_ip.hip"]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "scan_canonical_reduce_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(f.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def workload_tag(op: str) -> str:
+    return "f64_16384x4096" if op.startswith("rows_") else "f64_n2e28"
+
+
+def read_traffic(op: str):
+    """HBM bytes per call of op from profiles/traffic_<op>_<workload>.txt
+    (lines 'key: value'), or None when missing or taken from other kernel
+    sources."""
+    path = os.path.join(PROFILES, f"traffic_{op}_{workload_tag(op)}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return {"fetch_bytes": int(kv["fetch_bytes_scaled"]),
+                "write_bytes": int(kv["write_bytes_scaled"]),
+                "bytes": int(kv["fetch_bytes_scaled"]) + int(kv["write_bytes_scaled"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-check", action="store_true", help="skip the oracle parity gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of ops to run (profiling)")
-    ap.add_argument("--reps", type=int, default=20, help="per-op timing repetitions")
     return ap.parse_args()
 
 
@@ -66,18 +115,23 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
+    only = set(args.only.split(",")) if args.only else None
+    want_rows = only is None or bool(only & {"rows_reduce", "rows_scan_bd16"})
+
     # ------------------------------------------------------------ inputs
     t0 = time.time()
     x_np = synth.config_input("reduce_2e28_f64")  # N = 2^28 mixed magnitude, seed 1003
-    X_np = synth.config_input("rows_16384x4096")
+    X_np = synth.config_input("rows_16384x4096") if want_rows else None
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s "
-        f"sha256(x)={synth.sha256(x_np)[:16]} sha256(X)={synth.sha256(X_np)[:16]}")
+        f"sha256(x)={synth.sha256(x_np)[:16]}"
+        + (f" sha256(X)={synth.sha256(X_np)[:16]}" if want_rows else ""))
     x = torch.from_numpy(x_np).to(dev)
-    X = torch.from_numpy(X_np).to(dev)
     y = torch.empty_like(x)
-    Y = torch.empty_like(X)
     r0 = torch.empty((), dtype=torch.float64, device=dev)
-    rr = torch.empty(ROWS, dtype=torch.float64, device=dev)
+    if want_rows:
+        X = torch.from_numpy(X_np).to(dev)
+        Y = torch.empty_like(X)
+        rr = torch.empty(ROWS, dtype=torch.float64, device=dev)
 
     have_ip = canon.scan_workspace_bytes(N_MAIN, "iterated_pairwise", 128, 8) > 0
     scans = [("scan_bd256", "block_dyadic", 256), ("scan_bd16", "block_dyadic", 16),
@@ -92,12 +146,14 @@ def main():
     ops["reduce"] = (lambda: canon.reduce(x, 128, 1.0, out=r0, ws=ws), N_MAIN * 8)
     for name, p, q in scans:
         ops[name] = ((lambda p=p, q=q: canon.scan(x, p, q, out=y, ws=ws)), 2 * N_MAIN * 8)
-    ops["rows_reduce"] = (lambda: canon.reduce_rows(X, 16, 0.0, out=rr), ROWS * COLS * 8)
-    ops["rows_scan_bd16"] = (lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y),
-                             2 * ROWS * COLS * 8)
-    if args.only:
-        keep = set(args.only.split(","))
-        ops = {k: v for k, v in ops.items() if k in keep}
+    if want_rows:
+        ops["rows_reduce"] = (lambda: canon.reduce_rows(X, 16, 0.0, out=rr), ROWS * COLS * 8)
+        ops["rows_scan_bd16"] = (lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y),
+                                 2 * ROWS * COLS * 8)
+    if only is not None:
+        if "copy" in only:  # calibration only, never part of the step
+            ops["copy"] = (lambda: y.copy_(x), 2 * N_MAIN * 8)
+        ops = {k: v for k, v in ops.items() if k in only}
 
     # ------------------------------------------------------- parity gate
     parity = {}
@@ -108,6 +164,8 @@ def main():
         probes = np.unique(np.concatenate([[0, 1, 4095, 4096, N_MAIN - 1],
                                            rng.integers(0, N_MAIN, 3)]))
         for name, (fn, _) in ops.items():
+            if name == "copy":
+                continue
             fn()
             torch.cuda.synchronize()
             if name == "reduce":
@@ -134,42 +192,30 @@ def main():
             print(json.dumps({"error": "parity gate failed", "parity": parity}))
             sys.exit(1)
 
-    # ------------------------------------------------- per-op timing
-    stream = torch.cuda.current_stream()
-    per_op = {}
-    for name, (fn, nbytes) in ops.items():
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.reps)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in evs)
-        med = ms[len(ms) // 2]
-        per_op[name] = {"ms_median": med, "ms_p10": ms[len(ms) // 10],
-                        "ms_p90": ms[(9 * len(ms)) // 10], "bytes": nbytes,
-                        "GBps": nbytes / (med * 1e-3) / 1e9,
-                        "pct_hbm_peak": 100.0 * nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        log(f"[bench] {name:15s} median {med * 1e3:9.1f} us  "
-            f"{per_op[name]['GBps']:8.1f} GB/s  {per_op[name]['pct_hbm_peak']:5.1f}% of peak")
-
     # ------------------------------------------------------ step timing
-    def step():
-        for fn, _ in ops.values():
-            fn()
+    # every op is bracketed by events on the stream it is launched on (the
+    # binding launches on torch's current stream)
+    stream = torch.cuda.current_stream()
+    names = list(ops)
+
+    def step(evs=None):
+        for i, name in enumerate(names):
+            if evs is not None:
+                evs[i][0].record(stream)
+            ops[name][0]()
+            if evs is not None:
+                evs[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    all_evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in names] for _ in range(args.steps)]
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(all_evs[k])
     b.record(stream)
     torch.cuda.synchronize()
     total_ms = a.elapsed_time(b)
@@ -177,14 +223,30 @@ def main():
     step_bytes = sum(nb for _, nb in ops.values())
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: the op with the largest share of the step
-    dom = max(per_op, key=lambda k: per_op[k]["ms_median"])
-    d = per_op[dom]
-    roofline = {"bound": "hbm", "achieved": round(d["GBps"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": dom}
+    per_op = {}
+    for i, name in enumerate(names):
+        ms = sorted(all_evs[k][i][0].elapsed_time(all_evs[k][i][1]) for k in range(args.steps))
+        mean = sum(ms) / len(ms)
+        nbytes = ops[name][1]
+        per_op[name] = {"ms_mean": mean, "ms_median": ms[len(ms) // 2], "ms_min": ms[0],
+                        "ms_max": ms[-1], "bytes": nbytes,
+                        "GBps": nbytes / (mean * 1e-3) / 1e9,
+                        "pct_hbm_peak": 100.0 * nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] {name:15s} mean {mean * 1e3:9.1f} us  "
+            f"{per_op[name]['GBps']:8.1f} GB/s  {per_op[name]['pct_hbm_peak']:5.1f}% of peak")
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(x_np, X_np)
+    # dominant kernel: the op with the largest mean time in the timed steps
+    dom = max(per_op, key=lambda k: per_op[k]["ms_mean"])
+    d = per_op[dom]
+    traffic = read_traffic(dom)
+    roofline = {"bound": "hbm", "achieved": round(d["GBps"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(d["GBps"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic["bytes"] if traffic else None, "kernel": dom,
+                "algorithmic_bytes": d["bytes"], "us_mean": round(d["ms_mean"] * 1e3, 1)}
+    if traffic:
+        roofline["traffic_detail"] = traffic
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x_np, X_np, have_ip)
 
     out = {
         "metric": "GB/s and % HBM peak, bit-exact canonical fp64 reduce & scan, N=2^28, 1 GPU",
@@ -216,31 +278,36 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(x_np, X_np):
+def cpu_baseline(x_np, X_np, have_ip):
     """The oracle (single-threaded C, as it stands) on a bounded sample of the
-    same step: every op over the first 2^26 of the 2^28 elements (the row ops
-    over the first 4096 of 16384 rows)."""
+    same step: reduce and the pairwise / block_dyadic scans over all 2^28
+    elements, the iterated_pairwise<128> scan over the first 2^26 (its oracle
+    combines 128 lane values per prefix, about 10x slower per element), the
+    row ops over all 16384 rows.  value = algorithmic bytes / seconds."""
     import oracle
-    n = 1 << 26
-    xs = x_np[:n]
-    Xs = X_np[:4096]
+    n = x_np.size
     nbytes = 0
     t0 = time.perf_counter()
-    oracle.reduce(xs, 128, 1.0)
+    oracle.reduce(x_np, 128, 1.0)
     nbytes += n * 8
     for p, q in (("block_dyadic", 256), ("block_dyadic", 16), ("pairwise", 0)):
-        oracle.scan(xs, p, q)
+        oracle.scan(x_np, p, q)
         nbytes += 2 * n * 8
-    oracle.reduce_rows(Xs, 16, 0.0)
-    nbytes += Xs.size * 8
-    oracle.scan_rows(Xs, "block_dyadic", 16)
-    nbytes += 2 * Xs.size * 8
+    sample = "reduce and the block_dyadic<256>, block_dyadic<16> and pairwise scans over all 2^28"
+    if have_ip:
+        n_ip = 1 << 26
+        oracle.scan(x_np[:n_ip], "iterated_pairwise", 128)
+        nbytes += 2 * n_ip * 8
+        sample += "; iterated_pairwise<128> over the first 2^26"
+    if X_np is not None:
+        oracle.reduce_rows(X_np, 16, 0.0)
+        nbytes += X_np.size * 8
+        oracle.scan_rows(X_np, "block_dyadic", 16)
+        nbytes += 2 * X_np.size * 8
+        sample += "; row reduce and row scan over all 16384 rows"
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "reduce and the block_dyadic<256>, block_dyadic<16> and pairwise scans over "
-                      "the first 2^26 of the 2^28 elements; row reduce and row scan over the "
-                      "first 4096 of 16384 rows",
-            "seconds": round(dt, 2)}
+            "sample": sample, "seconds": round(dt, 2)}
 
 
 if __name__ == "__main__":

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libcanon.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libcanon")
 
-SOURCES = ["api.cpp", "reduce.hip", "scan.hip", "scan_ip.hip"]
+SOURCES = ["api.cpp", "reduce.hip", "scan.hip", "scan_rows.hip", "scan_ip.hip"]
 
 # -ffp-contract=off: no FMA contraction; no fast-math; packed FP32 disabled.
 HIPFLAGS = [
@@ -43,7 +43,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = OUT + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

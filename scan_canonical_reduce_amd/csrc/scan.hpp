@@ -9,13 +9,13 @@ namespace canon {
 constexpr int kScanThreads = 256;  // 4 waves
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kScanVec = 8;        // 16-byte vectors per thread per tile
-constexpr int kGroupLog = 6;       // tile nodes below this level are rebuilt from tile totals
+constexpr int kGroupLog = 6;       // tile nodes up to this level are rebuilt from tile totals
 constexpr int kMaxLevels = 48;
 
 // Workspace layout of a single-pass scan (offsets in 64-bit words).
 //   word 0: error word (low 32 bits); word 1: tile counter (low 32 bits)
 //   [tiles_off, +ntiles): published tile totals (tile-level 0 nodes)
-//   [level_off[k], +ceil(ntiles / 2^k)): published tile-level k nodes, k >= kGroupLog
+//   [level_off[k], +ceil(ntiles / 2^k)): published tile-level k nodes, k > kGroupLog
 // Each published word holds one value (one lane value for the
 // iterated_pairwise scan, whose nodes are vectors of L words).
 struct ScanLayout {
@@ -35,7 +35,7 @@ inline ScanLayout make_scan_layout(uint64_t ntiles, uint64_t width)
     uint64_t off = l.tiles_off + ntiles * width;
     for (int k = 0; k < kMaxLevels; ++k) {
         l.level_off[k] = off;
-        if (k >= kGroupLog) {
+        if (k > kGroupLog) {
             uint64_t cnt = (ntiles + (1ull << k) - 1) >> k;
             off += cnt * width;
         }

@@ -1,0 +1,97 @@
+// Canonical inclusive scan of many independent rows (gfx950): policies
+// pairwise and block_dyadic<B> (canonical-reduce README, P4229R0 "Summary" /
+// "Key Design Points").  The in-tile network is ScanTile (scan_tile.hpp).
+#include "device.hpp"
+#include "launch.hpp"
+#include "scan.hpp"
+#include "scan_tile.hpp"
+
+namespace canon {
+
+// Row-batched scan: one workgroup per row, the row's tiles in order; the tile
+// nodes come from a binary-counter stack of the row's earlier tile totals
+// (held in LDS by thread 0).
+template <typename T, int MODE, bool ALIGNED, int LOGV>
+__global__ __launch_bounds__(kScanThreads) void k_scan_rows(const T* x, uint64_t ldx, T* y,
+                                                            uint64_t ldy, uint64_t rows,
+                                                            uint64_t cols, int b_log)
+{
+    using ST = ScanTile<T, MODE, LOGV>;
+    __shared__ T s_tot[kScanWaves];
+    __shared__ T s_stack[kMaxLevels];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t ntiles = (cols + (1ull << ST::LOG_S) - 1) >> ST::LOG_S;
+
+    for (uint64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const T* xr = x + row * ldx;
+        T* yr = y + row * ldy;
+        for (uint64_t t = 0; t < ntiles; ++t) {
+            const uint64_t g0 =
+                (t << ST::LOG_S) + ((uint64_t)w << ST::LOG_WSPAN) + (uint64_t)lane * ST::E;
+            ST st;
+            st.template load<ALIGNED>(xr, cols, g0);
+            st.begin(b_log);
+            st.in_wave(lane);
+            if (lane == 63) s_tot[w] = st.last(ST::V - 1);
+            __syncthreads();
+            const T t0 = s_tot[0], t1 = s_tot[1], t2 = s_tot[2], t3 = s_tot[3];
+            const T t01 = t0 + t1;
+            const T tile_total = t01 + (t2 + t3);
+            st.across_waves(w, t0, t01, t2);
+            for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
+                if ((t >> k) & 1) st.apply_all(ST::LOG_S + 1 + k, s_stack[k]);
+            st.template store<ALIGNED>(yr, cols, g0);
+            __syncthreads();  // everyone has read s_tot and s_stack
+            if (threadIdx.x == 0) {
+                T acc = tile_total;
+                const int merges = __builtin_ctzll(~t);
+                for (int l = 0; l < merges; ++l) acc = s_stack[l] + acc;
+                s_stack[merges] = acc;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int MODE, bool ALIGNED>
+static hipError_t launch_scan_rows_k(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
+                                     uint64_t cols, int b_log, hipStream_t s)
+{
+    // grid-stride over rows with about as many workgroups as fit at once
+    constexpr auto kern = k_scan_rows<T, MODE, ALIGNED, scan_log_v<T>()>;
+    uint64_t grid = resident_grid<kern>(kScanThreads);
+    if (grid > rows) grid = rows;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), 0, s, x, ldx, y, ldy, rows,
+                       cols, b_log);
+    return hipGetLastError();
+}
+
+template <typename T, int MODE>
+static hipError_t launch_scan_rows_m(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
+                                     uint64_t cols, int b_log, bool aligned, hipStream_t s)
+{
+    if (aligned) return launch_scan_rows_k<T, MODE, true>(x, ldx, y, ldy, rows, cols, b_log, s);
+    return launch_scan_rows_k<T, MODE, false>(x, ldx, y, ldy, rows, cols, b_log, s);
+}
+
+template <typename T>
+hipError_t launch_scan_rows(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
+                            uint64_t cols, bool pairwise, int b_log, bool aligned, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (pairwise || b_log == 0)
+        return launch_scan_rows_m<T, 0>(x, ldx, y, ldy, rows, cols, 0, aligned, s);
+    if constexpr (Elem<T>::LOGE >= 2) {
+        if (b_log < Elem<T>::LOGE)
+            return launch_scan_rows_m<T, 2>(x, ldx, y, ldy, rows, cols, b_log, aligned, s);
+    }
+    return launch_scan_rows_m<T, 1>(x, ldx, y, ldy, rows, cols, b_log, aligned, s);
+}
+
+template hipError_t launch_scan_rows<double>(const double*, uint64_t, double*, uint64_t, uint64_t,
+                                             uint64_t, bool, int, bool, hipStream_t);
+template hipError_t launch_scan_rows<float>(const float*, uint64_t, float*, uint64_t, uint64_t,
+                                            uint64_t, bool, int, bool, hipStream_t);
+
+}  // namespace canon

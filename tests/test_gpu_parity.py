@@ -156,6 +156,22 @@ def test_scan_tails(canon, dtype, policy, param):
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_scan_every_block_size(canon, dtype):
+    """Every B = 2^b from 1 to beyond one tile: the fork to block values falls
+    at every level inside and above the tile; several tiles, a ragged tail."""
+    S = 4096 if dtype == np.float64 else 16384
+    x = synth.generate(5 * S + 123, "mixed_magnitude", 18, dtype)
+    for b in range(0, 17):
+        B = 1 << b
+        assert_bit_exact(gpu_scan(canon, x, "block_dyadic", B), oracle.scan(x, "block_dyadic", B),
+                         f"B={B}")
+        # an unaligned start (element loads and stores)
+        xd = to_dev(x)
+        y = to_host(canon.scan(xd[1:], "block_dyadic", B))
+        assert_bit_exact(y, oracle.scan(x[1:], "block_dyadic", B), f"unaligned B={B}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 16),
                                           ("block_dyadic", 256)])
 def test_scan_many_tiles(canon, dtype, policy, param):
@@ -205,6 +221,19 @@ def test_scan_rows(canon, dtype, policy, param):
         got = to_host(canon.scan_rows(Xd[:, :cols], policy, param))
         want = oracle.scan_rows(X, policy, param, cols=cols)[:, :cols]
         assert_bit_exact(got, want, f"cols={cols}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_scan_rows_every_block_size(canon, dtype):
+    S = 4096 if dtype == np.float64 else 16384
+    rows, cols, ld = 5, 2 * S + 77, 2 * S + 128
+    X = synth.generate(rows * ld, "mixed_magnitude", 19, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for b in range(0, 17):
+        B = 1 << b
+        got = to_host(canon.scan_rows(Xd[:, :cols], "block_dyadic", B))
+        want = oracle.scan_rows(X, "block_dyadic", B, cols=cols)[:, :cols]
+        assert_bit_exact(got, want, f"B={B}")
 
 
 def test_scan_rows_shape_of_workload(canon):
