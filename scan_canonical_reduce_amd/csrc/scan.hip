@@ -206,9 +206,44 @@ __global__ void k_scan_init(uint64_t* __restrict__ ws, uint64_t total)
         ws[i] = i < 32 ? 0ull : nr;
 }
 
-// Single-pass scan: one workgroup per tile; tile numbers come from an atomic
-// ticket counter in the order workgroups start, so every tile waited on
-// belongs to a workgroup that is already running.
+// Every thread of the workgroup of tile t > 0: resolves the look-back into
+// s_h[k] = node (k, (t >> k) - 1) for every set bit k of t.  A publishing
+// tile first resolves what its climb needs, publishes, and only then waits
+// for the rest.
+template <typename T>
+__device__ __forceinline__ void run_lookback(uint64_t t, T tile_total, LookbackWords lw,
+                                             uint64_t* __restrict__ ws, const ScanLayout& lay,
+                                             uint32_t* err, T* s_low, T* s_g6, T* s_w3, T* s_h,
+                                             int w, int lane)
+{
+    const int top = climb_top(t);
+    if (w < 3)
+        lookback_collect<T>(t, lw, ws, lay, err, s_low, s_g6, w, lane);
+    else if (w == 3)
+        lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, 0, top);
+    if (top > kGroupLog) {
+        __syncthreads();
+        if (threadIdx.x == 0) lookback_climb<T>(t, top, tile_total, ws, lay, s_low, s_g6, s_w3);
+    }
+    if (w == 3) lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, top, 1 << 30);
+    __syncthreads();
+    if (threadIdx.x == 0) lookback_combine<T>(t, s_low, s_g6, s_w3, s_h);
+    __syncthreads();
+}
+
+// Shared memory of the look-back.
+template <typename T>
+struct LookbackShared {
+    T h[kMaxLevels];
+    T low[kGroupLog];
+    T g6[2];
+    T w3[kMaxLevels - kGroupLog];
+};
+
+// Single-pass scan, pairwise (MODE 0) or block_dyadic with B = 2 (MODE 2):
+// one workgroup per tile; tile numbers come from an atomic ticket counter in
+// the order workgroups start, so every tile waited on belongs to a workgroup
+// that is already running.
 template <typename T, int MODE, bool ALIGNED, int LOGV>
 __global__ __launch_bounds__(kScanThreads) void k_scan(const T* x, T* y, uint64_t n, int b_log,
                                                        uint64_t* __restrict__ ws, ScanLayout lay)
@@ -216,10 +251,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const T* x, T* y, uint64_
     using ST = ScanTile<T, MODE, LOGV>;
     __shared__ uint32_t s_tile;
     __shared__ T s_tot[kScanWaves];
-    __shared__ T s_h[kMaxLevels];
-    __shared__ T s_low[kGroupLog];
-    __shared__ T s_g6[2];
-    __shared__ T s_w3[kMaxLevels - kGroupLog];
+    __shared__ LookbackShared<T> s_lb;
     uint32_t* err = reinterpret_cast<uint32_t*>(ws);
     uint32_t* counter = reinterpret_cast<uint32_t*>(ws + 1);
 
@@ -234,7 +266,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const T* x, T* y, uint64_
     st.template load<ALIGNED>(x, n, g0);
     LookbackWords lw{};
     if (t > 0) lw = lookback_issue<T>(t, ws, lay, w, lane);
-    st.begin(b_log);
+    st.begin(b_log, g0);
     st.in_wave(lane);
 
     if (lane == 63) s_tot[w] = st.last(ST::V - 1);
@@ -245,25 +277,227 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const T* x, T* y, uint64_
     if (threadIdx.x == 0) publish(ws + lay.tiles_off + t, tile_total);
     st.across_waves(w, t0, t01, t2);
     if (t > 0) {
-        // a publishing tile first resolves what its climb needs, publishes,
-        // and only then waits for the rest
-        const int top = climb_top(t);
-        if (w < 3)
-            lookback_collect<T>(t, lw, ws, lay, err, s_low, s_g6, w, lane);
-        else
-            lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, 0, top);
-        if (top > kGroupLog) {
-            __syncthreads();
-            if (threadIdx.x == 0) lookback_climb<T>(t, top, tile_total, ws, lay, s_low, s_g6, s_w3);
-        }
-        if (w == 3) lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, top, 1 << 30);
-        __syncthreads();
-        if (threadIdx.x == 0) lookback_combine<T>(t, s_low, s_g6, s_w3, s_h);
-        __syncthreads();
+        run_lookback<T>(t, tile_total, lw, ws, lay, err, s_lb.low, s_lb.g6, s_lb.w3, s_lb.h, w,
+                        lane);
         for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
-            if ((t >> k) & 1) st.apply_all(ST::LOG_S + 1 + k, s_h[k]);
+            if ((t >> k) & 1) st.apply_all(ST::LOG_S + 1 + k, s_lb.h[k]);
     }
     st.template store<ALIGNED>(y, n, g0);
+}
+
+// Canonical inclusive pairwise scan of a tile's block totals, one value
+// per block: thread tau holds blocks tau*m .. tau*m + m - 1 (m = 2^lm, at
+// most 2^LMX), the same network as the elements' (levels inside a thread,
+// across lanes, across the 4 waves), so a[k] ends as the pairwise value
+// of the block totals up to and including its block.
+template <typename T, int LMX>
+struct BlockScan {
+    static constexpr int M = 1 << LMX;
+    T a[M];
+    T tot;  // value of the thread's last block
+
+    __device__ __forceinline__ void load(const T* s, int tau, int lm, int nblk)
+    {
+        const int m = 1 << lm;
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const int j = tau * m + k;
+            a[k] = (k < m && j < nblk) ? s[j] : neg_zero<T>();
+        }
+    }
+
+    __device__ __forceinline__ void receive(T s)
+    {
+#pragma unroll
+        for (int k = 0; k < M; ++k) a[k] = s + a[k];
+        tot = s + tot;
+    }
+
+    template <int K>
+    __device__ __forceinline__ void lane_level(int lane)
+    {
+        const T src = from_lower_half_end<(1 << K)>(tot);
+        receive(((lane >> K) & 1) ? src : neg_zero<T>());
+    }
+
+    __device__ __forceinline__ void scan(int lm, int lane, int w, T* s_wt)
+    {
+        // levels inside the thread; entries k >= m stay -0.0
+#pragma unroll
+        for (int l = 1; l <= LMX; ++l) {
+            if (l <= lm) {
+#pragma unroll
+                for (int k = 0; k < M; ++k)
+                    if ((k >> (l - 1)) & 1) a[k] = a[((k >> l) << l) + (1 << (l - 1)) - 1] + a[k];
+            }
+        }
+        tot = a[0];
+#pragma unroll
+        for (int l = 1; l <= LMX; ++l)
+            if (l == lm) tot = a[(1 << l) - 1];
+        lane_level<0>(lane);
+        lane_level<1>(lane);
+        lane_level<2>(lane);
+        lane_level<3>(lane);
+        lane_level<4>(lane);
+        lane_level<5>(lane);
+        if (lane == 63) s_wt[w] = tot;
+        __syncthreads();
+        const T w0 = s_wt[0], w1 = s_wt[1], w2 = s_wt[2];
+        if (w & 1) receive((w & 2) ? w2 : w0);
+        if (w & 2) receive(w0 + w1);
+    }
+};
+
+// Single-pass block_dyadic scan with B >= E.  With n = qB + r, the value at
+// a block's interior is C + W, C = PW(x[0..qB)) the pairwise value at the end
+// of the previous block, W the pairwise prefix inside the block; at a block
+// end it is the pairwise value there.  So the levels above b reduce to one
+// pairwise scan over block totals:
+//   B < tile:  the in-tile network stops at level b (W in every element, the
+//              block total at every block end); the block totals go through
+//              BlockScan (levels above b inside the tile), then the tile-level
+//              nodes are added on the left of each block value (right-nested,
+//              lowest level first), giving G(P_j) for every block j and
+//              G(-0.0) in front of block 0; an element outputs
+//              G(P_{j-1}) + W, a block end G(P_j).
+//   B >= tile: the whole tile lies in one block, the in-tile network is
+//              pairwise; tile-level nodes up to level b go to every element,
+//              those above b into one carry c (every element outputs c + W)
+//              and, at a tile that closes a block, into its last element.
+// BIG: B >= tile.  LMX bounds log2 of the blocks each thread holds in
+// BlockScan (B < tile).
+template <typename T, bool ALIGNED, int LOGV, bool BIG, int LMX>
+__global__ __launch_bounds__(kScanThreads) void k_scan_split(const T* x, T* y, uint64_t n,
+                                                             int b_log, uint64_t* __restrict__ ws,
+                                                             ScanLayout lay)
+{
+    using ST = ScanTile<T, 3, LOGV>;
+    constexpr int E = ST::E;
+    __shared__ uint32_t s_tile;
+    __shared__ T s_tot[kScanWaves];
+    __shared__ T s_tt;
+    __shared__ LookbackShared<T> s_lb;
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    T* s_blk = reinterpret_cast<T*>(s_dyn);  // nblk + 1 block values (B < tile)
+    uint32_t* err = reinterpret_cast<uint32_t*>(ws);
+    uint32_t* counter = reinterpret_cast<uint32_t*>(ws + 1);
+
+    if (threadIdx.x == 0)
+        s_tile = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint64_t t = s_tile;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t off0 = ((uint64_t)w << ST::LOG_WSPAN) + (uint64_t)lane * E;  // in the tile
+    const uint64_t g0 = (t << ST::LOG_S) + off0;
+
+    ST st;
+    st.template load<ALIGNED>(x, n, g0);
+    LookbackWords lw{};
+    if (t > 0) lw = lookback_issue<T>(t, ws, lay, w, lane);
+    st.begin(b_log, g0);
+    st.in_wave(lane);  // levels <= b
+
+    if (lane == 63) s_tot[w] = st.last(ST::V - 1);
+    __syncthreads();
+    const T t0 = s_tot[0], t1 = s_tot[1], t2 = s_tot[2], t3 = s_tot[3];
+    const T t01 = t0 + t1;
+    st.across_waves(w, t0, t01, t2);  // levels <= b
+
+    if constexpr (BIG) {
+        const T tile_total = t01 + (t2 + t3);
+        if (threadIdx.x == 0) publish(ws + lay.tiles_off + t, tile_total);
+        T c = neg_zero<T>();
+        bool forked = false;
+        if (t > 0) {
+            run_lookback<T>(t, tile_total, lw, ws, lay, err, s_lb.low, s_lb.g6, s_lb.w3, s_lb.h,
+                            w, lane);
+            const uint64_t bmask = (1ull << b_log) - 1;
+            const bool closes = threadIdx.x == kScanThreads - 1 &&
+                                (((t + 1) << ST::LOG_S) & bmask) == 0;
+            // levels up to b (every element), then the levels above b
+            int k = 0;
+#pragma unroll 1
+            for (; k < kMaxLevels && (t >> k) != 0 && ST::LOG_S + 1 + k <= b_log; ++k)
+                if ((t >> k) & 1) st.apply_all(ST::LOG_S + 1 + k, s_lb.h[k]);
+#pragma unroll 1
+            for (; k < kMaxLevels && (t >> k) != 0; ++k) {
+                if (!((t >> k) & 1)) continue;
+                const T s = s_lb.h[k];
+                forked = true;
+                c = s + c;
+                if (closes) st.v[ST::V - 1][E - 1] = s + st.v[ST::V - 1][E - 1];
+            }
+        }
+        if (!forked) {
+            st.template store<ALIGNED>(y, n, g0);
+            return;
+        }
+        const bool closes = threadIdx.x == kScanThreads - 1 &&
+                            ((((t + 1) << ST::LOG_S) & ((1ull << b_log) - 1)) == 0);
+#pragma unroll
+        for (int u = 0; u < ST::V; ++u) {
+            T o[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                o[e] = (closes && u == ST::V - 1 && e == E - 1) ? st.v[u][e] : c + st.v[u][e];
+            st.template put<ALIGNED>(y, n, g0, u, o);
+        }
+    } else {
+    // ---- B < tile: block totals, one pairwise scan over them
+    const int nb_log = ST::LOG_S - b_log;  // log2 of the blocks in the tile
+    const int nblk = 1 << nb_log;
+    const int lm = nb_log > 8 ? nb_log - 8 : 0;
+    const uint64_t bmask = (1ull << b_log) - 1;
+#pragma unroll
+    for (int u = 0; u < ST::V; ++u) {
+        const uint64_t end = off0 + (uint64_t)u * 64 * E + E;  // one past the vector
+        if ((end & bmask) == 0) s_blk[(end >> b_log) - 1] = st.v[u][E - 1];
+    }
+    __syncthreads();
+    BlockScan<T, LMX> bs;
+    const int tau = threadIdx.x;
+    bs.load(s_blk, tau, lm, nblk);
+    bs.scan(lm, lane, w, s_tot);
+    if (tau == (nblk >> lm) - 1) s_tt = bs.tot;  // the tile's complete tree
+    __syncthreads();
+    const T tile_total = s_tt;
+    if (threadIdx.x == 0) publish(ws + lay.tiles_off + t, tile_total);
+    T g = neg_zero<T>();
+    if (t > 0) {
+        run_lookback<T>(t, tile_total, lw, ws, lay, err, s_lb.low, s_lb.g6, s_lb.w3, s_lb.h, w,
+                        lane);
+        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
+            if ((t >> k) & 1) {
+                bs.receive(s_lb.h[k]);
+                g = s_lb.h[k] + g;
+            }
+    }
+    // s_blk[j + 1] = G(P_j), s_blk[0] = G(-0.0); every read of the block
+    // totals above happened before the barriers since
+    {
+        const int m = 1 << lm;
+#pragma unroll
+        for (int k = 0; k < BlockScan<T, LMX>::M; ++k) {
+            const int j = tau * m + k;
+            if (k < m && j < nblk) s_blk[j + 1] = bs.a[k];
+        }
+        if (threadIdx.x == 0) s_blk[0] = g;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < ST::V; ++u) {
+        const uint64_t off = off0 + (uint64_t)u * 64 * E;
+        const int j = (int)(off >> b_log);
+        const bool end = ((off + E) & bmask) == 0;
+        const T cj = s_blk[j];
+        T o[E];
+#pragma unroll
+        for (int e = 0; e < E - 1; ++e) o[e] = cj + st.v[u][e];
+        o[E - 1] = end ? s_blk[j + 1] : cj + st.v[u][E - 1];
+        st.template put<ALIGNED>(y, n, g0, u, o);
+    }
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -285,6 +519,37 @@ static hipError_t launch_scan_m(const T* x, T* y, uint64_t n, int b_log, bool al
     return launch_scan_k<T, MODE, false>(x, y, n, b_log, ws, lay, s);
 }
 
+template <typename T, bool ALIGNED, bool BIG, int LMX>
+static hipError_t launch_split_k(const T* x, T* y, uint64_t n, int b_log, uint64_t* ws,
+                                 const ScanLayout& lay, hipStream_t s)
+{
+    constexpr int LOG_S = scan_tile_log<T>();
+    const size_t shmem = BIG ? 0 : ((1ull << (LOG_S - b_log)) + 1) * sizeof(T);
+    hipLaunchKernelGGL((k_scan_split<T, ALIGNED, scan_log_v<T>(), BIG, LMX>),
+                       dim3((unsigned)lay.ntiles), dim3(kScanThreads), shmem, s, x, y, n, b_log,
+                       ws, lay);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_split(const T* x, T* y, uint64_t n, int b_log, bool aligned,
+                               uint64_t* ws, const ScanLayout& lay, hipStream_t s)
+{
+    // blocks per thread in the block scan: 2^(log2(tile / B) - 8) when that is > 1
+    constexpr int LOG_S = scan_tile_log<T>();
+    if (b_log >= LOG_S) {
+        if (aligned) return launch_split_k<T, true, true, 0>(x, y, n, b_log, ws, lay, s);
+        return launch_split_k<T, false, true, 0>(x, y, n, b_log, ws, lay, s);
+    }
+    const int lm = LOG_S - b_log > 8 ? LOG_S - b_log - 8 : 0;
+    if (lm <= 2) {
+        if (aligned) return launch_split_k<T, true, false, 2>(x, y, n, b_log, ws, lay, s);
+        return launch_split_k<T, false, false, 2>(x, y, n, b_log, ws, lay, s);
+    }
+    if (aligned) return launch_split_k<T, true, false, 4>(x, y, n, b_log, ws, lay, s);
+    return launch_split_k<T, false, false, 4>(x, y, n, b_log, ws, lay, s);
+}
+
 template <typename T>
 hipError_t launch_scan(const T* x, T* y, uint64_t n, bool pairwise, int b_log, bool aligned,
                        uint64_t* ws, const ScanLayout& lay, hipStream_t s)
@@ -300,7 +565,7 @@ hipError_t launch_scan(const T* x, T* y, uint64_t n, bool pairwise, int b_log, b
     if constexpr (Elem<T>::LOGE >= 2) {
         if (b_log < Elem<T>::LOGE) return launch_scan_m<T, 2>(x, y, n, b_log, aligned, ws, lay, s);
     }
-    return launch_scan_m<T, 1>(x, y, n, b_log, aligned, ws, lay, s);
+    return launch_split<T>(x, y, n, b_log, aligned, ws, lay, s);
 }
 
 template hipError_t launch_scan<double>(const double*, double*, uint64_t, bool, int, bool,

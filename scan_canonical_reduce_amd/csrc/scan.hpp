@@ -45,10 +45,19 @@ inline ScanLayout make_scan_layout(uint64_t ntiles, uint64_t width)
 }
 
 // log2 of the 16-byte vectors each thread of the single-pass scan holds:
-// 128 bytes of the tile per thread (measured best on MI355X: fewer bytes per
-// tile leave each tile's look-back round trip exposed, more spill registers)
+// 256 bytes of the tile per thread for both types (measured best on MI355X:
+// fewer bytes per tile leave more tiles, each with its look-back round trip;
+// more cost occupancy)
 template <typename T>
 constexpr int scan_log_v()
+{
+    return 4;
+}
+
+// The same for the row-batched scan, whose tiles hold 128 bytes per thread
+// in double (a 4096-element row is one tile).
+template <typename T>
+constexpr int scan_rows_log_v()
 {
     return sizeof(T) == 8 ? 3 : 4;
 }

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_rows(const T* x, uint64_t
                 (t << ST::LOG_S) + ((uint64_t)w << ST::LOG_WSPAN) + (uint64_t)lane * ST::E;
             ST st;
             st.template load<ALIGNED>(xr, cols, g0);
-            st.begin(b_log);
+            st.begin(b_log, g0);
             st.in_wave(lane);
             if (lane == 63) s_tot[w] = st.last(ST::V - 1);
             __syncthreads();
@@ -59,7 +59,7 @@ static hipError_t launch_scan_rows_k(const T* x, uint64_t ldx, T* y, uint64_t ld
                                      uint64_t cols, int b_log, hipStream_t s)
 {
     // grid-stride over rows with about as many workgroups as fit at once
-    constexpr auto kern = k_scan_rows<T, MODE, ALIGNED, scan_log_v<T>()>;
+    constexpr auto kern = k_scan_rows<T, MODE, ALIGNED, scan_rows_log_v<T>()>;
     uint64_t grid = resident_grid<kern>(kScanThreads);
     if (grid > rows) grid = rows;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), 0, s, x, ldx, y, ldy, rows,

@@ -35,14 +35,19 @@
 namespace canon {
 
 // Scan state of one tile.  MODE 0: pairwise.  MODE 1: block_dyadic with
-// B >= E (a 16-byte vector never straddles two blocks).  MODE 2: block_dyadic
-// with B = 2 < E (float: two blocks per vector).
+// B >= E (a 16-byte vector never straddles two blocks), carries kept per
+// vector.  MODE 2: block_dyadic with B = 2 < E (float: two blocks per
+// vector).  MODE 3: block_dyadic with B >= E, levels <= b only: the levels
+// above b are left to the kernel, which runs them on the block totals.
 //
-// block_dyadic keeps, per block, a carry c (nodes received at levels above
-// b, right-nested) and the block end's pairwise value pe; levels <= b build
-// the in-block prefix W in v.  From level b+1 on ("fork"), every level
-// updates c and pe of the receiving blocks and never touches v again.
-template <typename T, int MODE, int LOGV_ = 3>
+// Levels <= b build the in-block prefix W in v.  From level b+1 on ("fork"),
+// the elements of a block share one carry c, the nodes received at levels
+// above b combined right-nested, and output c + W; only the block's last
+// element keeps adding what it receives to its own value, which thereby
+// becomes the pairwise value of the prefix ending there, its output.  Above
+// b the end of a lower half is always a block end, so the value a receiving
+// half takes is always the last element's value.
+template <typename T, int MODE, int LOGV_>
 struct ScanTile {
     static constexpr int E = Elem<T>::E;
     static constexpr int LOGE = Elem<T>::LOGE;
@@ -50,20 +55,29 @@ struct ScanTile {
     static constexpr int V = 1 << LOGV;
     static constexpr int LOG_WSPAN = LOGE + 6 + LOGV;  // elements per wave (log2)
     static constexpr int LOG_S = LOG_WSPAN + 2;        // elements per tile (log2)
-    static constexpr bool BD = MODE != 0;
+    static constexpr bool BD = MODE == 1 || MODE == 2;  // carries per vector
     static constexpr int NB = MODE == 2 ? E / 2 : 1;   // blocks per vector
     static_assert(MODE != 2 || E == 4, "two-element blocks inside a vector: float only");
+    static_assert(V <= 32, "block-end mask holds one bit per vector");
 
     T v[V][E];
     T c[V][NB];
-    T pe[V][NB];
-    int b;        // log2 B
-    bool forked;  // a level above b has been applied
+    uint32_t endm;  // MODE 1: bit u set when slot E-1 of vector u ends a block
+    int b;          // log2 B
+    bool forked;    // a level above b has been applied
 
-    __device__ __forceinline__ void begin(int b_log)
+    // g0: sequence index of the thread's first element in the tile
+    __device__ __forceinline__ void begin(int b_log, uint64_t g0)
     {
         b = MODE == 2 ? 1 : b_log;
         forked = false;
+        endm = 0;
+        if constexpr (MODE == 1) {
+            const uint64_t bmask = (1ull << b) - 1;
+#pragma unroll
+            for (int u = 0; u < V; ++u)
+                if (((g0 + (uint64_t)u * 64 * E + E) & bmask) == 0) endm |= 1u << u;
+        }
     }
 
     // level lam merges two halves of one block (lam <= b); b is uniform, so
@@ -72,11 +86,7 @@ struct ScanTile {
 
     // value at the end of vector u's last slot: the source a receiving half
     // takes from the end of the lower half
-    __device__ __forceinline__ T last(int u) const
-    {
-        if constexpr (BD) return forked ? pe[u][NB - 1] : v[u][E - 1];
-        return v[u][E - 1];
-    }
+    __device__ __forceinline__ T last(int u) const { return v[u][E - 1]; }
 
     __device__ __forceinline__ void fork()
     {
@@ -84,10 +94,7 @@ struct ScanTile {
 #pragma unroll
             for (int u = 0; u < V; ++u)
 #pragma unroll
-                for (int k = 0; k < NB; ++k) {
-                    pe[u][k] = v[u][k * (E / NB) + (E / NB) - 1];
-                    c[u][k] = neg_zero<T>();
-                }
+                for (int k = 0; k < NB; ++k) c[u][k] = neg_zero<T>();
             forked = true;
         }
     }
@@ -100,14 +107,20 @@ struct ScanTile {
     // Every block of vector u receives s at level lam (lam > LOGE).
     __device__ __forceinline__ void apply_vec(int lam, T s, int u)
     {
+        if constexpr (MODE == 3)
+            if (!in_block(lam)) return;
         if (!BD || in_block(lam)) {
 #pragma unroll
             for (int e = 0; e < E; ++e) v[u][e] = s + v[u][e];
+        } else if constexpr (MODE == 1) {
+            c[u][0] = s + c[u][0];
+            const T t = s + v[u][E - 1];
+            v[u][E - 1] = ((endm >> u) & 1) ? t : v[u][E - 1];
         } else {
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 c[u][k] = s + c[u][k];
-                pe[u][k] = s + pe[u][k];
+                v[u][2 * k + 1] = s + v[u][2 * k + 1];
             }
         }
     }
@@ -116,6 +129,22 @@ struct ScanTile {
         maybe_fork(lam);
 #pragma unroll
         for (int u = 0; u < V; ++u) apply_vec(lam, s, u);
+    }
+
+    // Makes the compiler finish a level's additions before the next level:
+    // otherwise it defers those whose results feed no later level to the
+    // end, holding every received value in registers until then.
+    __device__ __forceinline__ void pin()
+    {
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[u][e]));
+            if constexpr (BD) {
+#pragma unroll
+                for (int k = 0; k < NB; ++k) asm volatile("" : "+v"(c[u][k]));
+            }
+        }
     }
 
     // Levels inside a vector (static positions).
@@ -131,11 +160,12 @@ struct ScanTile {
             // level 2 (float): slots 2, 3 receive slot 1
             maybe_fork(2);
             if (MODE == 2) {
-                // b = 1: the second block of the vector receives the first
+                // b = 1: the second block of the vector receives the end of
+                // the first
 #pragma unroll
                 for (int u = 0; u < V; ++u) {
-                    c[u][1] = pe[u][0] + c[u][1];
-                    pe[u][1] = pe[u][0] + pe[u][1];
+                    c[u][1] = v[u][1] + c[u][1];
+                    v[u][3] = v[u][1] + v[u][3];
                 }
             } else if (!BD || in_block(2)) {
 #pragma unroll
@@ -152,6 +182,8 @@ struct ScanTile {
     {
         constexpr int H = 1 << K;
         const int lam = LOGE + 1 + K;
+        if constexpr (MODE == 3)
+            if (!in_block(lam)) return;
         maybe_fork(lam);
         const bool upper = (lane >> K) & 1;
 #pragma unroll
@@ -159,6 +191,7 @@ struct ScanTile {
             const T src = from_lower_half_end<H>(last(u));
             apply_vec(lam, upper ? src : neg_zero<T>(), u);
         }
+        pin();
     }
 
     template <int K>
@@ -166,6 +199,8 @@ struct ScanTile {
     {
         constexpr int H = 1 << K;
         const int lam = LOGE + 7 + K;
+        if constexpr (MODE == 3)
+            if (!in_block(lam)) return;
         maybe_fork(lam);
         T src[V];
 #pragma unroll
@@ -174,6 +209,7 @@ struct ScanTile {
 #pragma unroll
         for (int u = 0; u < V; ++u)
             if (u & H) apply_vec(lam, src[u], u);
+        pin();
     }
 
     // All levels inside one wave's 2^LOG_WSPAN elements.
@@ -216,10 +252,24 @@ struct ScanTile {
         }
     }
 
+    // Writes vector u's outputs o[0..E) at sequence index g0 + u*64*E.
+    template <bool ALIGNED>
+    __device__ __forceinline__ void put(T* __restrict__ y, uint64_t n, uint64_t g0, int u,
+                                        const T (&o)[E]) const
+    {
+        const uint64_t gi = g0 + (uint64_t)u * 64 * E;
+        if (ALIGNED && gi + E <= n) {
+            store_vec(y + gi, o);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (gi + e < n) y[gi + e] = o[e];
+        }
+    }
+
     template <bool ALIGNED>
     __device__ __forceinline__ void store(T* __restrict__ y, uint64_t n, uint64_t g0) const
     {
-        const uint64_t bmask = (1ull << b) - 1;
 #pragma unroll
         for (int u = 0; u < V; ++u) {
             T o[E];
@@ -227,24 +277,16 @@ struct ScanTile {
 #pragma unroll
                 for (int e = 0; e < E; ++e) o[e] = v[u][e];
             } else {
-                const uint64_t gi = g0 + (uint64_t)u * 64 * E;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     constexpr int BS = E / NB;  // slots per block inside a vector
                     const int k = e / BS;
                     const bool end = (MODE == 2) ? ((e % BS) == BS - 1)
-                                                 : (e == E - 1 && ((gi + E) & bmask) == 0);
-                    o[e] = end ? pe[u][k] : c[u][k] + v[u][e];
+                                                 : (e == E - 1 && ((endm >> u) & 1));
+                    o[e] = end ? v[u][e] : c[u][k] + v[u][e];
                 }
             }
-            const uint64_t gi = g0 + (uint64_t)u * 64 * E;
-            if (ALIGNED && gi + E <= n) {
-                store_vec(y + gi, o);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (gi + e < n) y[gi + e] = o[e];
-            }
+            put<ALIGNED>(y, n, g0, u, o);
         }
     }
 };
