@@ -6,25 +6,33 @@
 
 namespace canon {
 
-// Workgroups of kernel KERN (with `threads` threads each) that fit on the
-// current device at once, cached per device.  Grid-stride and ticket-driven
-// kernels are launched with about this many workgroups: one workgroup per
-// tile or row would be bounded by the workgroup launch rate, not by memory.
+// Workgroups of kernel KERN (with `threads` threads and `shmem` bytes of
+// dynamic shared memory each) that fit on the current device at once, cached
+// per device and shared-memory size.  Grid-stride and ticket-driven kernels
+// are launched with about this many workgroups: one workgroup per tile or row
+// would be bounded by the workgroup launch rate, not by memory.
 template <auto KERN>
-uint64_t resident_grid(int threads)
+uint64_t resident_grid(int threads, size_t shmem = 0)
 {
-    static uint64_t cache[64] = {};
+    struct Entry {
+        int dev;
+        size_t shmem;
+        uint64_t grid;
+    };
+    static Entry cache[32] = {};
+    static int used = 0;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cache[dev] == 0) {
-        int cus = 0, per = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, KERN, threads, 0) != hipSuccess)
-            per = 0;
-        cache[dev] = (uint64_t)(cus > 0 ? cus : 256) * (uint64_t)(per > 0 ? per : 1);
-    }
-    return cache[dev];
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    for (int i = 0; i < used; ++i)
+        if (cache[i].dev == dev && cache[i].shmem == shmem) return cache[i].grid;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, KERN, threads, shmem) != hipSuccess)
+        per = 0;
+    const uint64_t grid = (uint64_t)(cus > 0 ? cus : 256) * (uint64_t)(per > 0 ? per : 1);
+    if (used < 32) cache[used++] = Entry{dev, shmem, grid};
+    return grid;
 }
 
 }  // namespace canon

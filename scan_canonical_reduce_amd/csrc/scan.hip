@@ -40,9 +40,9 @@ namespace canon {
 // on a chain of look-backs that grows with the number of tiles.  Every value
 // is fixed by position only.
 //
-// The words are read once right after the tile's own loads are issued
-// (lookback_issue), so that their latency overlaps the loads; words not
-// ready then are polled in lookback_collect.
+// The words are read once right after the loads of the workgroup's next
+// tile are issued (lookback_issue), so that they arrive with that data;
+// words not ready then are polled in lookback_collect.
 struct LookbackWords {
     uint64_t w;  // the word this lane of this wave reads (see lookback_slot)
 };
@@ -240,50 +240,83 @@ struct LookbackShared {
     T w3[kMaxLevels - kGroupLog];
 };
 
-// Single-pass scan, pairwise (MODE 0) or block_dyadic with B = 2 (MODE 2):
-// one workgroup per tile; tile numbers come from an atomic ticket counter in
-// the order workgroups start, so every tile waited on belongs to a workgroup
-// that is already running.
-template <typename T, int MODE, bool ALIGNED, int LOGV>
-__global__ __launch_bounds__(kScanThreads) void k_scan(const T* x, T* y, uint64_t n, int b_log,
-                                                       uint64_t* __restrict__ ws, ScanLayout lay)
+// Shared memory of a single-pass scan workgroup (the block values of
+// block_dyadic with B < tile are in dynamic shared memory).
+template <typename T>
+struct ScanShared {
+    uint32_t tile;
+    T tot[kScanWaves];
+    T tt;
+    LookbackShared<T> lb;
+};
+
+// What every phase of a single-pass scan workgroup needs.
+template <typename T>
+struct ScanCtx {
+    const T* x;
+    T* y;
+    uint64_t n;
+    int b_log;
+    uint64_t* ws;
+    const ScanLayout* lay;
+    uint32_t* err;
+    ScanShared<T>* sh;
+    T* blk;  // block values (B < tile)
+    int lane, w;
+};
+
+// Next tile number from the ticket counter, for the whole workgroup.  The
+// shared slot is rewritten only after a later barrier of the caller.
+template <typename T>
+__device__ __forceinline__ uint64_t next_ticket(const ScanCtx<T>& c)
 {
-    using ST = ScanTile<T, MODE, LOGV>;
-    __shared__ uint32_t s_tile;
-    __shared__ T s_tot[kScanWaves];
-    __shared__ LookbackShared<T> s_lb;
-    uint32_t* err = reinterpret_cast<uint32_t*>(ws);
-    uint32_t* counter = reinterpret_cast<uint32_t*>(ws + 1);
-
     if (threadIdx.x == 0)
-        s_tile = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c.sh->tile = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(c.ws + 1), 1u,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const uint64_t t = s_tile;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint64_t g0 = (t << ST::LOG_S) + ((uint64_t)w << ST::LOG_WSPAN) + (uint64_t)lane * ST::E;
-
-    ST st;
-    st.template load<ALIGNED>(x, n, g0);
-    LookbackWords lw{};
-    if (t > 0) lw = lookback_issue<T>(t, ws, lay, w, lane);
-    st.begin(b_log, g0);
-    st.in_wave(lane);
-
-    if (lane == 63) s_tot[w] = st.last(ST::V - 1);
-    __syncthreads();
-    const T t0 = s_tot[0], t1 = s_tot[1], t2 = s_tot[2], t3 = s_tot[3];
-    const T t01 = t0 + t1;
-    const T tile_total = t01 + (t2 + t3);
-    if (threadIdx.x == 0) publish(ws + lay.tiles_off + t, tile_total);
-    st.across_waves(w, t0, t01, t2);
-    if (t > 0) {
-        run_lookback<T>(t, tile_total, lw, ws, lay, err, s_lb.low, s_lb.g6, s_lb.w3, s_lb.h, w,
-                        lane);
-        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
-            if ((t >> k) & 1) st.apply_all(ST::LOG_S + 1 + k, s_lb.h[k]);
-    }
-    st.template store<ALIGNED>(y, n, g0);
+    return c.sh->tile;
 }
+
+// Pairwise (MODE 0) and block_dyadic with B = 2 in float (MODE 2): the tile
+// network through every level, the tile-level nodes applied to every element.
+template <typename T, int MODE, bool ALIGNED, int LOGV>
+struct FullTile {
+    using ST = ScanTile<T, MODE, LOGV>;
+    struct State {
+        ST st;
+    };
+    static constexpr int LOG_S = ST::LOG_S;
+
+    static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
+    {
+        return (t << LOG_S) + ((uint64_t)c.w << ST::LOG_WSPAN) + (uint64_t)c.lane * ST::E;
+    }
+    static __device__ __forceinline__ void load(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        s.st.template load<ALIGNED>(c.x, c.n, g0(t, c));
+    }
+    // in-tile scan; publishes and returns the tile total
+    static __device__ __forceinline__ T front(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        s.st.begin(c.b_log, g0(t, c));
+        s.st.in_wave(c.lane);
+        if (c.lane == 63) c.sh->tot[c.w] = s.st.last(ST::V - 1);
+        __syncthreads();
+        const T t0 = c.sh->tot[0], t1 = c.sh->tot[1], t2 = c.sh->tot[2], t3 = c.sh->tot[3];
+        const T t01 = t0 + t1;
+        const T total = t01 + (t2 + t3);
+        if (threadIdx.x == 0) publish(c.ws + c.lay->tiles_off + t, total);
+        s.st.across_waves(c.w, t0, t01, t2);
+        return total;
+    }
+    // the tile-level nodes (in c.sh->lb.h when t > 0), then the stores
+    static __device__ __forceinline__ void back(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
+            if ((t >> k) & 1) s.st.apply_all(LOG_S + 1 + k, c.sh->lb.h[k]);
+        s.st.template store<ALIGNED>(c.y, c.n, g0(t, c));
+    }
+};
 
 // Canonical inclusive pairwise scan of a tile's block totals, one value
 // per block: thread tau holds blocks tau*m .. tau*m + m - 1 (m = 2^lm, at
@@ -349,186 +382,235 @@ struct BlockScan {
     }
 };
 
-// Single-pass block_dyadic scan with B >= E.  With n = qB + r, the value at
-// a block's interior is C + W, C = PW(x[0..qB)) the pairwise value at the end
-// of the previous block, W the pairwise prefix inside the block; at a block
-// end it is the pairwise value there.  So the levels above b reduce to one
-// pairwise scan over block totals:
-//   B < tile:  the in-tile network stops at level b (W in every element, the
-//              block total at every block end); the block totals go through
-//              BlockScan (levels above b inside the tile), then the tile-level
-//              nodes are added on the left of each block value (right-nested,
-//              lowest level first), giving G(P_j) for every block j and
-//              G(-0.0) in front of block 0; an element outputs
+// Block_dyadic with B >= E.  With n = qB + r, the value at a block's
+// interior is C + W, C = PW(x[0..qB)) the pairwise value at the end of the
+// previous block, W the pairwise prefix inside the block; at a block end it
+// is the pairwise value there.  So the levels above b reduce to one pairwise
+// scan over block totals:
+//   B < tile (BIG false): the in-tile network stops at level b (W in every
+//              element, the block total at every block end); the block totals
+//              go through BlockScan (levels above b inside the tile), then the
+//              tile-level nodes are added on the left of each block value
+//              (right-nested, lowest level first), giving G(P_j) for every
+//              block j and G(-0.0) in front of block 0; an element outputs
 //              G(P_{j-1}) + W, a block end G(P_j).
-//   B >= tile: the whole tile lies in one block, the in-tile network is
+//   B >= tile (BIG):  the whole tile lies in one block, the in-tile network is
 //              pairwise; tile-level nodes up to level b go to every element,
 //              those above b into one carry c (every element outputs c + W)
 //              and, at a tile that closes a block, into its last element.
-// BIG: B >= tile.  LMX bounds log2 of the blocks each thread holds in
-// BlockScan (B < tile).
+// LMX bounds log2 of the blocks each thread holds in BlockScan.
 template <typename T, bool ALIGNED, int LOGV, bool BIG, int LMX>
-__global__ __launch_bounds__(kScanThreads) void k_scan_split(const T* x, T* y, uint64_t n,
-                                                             int b_log, uint64_t* __restrict__ ws,
-                                                             ScanLayout lay)
-{
+struct SplitTile {
     using ST = ScanTile<T, 3, LOGV>;
-    constexpr int E = ST::E;
-    __shared__ uint32_t s_tile;
-    __shared__ T s_tot[kScanWaves];
-    __shared__ T s_tt;
-    __shared__ LookbackShared<T> s_lb;
-    extern __shared__ __align__(16) unsigned char s_dyn[];
-    T* s_blk = reinterpret_cast<T*>(s_dyn);  // nblk + 1 block values (B < tile)
-    uint32_t* err = reinterpret_cast<uint32_t*>(ws);
-    uint32_t* counter = reinterpret_cast<uint32_t*>(ws + 1);
+    static constexpr int E = ST::E;
+    static constexpr int LOG_S = ST::LOG_S;
+    struct State {
+        ST st;
+        BlockScan<T, LMX> bs;
+    };
 
-    if (threadIdx.x == 0)
-        s_tile = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const uint64_t t = s_tile;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint64_t off0 = ((uint64_t)w << ST::LOG_WSPAN) + (uint64_t)lane * E;  // in the tile
-    const uint64_t g0 = (t << ST::LOG_S) + off0;
+    static __device__ __forceinline__ int off0(const ScanCtx<T>& c)
+    {
+        return (c.w << ST::LOG_WSPAN) + c.lane * E;  // in the tile
+    }
+    static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
+    {
+        return (t << LOG_S) + (uint64_t)off0(c);
+    }
+    static __device__ __forceinline__ void load(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        s.st.template load<ALIGNED>(c.x, c.n, g0(t, c));
+    }
 
-    ST st;
-    st.template load<ALIGNED>(x, n, g0);
-    LookbackWords lw{};
-    if (t > 0) lw = lookback_issue<T>(t, ws, lay, w, lane);
-    st.begin(b_log, g0);
-    st.in_wave(lane);  // levels <= b
+    static __device__ __forceinline__ T front(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        s.st.begin(c.b_log, g0(t, c));
+        s.st.in_wave(c.lane);  // levels <= b
+        if (c.lane == 63) c.sh->tot[c.w] = s.st.last(ST::V - 1);
+        __syncthreads();
+        const T t0 = c.sh->tot[0], t1 = c.sh->tot[1], t2 = c.sh->tot[2], t3 = c.sh->tot[3];
+        const T t01 = t0 + t1;
+        s.st.across_waves(c.w, t0, t01, t2);  // levels <= b
+        T total;
+        if constexpr (BIG) {
+            total = t01 + (t2 + t3);
+        } else {
+            const int nb_log = LOG_S - c.b_log;  // log2 of the blocks in the tile
+            const int nblk = 1 << nb_log;
+            const int lm = nb_log > 8 ? nb_log - 8 : 0;
+            const int bmask = (1 << c.b_log) - 1;
+            const int o0 = off0(c);
+#pragma unroll
+            for (int u = 0; u < ST::V; ++u) {
+                const int end = o0 + u * 64 * E + E;  // one past the vector
+                if ((end & bmask) == 0) c.blk[(end >> c.b_log) - 1] = s.st.v[u][E - 1];
+            }
+            __syncthreads();
+            s.bs.load(c.blk, threadIdx.x, lm, nblk);
+            s.bs.scan(lm, c.lane, c.w, c.sh->tot);
+            if ((int)threadIdx.x == (nblk >> lm) - 1) c.sh->tt = s.bs.tot;  // complete tree
+            __syncthreads();
+            total = c.sh->tt;
+        }
+        if (threadIdx.x == 0) publish(c.ws + c.lay->tiles_off + t, total);
+        return total;
+    }
 
-    if (lane == 63) s_tot[w] = st.last(ST::V - 1);
-    __syncthreads();
-    const T t0 = s_tot[0], t1 = s_tot[1], t2 = s_tot[2], t3 = s_tot[3];
-    const T t01 = t0 + t1;
-    st.across_waves(w, t0, t01, t2);  // levels <= b
-
-    if constexpr (BIG) {
-        const T tile_total = t01 + (t2 + t3);
-        if (threadIdx.x == 0) publish(ws + lay.tiles_off + t, tile_total);
-        T c = neg_zero<T>();
-        bool forked = false;
-        if (t > 0) {
-            run_lookback<T>(t, tile_total, lw, ws, lay, err, s_lb.low, s_lb.g6, s_lb.w3, s_lb.h,
-                            w, lane);
-            const uint64_t bmask = (1ull << b_log) - 1;
+    static __device__ __forceinline__ void back(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        const T* h = c.sh->lb.h;
+        if constexpr (BIG) {
+            T cr = neg_zero<T>();
+            bool forked = false;
             const bool closes = threadIdx.x == kScanThreads - 1 &&
-                                (((t + 1) << ST::LOG_S) & bmask) == 0;
+                                (((t + 1) << LOG_S) & ((1ull << c.b_log) - 1)) == 0;
             // levels up to b (every element), then the levels above b
             int k = 0;
 #pragma unroll 1
-            for (; k < kMaxLevels && (t >> k) != 0 && ST::LOG_S + 1 + k <= b_log; ++k)
-                if ((t >> k) & 1) st.apply_all(ST::LOG_S + 1 + k, s_lb.h[k]);
+            for (; k < kMaxLevels && (t >> k) != 0 && LOG_S + 1 + k <= c.b_log; ++k)
+                if ((t >> k) & 1) s.st.apply_all(LOG_S + 1 + k, h[k]);
 #pragma unroll 1
             for (; k < kMaxLevels && (t >> k) != 0; ++k) {
                 if (!((t >> k) & 1)) continue;
-                const T s = s_lb.h[k];
                 forked = true;
-                c = s + c;
-                if (closes) st.v[ST::V - 1][E - 1] = s + st.v[ST::V - 1][E - 1];
+                cr = h[k] + cr;
+                if (closes) s.st.v[ST::V - 1][E - 1] = h[k] + s.st.v[ST::V - 1][E - 1];
+            }
+            if (!forked) {
+                s.st.template store<ALIGNED>(c.y, c.n, g0(t, c));
+                return;
+            }
+#pragma unroll
+            for (int u = 0; u < ST::V; ++u) {
+                T o[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    o[e] = (closes && u == ST::V - 1 && e == E - 1) ? s.st.v[u][e]
+                                                                    : cr + s.st.v[u][e];
+                s.st.template put<ALIGNED>(c.y, c.n, g0(t, c), u, o);
+            }
+        } else {
+            const int nb_log = LOG_S - c.b_log;
+            const int nblk = 1 << nb_log;
+            const int lm = nb_log > 8 ? nb_log - 8 : 0;
+            T g = neg_zero<T>();
+            for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
+                if ((t >> k) & 1) {
+                    s.bs.receive(h[k]);
+                    g = h[k] + g;
+                }
+            // c.blk[j + 1] = G(P_j), c.blk[0] = G(-0.0); every read of the
+            // block totals happened before a barrier since
+            const int m = 1 << lm;
+#pragma unroll
+            for (int k = 0; k < BlockScan<T, LMX>::M; ++k) {
+                const int j = (int)threadIdx.x * m + k;
+                if (k < m && j < nblk) c.blk[j + 1] = s.bs.a[k];
+            }
+            if (threadIdx.x == 0) c.blk[0] = g;
+            __syncthreads();
+            const int bmask = (1 << c.b_log) - 1;
+            const int o0 = off0(c);
+#pragma unroll
+            for (int u = 0; u < ST::V; ++u) {
+                const int off = o0 + u * 64 * E;
+                const int j = off >> c.b_log;
+                const bool end = ((off + E) & bmask) == 0;
+                const T cj = c.blk[j];
+                T o[E];
+#pragma unroll
+                for (int e = 0; e < E - 1; ++e) o[e] = cj + s.st.v[u][e];
+                o[E - 1] = end ? c.blk[j + 1] : cj + s.st.v[u][E - 1];
+                s.st.template put<ALIGNED>(c.y, c.n, g0(t, c), u, o);
             }
         }
-        if (!forked) {
-            st.template store<ALIGNED>(y, n, g0);
-            return;
-        }
-        const bool closes = threadIdx.x == kScanThreads - 1 &&
-                            ((((t + 1) << ST::LOG_S) & ((1ull << b_log) - 1)) == 0);
-#pragma unroll
-        for (int u = 0; u < ST::V; ++u) {
-            T o[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                o[e] = (closes && u == ST::V - 1 && e == E - 1) ? st.v[u][e] : c + st.v[u][e];
-            st.template put<ALIGNED>(y, n, g0, u, o);
-        }
-    } else {
-    // ---- B < tile: block totals, one pairwise scan over them
-    const int nb_log = ST::LOG_S - b_log;  // log2 of the blocks in the tile
-    const int nblk = 1 << nb_log;
-    const int lm = nb_log > 8 ? nb_log - 8 : 0;
-    const uint64_t bmask = (1ull << b_log) - 1;
-#pragma unroll
-    for (int u = 0; u < ST::V; ++u) {
-        const uint64_t end = off0 + (uint64_t)u * 64 * E + E;  // one past the vector
-        if ((end & bmask) == 0) s_blk[(end >> b_log) - 1] = st.v[u][E - 1];
     }
-    __syncthreads();
-    BlockScan<T, LMX> bs;
-    const int tau = threadIdx.x;
-    bs.load(s_blk, tau, lm, nblk);
-    bs.scan(lm, lane, w, s_tot);
-    if (tau == (nblk >> lm) - 1) s_tt = bs.tot;  // the tile's complete tree
-    __syncthreads();
-    const T tile_total = s_tt;
-    if (threadIdx.x == 0) publish(ws + lay.tiles_off + t, tile_total);
-    T g = neg_zero<T>();
-    if (t > 0) {
-        run_lookback<T>(t, tile_total, lw, ws, lay, err, s_lb.low, s_lb.g6, s_lb.w3, s_lb.h, w,
-                        lane);
-        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
-            if ((t >> k) & 1) {
-                bs.receive(s_lb.h[k]);
-                g = s_lb.h[k] + g;
-            }
-    }
-    // s_blk[j + 1] = G(P_j), s_blk[0] = G(-0.0); every read of the block
-    // totals above happened before the barriers since
-    {
-        const int m = 1 << lm;
-#pragma unroll
-        for (int k = 0; k < BlockScan<T, LMX>::M; ++k) {
-            const int j = tau * m + k;
-            if (k < m && j < nblk) s_blk[j + 1] = bs.a[k];
-        }
-        if (threadIdx.x == 0) s_blk[0] = g;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < ST::V; ++u) {
-        const uint64_t off = off0 + (uint64_t)u * 64 * E;
-        const int j = (int)(off >> b_log);
-        const bool end = ((off + E) & bmask) == 0;
-        const T cj = s_blk[j];
-        T o[E];
-#pragma unroll
-        for (int e = 0; e < E - 1; ++e) o[e] = cj + st.v[u][e];
-        o[E - 1] = end ? s_blk[j + 1] : cj + st.v[u][E - 1];
-        st.template put<ALIGNED>(y, n, g0, u, o);
-    }
+};
+
+// One pipeline step of a persistent workgroup: tile t is in `cur` with its
+// front done (total published).  Takes the next ticket and issues its loads
+// into `nxt`, reads t's look-back words afresh right behind them, runs the
+// next tile's front (so a tile's total never waits for another tile's
+// look-back), then resolves t's look-back (its words have had the whole
+// front to arrive) and finishes t.  Returns false when no tile is left.
+template <class P, typename T>
+__device__ __forceinline__ bool pipe_step(typename P::State& cur, typename P::State& nxt,
+                                          uint64_t& t, T& total, const ScanCtx<T>& c)
+{
+    const uint64_t tn = next_ticket(c);
+    const bool more = tn < c.lay->ntiles;
+    if (more) P::load(nxt, tn, c);
+    LookbackWords lw{};
+    if (t > 0) lw = lookback_issue<T>(t, c.ws, *c.lay, c.w, c.lane);
+    T totn = total;
+    if (more) totn = P::front(nxt, tn, c);
+    if (t > 0)
+        run_lookback<T>(t, total, lw, c.ws, *c.lay, c.err, c.sh->lb.low, c.sh->lb.g6,
+                        c.sh->lb.w3, c.sh->lb.h, c.w, c.lane);
+    P::back(cur, t, c);
+    t = tn;
+    total = totn;
+    return more;
+}
+
+// Single-pass scan kernel: a persistent grid (about as many workgroups as
+// fit at once); each workgroup walks tiles in ticket order, two at a time
+// (pipe_step).  Tile numbers come from an atomic ticket counter in the order
+// workgroups ask, so every tile waited on belongs to a workgroup that is
+// running; no front waits for anything, so every published total arrives.
+template <class P, typename T>
+__global__ __launch_bounds__(kScanThreads) void k_scan(const T* x, T* y, uint64_t n, int b_log,
+                                                       uint64_t* __restrict__ ws, ScanLayout lay)
+{
+    __shared__ ScanShared<T> sh;
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    const ScanCtx<T> c{x,   y,  n, b_log, ws, &lay, reinterpret_cast<uint32_t*>(ws), &sh,
+                       reinterpret_cast<T*>(s_dyn), (int)(threadIdx.x & 63),
+                       (int)(threadIdx.x >> 6)};
+    uint64_t t = next_ticket(c);
+    if (t >= lay.ntiles) return;
+    typename P::State a, b;
+    P::load(a, t, c);
+    T total = P::front(a, t, c);
+    for (;;) {
+        if (!pipe_step<P, T>(a, b, t, total, c)) break;
+        if (!pipe_step<P, T>(b, a, t, total, c)) break;
     }
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int MODE, bool ALIGNED>
-static hipError_t launch_scan_k(const T* x, T* y, uint64_t n, int b_log, uint64_t* ws,
-                                const ScanLayout& lay, hipStream_t s)
+template <class P, typename T>
+static hipError_t launch_k(const T* x, T* y, uint64_t n, int b_log, uint64_t* ws,
+                           const ScanLayout& lay, size_t shmem, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_scan<T, MODE, ALIGNED, scan_log_v<T>()>),
-                       dim3((unsigned)lay.ntiles), dim3(kScanThreads), 0, s, x, y, n, b_log, ws,
-                       lay);
+    constexpr auto kern = k_scan<P, T>;
+    uint64_t grid = resident_grid<kern>(kScanThreads, shmem);
+    if (grid > lay.ntiles) grid = lay.ntiles;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), shmem, s, x, y, n, b_log,
+                       ws, lay);
     return hipGetLastError();
 }
 
 template <typename T, int MODE>
-static hipError_t launch_scan_m(const T* x, T* y, uint64_t n, int b_log, bool aligned,
-                                uint64_t* ws, const ScanLayout& lay, hipStream_t s)
+static hipError_t launch_full(const T* x, T* y, uint64_t n, int b_log, bool aligned,
+                              uint64_t* ws, const ScanLayout& lay, hipStream_t s)
 {
-    if (aligned) return launch_scan_k<T, MODE, true>(x, y, n, b_log, ws, lay, s);
-    return launch_scan_k<T, MODE, false>(x, y, n, b_log, ws, lay, s);
+    if (aligned)
+        return launch_k<FullTile<T, MODE, true, scan_log_v<T>()>>(x, y, n, b_log, ws, lay, 0, s);
+    return launch_k<FullTile<T, MODE, false, scan_log_v<T>()>>(x, y, n, b_log, ws, lay, 0, s);
 }
 
-template <typename T, bool ALIGNED, bool BIG, int LMX>
-static hipError_t launch_split_k(const T* x, T* y, uint64_t n, int b_log, uint64_t* ws,
-                                 const ScanLayout& lay, hipStream_t s)
+template <typename T, bool BIG, int LMX>
+static hipError_t launch_split_k(const T* x, T* y, uint64_t n, int b_log, bool aligned,
+                                 uint64_t* ws, const ScanLayout& lay, hipStream_t s)
 {
     constexpr int LOG_S = scan_tile_log<T>();
     const size_t shmem = BIG ? 0 : ((1ull << (LOG_S - b_log)) + 1) * sizeof(T);
-    hipLaunchKernelGGL((k_scan_split<T, ALIGNED, scan_log_v<T>(), BIG, LMX>),
-                       dim3((unsigned)lay.ntiles), dim3(kScanThreads), shmem, s, x, y, n, b_log,
-                       ws, lay);
-    return hipGetLastError();
+    if (aligned)
+        return launch_k<SplitTile<T, true, scan_log_v<T>(), BIG, LMX>>(x, y, n, b_log, ws, lay,
+                                                                      shmem, s);
+    return launch_k<SplitTile<T, false, scan_log_v<T>(), BIG, LMX>>(x, y, n, b_log, ws, lay,
+                                                                   shmem, s);
 }
 
 template <typename T>
@@ -537,17 +619,10 @@ static hipError_t launch_split(const T* x, T* y, uint64_t n, int b_log, bool ali
 {
     // blocks per thread in the block scan: 2^(log2(tile / B) - 8) when that is > 1
     constexpr int LOG_S = scan_tile_log<T>();
-    if (b_log >= LOG_S) {
-        if (aligned) return launch_split_k<T, true, true, 0>(x, y, n, b_log, ws, lay, s);
-        return launch_split_k<T, false, true, 0>(x, y, n, b_log, ws, lay, s);
-    }
+    if (b_log >= LOG_S) return launch_split_k<T, true, 0>(x, y, n, b_log, aligned, ws, lay, s);
     const int lm = LOG_S - b_log > 8 ? LOG_S - b_log - 8 : 0;
-    if (lm <= 2) {
-        if (aligned) return launch_split_k<T, true, false, 2>(x, y, n, b_log, ws, lay, s);
-        return launch_split_k<T, false, false, 2>(x, y, n, b_log, ws, lay, s);
-    }
-    if (aligned) return launch_split_k<T, true, false, 4>(x, y, n, b_log, ws, lay, s);
-    return launch_split_k<T, false, false, 4>(x, y, n, b_log, ws, lay, s);
+    if (lm <= 2) return launch_split_k<T, false, 2>(x, y, n, b_log, aligned, ws, lay, s);
+    return launch_split_k<T, false, 4>(x, y, n, b_log, aligned, ws, lay, s);
 }
 
 template <typename T>
@@ -561,9 +636,9 @@ hipError_t launch_scan(const T* x, T* y, uint64_t n, bool pairwise, int b_log, b
                        lay.total_words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (pairwise || b_log == 0) return launch_scan_m<T, 0>(x, y, n, 0, aligned, ws, lay, s);
+    if (pairwise || b_log == 0) return launch_full<T, 0>(x, y, n, 0, aligned, ws, lay, s);
     if constexpr (Elem<T>::LOGE >= 2) {
-        if (b_log < Elem<T>::LOGE) return launch_scan_m<T, 2>(x, y, n, b_log, aligned, ws, lay, s);
+        if (b_log < Elem<T>::LOGE) return launch_full<T, 2>(x, y, n, b_log, aligned, ws, lay, s);
     }
     return launch_split<T>(x, y, n, b_log, aligned, ws, lay, s);
 }
