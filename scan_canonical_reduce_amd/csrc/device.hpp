@@ -190,6 +190,14 @@ __device__ __forceinline__ T wait_word(uint64_t* slot, uint32_t* err)
     return unpack_word<T>(w);
 }
 
+// The value of a word read earlier, or, when it was not ready then, the
+// value once it is (wait_word).
+template <typename T>
+__device__ __forceinline__ T ready_or_wait(uint64_t w, uint64_t* slot, uint32_t* err)
+{
+    return w != not_ready_word<T>() ? unpack_word<T>(w) : wait_word<T>(slot, err);
+}
+
 // Binary-counter ("shift-reduce") stack of complete pairwise subtrees, one
 // entry per level, each entry a small vector of W values.  push(k, v) adds the
 // k-th (0-based) subtree of equal size; after n pushes, collapse(n) returns

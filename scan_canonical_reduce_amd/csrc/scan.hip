@@ -75,12 +75,6 @@ __device__ __forceinline__ LookbackWords lookback_issue(uint64_t t, uint64_t* __
     return w;
 }
 
-template <typename T>
-__device__ __forceinline__ T ready_or_wait(uint64_t w, uint64_t* slot, uint32_t* err)
-{
-    return w != not_ready_word<T>() ? unpack_word<T>(w) : wait_word<T>(slot, err);
-}
-
 // Complete tree over the 64 lane values, lower lanes on the left; node[k]
 // receives the value of the aligned 2^k group starting at lane
 // (r >> (k+1)) << (k+1) when bit k of r is set (r < 64), and the full tree

@@ -202,9 +202,9 @@ static hipError_t launch_ip_nodes(T* nodes, const IpLayout& lay, hipStream_t s)
 
 // ============================================================================
 // Fast path: L = 64 * E * RV with RV = 2^LOGRV in {1, ..., 8} (a row is RV
-// wave-wide 16-byte loads), 16-byte aligned rows.  A tile is 32 / RV rows;
-// each thread holds 8 vectors: wave w owns rows w*RW .. w*RW + RW-1
-// (RW = 8 / RV), vector u = row-in-wave u / RV, row-vector q = u % RV, lanes
+// wave-wide 16-byte loads), 16-byte aligned rows.  A tile is 64 / RV rows;
+// each thread holds 16 vectors: wave w owns rows w*RW .. w*RW + RW-1
+// (RW = 16 / RV), vector u = row-in-wave u / RV, row-vector q = u % RV, lanes
 // (q * 64 + lane) * E + e.  The lane tree of a row has three kinds of levels:
 // inside a vector (static), across the 64 lanes (xor butterfly), across the
 // RV vectors of the row (in the thread).
@@ -214,9 +214,9 @@ struct IpFast {
     static constexpr int E = Elem<T>::E;
     static constexpr int LOGE = Elem<T>::LOGE;
     static constexpr int RV = 1 << LOGRV;
-    static constexpr int NV = 8;
+    static constexpr int NV = 16;
     static constexpr int RW = NV / RV;
-    static constexpr int LOGRW = 3 - LOGRV;
+    static constexpr int LOGRW = 4 - LOGRV;
     static constexpr int R = 4 * RW;  // rows per tile
     static constexpr int L = 64 * E * RV;
 };
@@ -230,7 +230,7 @@ __device__ __forceinline__ T xor_lane(T v)
 
 template <typename T, int LOGRV, bool GUARD>
 __device__ __forceinline__ void ipf_load(const T* __restrict__ xs, uint64_t cols, uint64_t row0,
-                                         int w, int lane, T (&a)[8][Elem<T>::E])
+                                         int w, int lane, T (&a)[16][Elem<T>::E])
 {
     using F = IpFast<T, LOGRV>;
 #pragma unroll
@@ -249,7 +249,7 @@ __device__ __forceinline__ void ipf_load(const T* __restrict__ xs, uint64_t cols
 // In-wave pairwise prefix down each lane over the wave's RW rows (Sklansky
 // over rows; the upper half receives the end of the lower half).
 template <typename T, int LOGRV>
-__device__ __forceinline__ void ipf_columns_in_wave(T (&a)[8][Elem<T>::E])
+__device__ __forceinline__ void ipf_columns_in_wave(T (&a)[16][Elem<T>::E])
 {
     using F = IpFast<T, LOGRV>;
 #pragma unroll
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_totals_fast(const T* __restri
     for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const uint64_t seg = item / lay.tps, t = item % lay.tps;
         const T* xs = x + seg * ldx;
-        T a[8][F::E];
+        T a[F::NV][F::E];
         const uint64_t row0 = t * F::R;
         if ((row0 + F::R) * F::L <= cols) ipf_load<T, LOGRV, false>(xs, cols, row0, w, lane, a);
         else ipf_load<T, LOGRV, true>(xs, cols, row0, w, lane, a);
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict
         T* ys = y + seg * ldy;
         const uint64_t row0 = t * F::R;
         const bool full = (row0 + F::R) * F::L <= cols;
-        T a[8][E];
+        T a[F::NV][E];
         if (full) ipf_load<T, LOGRV, false>(xs, cols, row0, w, lane, a);
         else ipf_load<T, LOGRV, true>(xs, cols, row0, w, lane, a);
 

@@ -10,7 +10,7 @@ constexpr int kIpThreads = 256;
 constexpr int kIpMaxRLog = 6;         // at most 64 rows per tile
 constexpr int kIpLevelsPerPass = 4;   // node levels built per launch
 constexpr int kIpMaxLevels = 48;
-constexpr uint64_t kIpMaxGrid = 8192;
+constexpr uint64_t kIpMaxGrid = 0x7FFFFFFFull;  // one workgroup per item
 constexpr uint32_t kIpMaxL = 2048;    // largest lane count of the scan
 
 // Geometry of an iterated_pairwise scan over nseg independent segments of
@@ -49,7 +49,7 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
     int rl;
     if (aligned && Lp == L && lp >= loge + 6 && lp <= loge + 9) {
         lay.fast_logrv = lp - loge - 6;
-        rl = 5 - lay.fast_logrv;  // 32 / RV rows per tile
+        rl = 6 - lay.fast_logrv;  // 64 / RV rows per tile
     } else {
         rl = kIpMaxRLog;
         while (rl > 0 && ((1ull << rl) + 1) * 2 * Lp > ip_lds_elems(elem_size)) --rl;

@@ -247,7 +247,7 @@ def test_scan_rows_shape_of_workload(canon):
 
 # ------------------------------------------------- iterated_pairwise scan
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
-@pytest.mark.parametrize("L", [1, 2, 3, 5, 7, 16, 100, 128, 1024, 2048])
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 7, 16, 100, 128, 256, 1024, 2048])
 def test_scan_iterated_pairwise(canon, dtype, L):
     x = synth.generate(200_003, "mixed_magnitude", 300 + L, dtype)
     want_all = oracle.scan(x[:60_000] if L > 128 else x, "iterated_pairwise", L)
@@ -262,7 +262,7 @@ def test_scan_iterated_pairwise(canon, dtype, L):
 
 def test_scan_iterated_pairwise_many_tiles(canon):
     x = synth.generate((1 << 21) + 777, "mixed_magnitude", 401)
-    for L in (16, 128):
+    for L in (16, 128, 256):
         y = gpu_scan(canon, x, "iterated_pairwise", L)
         assert_bit_exact(y, oracle.scan(x, "iterated_pairwise", L), f"L={L}")
 
