@@ -19,7 +19,6 @@
 //   2. a finishing kernel (one workgroup): PW over the partials of each lane
 //      in range order, PW over lanes, then init + R.
 #include "device.hpp"
-#include "launch.hpp"
 #include "reduce.hpp"
 
 namespace canon {
@@ -331,7 +330,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_finish(const T* __res
 }
 
 // ============================================================================
-// Row-batched reduce: one workgroup per row (grid-stride over rows).  Lanes
+// Row-batched reduce: one workgroup per row.  Lanes
 // are processed in chunks of LW = min(Lp, 256); S = 256 / LW threads share a
 // lane, each over an aligned segment of the row's rows-of-L.  Lane values of
 // a chunk are merged in LDS to the chunk's complete subtree, and chunk values
@@ -456,8 +455,8 @@ hipError_t launch_reduce_rows(const T* x, uint64_t rows, uint64_t cols, uint64_t
     while ((1ull << lp_log) < L) ++lp_log;
     int lw_log = lp_log < 8 ? lp_log : 8;
     constexpr auto kern = k_reduce_rows<T>;
-    uint64_t grid = resident_grid<kern>(kRowsThreads);
-    if (grid > rows) grid = rows;
+    // one workgroup per row (the kernel strides over rows past the grid limit)
+    const uint64_t grid = rows < 0x7FFFFFFFull ? rows : 0x7FFFFFFFull;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRowsThreads), 0, s, x, rows, cols, ldx, L,
                        lw_log, init, out);
     return hipGetLastError();

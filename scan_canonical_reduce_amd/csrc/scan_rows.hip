@@ -2,7 +2,6 @@
 // pairwise and block_dyadic<B> (canonical-reduce README, P4229R0 "Summary" /
 // "Key Design Points").  The in-tile network is ScanTile (scan_tile.hpp).
 #include "device.hpp"
-#include "launch.hpp"
 #include "scan.hpp"
 #include "scan_tile.hpp"
 
@@ -58,10 +57,9 @@ template <typename T, int MODE, bool ALIGNED>
 static hipError_t launch_scan_rows_k(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
                                      uint64_t cols, int b_log, hipStream_t s)
 {
-    // grid-stride over rows with about as many workgroups as fit at once
     constexpr auto kern = k_scan_rows<T, MODE, ALIGNED, scan_rows_log_v<T>()>;
-    uint64_t grid = resident_grid<kern>(kScanThreads);
-    if (grid > rows) grid = rows;
+    // one workgroup per row (the kernel strides over rows past the grid limit)
+    const uint64_t grid = rows < 0x7FFFFFFFull ? rows : 0x7FFFFFFFull;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), 0, s, x, ldx, y, ldy, rows,
                        cols, b_log);
     return hipGetLastError();
