@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the oracle parity gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of ops to run (profiling)")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload config (parity-checked) and print a table")
     return ap.parse_args()
 
 
@@ -114,6 +116,9 @@ def main():
     canon.lib()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.configs:
+        run_configs(torch, canon, synth, dev)
+        return
 
     only = set(args.only.split(",")) if args.only else None
     want_rows = only is None or bool(only & {"rows_reduce", "rows_scan_bd16"})
@@ -276,6 +281,108 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_configs(torch, canon, synth, dev, reps=20):
+    """Every workload config: each op checked against the oracle (full result
+    for reduces and for the 2^20 scans, 32 sampled prefixes evaluated from
+    scratch for the large scans, 64 sampled rows for the row ops), then the
+    mean of `reps` calls timed with HIP events on the current stream.  Prints
+    one markdown table."""
+    import oracle
+    rng = np.random.default_rng(7)
+    stream = torch.cuda.current_stream()
+    rows = []
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3  # us
+
+    def same(got, want):
+        got = np.asarray(got)
+        want = np.asarray(want, dtype=got.dtype)
+        u = np.uint64 if got.dtype == np.float64 else np.uint32
+        return bool(np.array_equal(got.view(u), want.view(u)))
+
+    def add(cfg, op, dt, n, nbytes, us, ok):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append((cfg, op, dt, n, us, gbs, 100.0 * gbs / HBM_PEAK_GBS, n / (us * 1e-6), ok))
+        log(f"[configs] {cfg} {op}: {us:.1f} us {gbs:.0f} GB/s parity {'PASS' if ok else 'FAIL'}")
+
+    def reduce_cfg(cfg, name, Ls, init):
+        xn = synth.config_input(name)
+        x = torch.from_numpy(xn).to(dev)
+        out = torch.empty((), dtype=x.dtype, device=dev)
+        for L in Ls:
+            ws = torch.empty(max(canon.reduce_workspace_bytes(xn.size, L, xn.itemsize), 1),
+                             dtype=torch.uint8, device=dev)
+            canon.reduce(x, L, init, out=out, ws=ws)
+            ok = same(out.cpu().numpy().reshape(1), [oracle.reduce(xn, L, init)])
+            us = timed(lambda: canon.reduce(x, L, init, out=out, ws=ws))
+            add(cfg, f"reduce L={L} init={init}", str(xn.dtype), xn.size, xn.nbytes, us, ok)
+
+    def scan_cfg(cfg, name, pols, full):
+        xn = synth.config_input(name)
+        x = torch.from_numpy(xn).to(dev)
+        y = torch.empty_like(x)
+        for pol, q in pols:
+            ws = torch.empty(max(canon.scan_workspace_bytes(xn.size, pol, q, xn.itemsize), 1),
+                             dtype=torch.uint8, device=dev)
+            canon.scan(x, pol, q, out=y, ws=ws)
+            ok = canon.workspace_error(ws) == 0
+            if full:
+                yn = y.cpu().numpy()
+                ok = ok and same(yn, oracle.scan(xn, pol, q))
+                # scan back == reduce under the same expression
+                L = q if pol == "iterated_pairwise" else 1
+                if pol != "block_dyadic" or xn.size % q == 0:
+                    ok = ok and same(yn[-1:], [oracle.reduce(xn, L, -0.0)])
+            else:
+                idx = np.unique(np.concatenate([[0, xn.size - 1], rng.integers(0, xn.size, 30)]))
+                got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
+                want = [oracle.scan_prefix(xn, int(i), pol, q) for i in idx]
+                ok = ok and same(got, want)
+            us = timed(lambda: canon.scan(x, pol, q, out=y, ws=ws))
+            label = pol if pol == "pairwise" else f"{pol}<{q}>"
+            add(cfg, f"scan {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok)
+
+    reduce_cfg("C1", "reduce_1m", (16, 128), 0.0)
+    scan_cfg("C2", "scan_1m", (("block_dyadic", 256), ("pairwise", 0)), True)
+    reduce_cfg("C3", "reduce_2e28_f64", (128,), 1.0)
+    reduce_cfg("C3", "reduce_2e29_f32", (128,), 1.0)
+    Xn = synth.config_input("rows_16384x4096")
+    X = torch.from_numpy(Xn).to(dev)
+    rr = torch.empty(Xn.shape[0], dtype=X.dtype, device=dev)
+    Y = torch.empty_like(X)
+    canon.reduce_rows(X, 16, 0.0, out=rr)
+    ok = same(rr.cpu().numpy(), oracle.reduce_rows(Xn, 16, 0.0))
+    add("C4", "row reduce L=16", "float64", Xn.size, Xn.nbytes,
+        timed(lambda: canon.reduce_rows(X, 16, 0.0, out=rr)), ok)
+    canon.scan_rows(X, "block_dyadic", 16, out=Y)
+    sel = rng.integers(0, Xn.shape[0], 64)
+    ok = same(Y[torch.from_numpy(sel).to(dev)].cpu().numpy(),
+              oracle.scan_rows(Xn[sel], "block_dyadic", 16))
+    add("C4", "row scan block_dyadic<16>", "float64", Xn.size, 2 * Xn.nbytes,
+        timed(lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y)), ok)
+    del X, Y, rr
+    scan_cfg("C5", "scan_2e27_f64", (("iterated_pairwise", 128), ("block_dyadic", 16),
+                                     ("block_dyadic", 256)), False)
+    scan_cfg("C5", "scan_2e28_f32", (("block_dyadic", 256),), False)
+
+    print("| config | op | dtype | N | us | GB/s | % of 8 TB/s | elements/s | bit-exact |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for cfg, op, dt, n, us, gbs, pct, eps, ok in rows:
+        print(f"| {cfg} | {op} | {dt} | {n} | {us:.1f} | {gbs:.0f} | {pct:.1f} | {eps:.3g} | "
+              f"{'yes' if ok else 'NO'} |")
 
 
 def cpu_baseline(x_np, X_np, have_ip):
