@@ -265,6 +265,111 @@ __device__ __forceinline__ void ipf_columns_in_wave(T (&a)[16][Elem<T>::E])
                                               a[r * F::RV + q][e];
 }
 
+// The sibling values one row contributes to the walks of the lanes of a
+// row (its own, as the A side, or the next one, as the B side), per 16-byte
+// vector q of the row held by this thread:
+//   sv[l][q][s]: the complete subtree of 2^l slots starting at slot s 2^l
+//                (inside the vector, l < log2 E);
+//   o[K][q]:     the partner lane's subtree at lane level K (lane ^ 2^K);
+//   pv[l][q]:    this thread's subtree of vector q at vector level l.
+template <typename T, int LOGRV>
+struct IpRowTree {
+    static constexpr int E = Elem<T>::E, LOGE = Elem<T>::LOGE, RV = 1 << LOGRV;
+    T sv[LOGE][RV][E];
+    T o[6][RV];
+    T pv[LOGRV > 0 ? LOGRV : 1][RV];
+
+    // row = vectors rows[v0 .. v0 + RV)
+    template <int NV>
+    __device__ __forceinline__ void build(const T (&rows)[NV][E], int v0, int lane)
+    {
+        T p[RV];
+#pragma unroll
+        for (int q = 0; q < RV; ++q) {
+            T cur[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) cur[e] = rows[v0 + q][e];
+#pragma unroll
+            for (int l = 0; l < LOGE; ++l) {
+#pragma unroll
+                for (int s2 = 0; s2 < (E >> l); ++s2) sv[l][q][s2] = cur[s2];
+#pragma unroll
+                for (int s2 = 0; s2 < (E >> (l + 1)); ++s2) cur[s2] = cur[2 * s2] + cur[2 * s2 + 1];
+            }
+            p[q] = cur[0];
+        }
+#define CANON_IP_TREE_LANE(K)                                                           \
+    {                                                                                   \
+        const bool right = (lane >> (K)) & 1;                                           \
+        _Pragma("unroll") for (int q = 0; q < RV; ++q)                                  \
+        {                                                                               \
+            o[K][q] = xor_lane<K>(p[q]);                                                \
+            p[q] = right ? (o[K][q] + p[q]) : (p[q] + o[K][q]);                         \
+        }                                                                               \
+    }
+        CANON_IP_TREE_LANE(0)
+        CANON_IP_TREE_LANE(1)
+        CANON_IP_TREE_LANE(2)
+        CANON_IP_TREE_LANE(3)
+        CANON_IP_TREE_LANE(4)
+        CANON_IP_TREE_LANE(5)
+#undef CANON_IP_TREE_LANE
+#pragma unroll
+        for (int l = 0; l < LOGRV; ++l) {
+            const int h = 1 << l;
+#pragma unroll
+            for (int q = 0; q < RV; ++q) pv[l][q] = p[q];
+#pragma unroll
+            for (int i = 0; i < RV / (2 * h); ++i) p[2 * i * h] = p[2 * i * h] + p[(2 * i + 1) * h];
+        }
+    }
+};
+
+// val[q][e]: the walk of every lane of row vectors rows[v0 .. v0 + RV) from
+// its leaf to the root: at each level the sibling subtree lies wholly left
+// (A row, added on the left) or wholly right (B row, added on the right).
+template <typename T, int LOGRV, int NV>
+__device__ __forceinline__ void ip_walk(const T (&rows)[NV][Elem<T>::E], int v0,
+                                        const IpRowTree<T, LOGRV>& A,
+                                        const IpRowTree<T, LOGRV>& B, int lane,
+                                        T (&val)[1 << LOGRV][Elem<T>::E])
+{
+    constexpr int E = Elem<T>::E, LOGE = Elem<T>::LOGE, RV = 1 << LOGRV;
+#pragma unroll
+    for (int q = 0; q < RV; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e) val[q][e] = rows[v0 + q][e];
+#pragma unroll
+    for (int l = 0; l < LOGE; ++l)
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int node = e >> l, sib = node ^ 1;
+                val[q][e] = (node & 1) ? A.sv[l][q][sib] + val[q][e] : val[q][e] + B.sv[l][q][sib];
+            }
+#pragma unroll
+    for (int K = 0; K < 6; ++K) {
+        const bool right = (lane >> K) & 1;
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                val[q][e] = right ? (A.o[K][q] + val[q][e]) : (val[q][e] + B.o[K][q]);
+    }
+#pragma unroll
+    for (int l = 0; l < LOGRV; ++l) {
+        const int h = 1 << l;
+#pragma unroll
+        for (int q = 0; q < RV; ++q) {
+            const int node = q >> l, sib = node ^ 1;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                val[q][e] = (node & 1) ? A.pv[l][sib * h] + val[q][e] : val[q][e] + B.pv[l][sib * h];
+        }
+    }
+}
+
 // Kernel 1 (fast): tile totals, lane by lane, into node level 0.
 template <typename T, int LOGRV>
 __global__ __launch_bounds__(kIpThreads) void k_ip_totals_fast(const T* __restrict__ x,
@@ -392,78 +497,18 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict
         }
 
         // walk every lane up its row's tree.  For row r: A = a[row r],
-        // B = a[row r-1] (b for the wave's first row).  pa[l] / pb[l]: value of
-        // this lane-group's subtree at lane level l for the A / B row.
+        // B = a[row r-1] (b for the wave's first row).  The sibling subtree
+        // values a walk needs depend only on the row, so each row's are
+        // built once (IpRowTree) and serve as its A side and as the next
+        // row's B side.
+        IpRowTree<T, LOGRV> tb;
+        tb.template build<RV>(b, 0, lane);
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
+            IpRowTree<T, LOGRV> ta;
+            ta.template build<F::NV>(a, r * RV, lane);
             T val[RV][E];
-            T pa[RV], pb[RV];  // subtree values after the in-vector levels
-#pragma unroll
-            for (int q = 0; q < RV; ++q) {
-                const T* A = a[r * RV + q];
-                const T* Bv = (r == 0) ? b[q] : a[(r - 1) * RV + q];
-                // in-vector levels: slot e's sibling at each level
-                T av[E], bv[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    av[e] = A[e];
-                    bv[e] = Bv[e];
-                    val[q][e] = A[e];
-                }
-#pragma unroll
-                for (int h = 1; h < E; h *= 2) {
-                    // subtrees of size h at slots s*h; pair (2i, 2i+1)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int node = e / h, sib = node ^ 1;
-                        val[q][e] = (node & 1) ? av[sib * h] + val[q][e] : val[q][e] + bv[sib * h];
-                    }
-#pragma unroll
-                    for (int i = 0; i < E / (2 * h); ++i) {
-                        av[2 * i * h] = av[2 * i * h] + av[(2 * i + 1) * h];
-                        bv[2 * i * h] = bv[2 * i * h] + bv[(2 * i + 1) * h];
-                    }
-                }
-                pa[q] = av[0];
-                pb[q] = bv[0];
-            }
-            // lane levels
-#define CANON_IP_LANE_LEVEL(K)                                                          \
-    {                                                                                   \
-        const bool right = (lane >> (K)) & 1;                                           \
-        _Pragma("unroll") for (int q = 0; q < RV; ++q)                                  \
-        {                                                                               \
-            const T oa = xor_lane<K>(pa[q]);                                            \
-            const T ob = xor_lane<K>(pb[q]);                                            \
-            _Pragma("unroll") for (int e = 0; e < E; ++e) val[q][e] =                   \
-                right ? (oa + val[q][e]) : (val[q][e] + ob);                            \
-            pa[q] = right ? (oa + pa[q]) : (pa[q] + oa);                                \
-            pb[q] = right ? (ob + pb[q]) : (pb[q] + ob);                                \
-        }                                                                               \
-    }
-            CANON_IP_LANE_LEVEL(0)
-            CANON_IP_LANE_LEVEL(1)
-            CANON_IP_LANE_LEVEL(2)
-            CANON_IP_LANE_LEVEL(3)
-            CANON_IP_LANE_LEVEL(4)
-            CANON_IP_LANE_LEVEL(5)
-#undef CANON_IP_LANE_LEVEL
-            // vector levels (inside the thread)
-#pragma unroll
-            for (int h = 1; h < RV; h *= 2) {
-#pragma unroll
-                for (int q = 0; q < RV; ++q) {
-                    const int node = q / h, sib = node ^ 1;
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        val[q][e] = (node & 1) ? pa[sib * h] + val[q][e] : val[q][e] + pb[sib * h];
-                }
-#pragma unroll
-                for (int i = 0; i < RV / (2 * h); ++i) {
-                    pa[2 * i * h] = pa[2 * i * h] + pa[(2 * i + 1) * h];
-                    pb[2 * i * h] = pb[2 * i * h] + pb[(2 * i + 1) * h];
-                }
-            }
+            ip_walk<T, LOGRV>(a, r * RV, ta, tb, lane, val);
             // store row r
             const uint64_t row = row0 + (uint64_t)w * RW + r;
 #pragma unroll
@@ -477,6 +522,7 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict
                         if (gi + e < cols) ys[gi + e] = val[q][e];
                 }
             }
+            tb = ta;
         }
         __syncthreads();  // s_row is rewritten by the next tile
     }
