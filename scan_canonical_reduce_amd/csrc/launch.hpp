@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace canon {
 
 // Workgroups of kernel KERN (with `threads` threads and `shmem` bytes of
@@ -21,8 +23,10 @@ uint64_t resident_grid(int threads, size_t shmem = 0)
     };
     static Entry cache[32] = {};
     static int used = 0;
+    static std::mutex mu;  // host threads may launch concurrently
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < used; ++i)
         if (cache[i].dev == dev && cache[i].shmem == shmem) return cache[i].grid;
     int cus = 0, per = 0;
