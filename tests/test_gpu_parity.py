@@ -300,3 +300,54 @@ def test_scan_rows_iterated_pairwise_aligned_pitch(canon, dtype, L):
         got = to_host(canon.scan_rows(Xd[:, :cols], "iterated_pairwise", L))
         want = oracle.scan_rows(X, "iterated_pairwise", L, cols=cols)[:, :cols]
         assert_bit_exact(got, want, f"cols={cols}")
+
+
+# ------------------------------------------------------- use of the ABI
+def test_workspace_reused_across_policies_and_sizes(canon):
+    """One workspace, sized for the largest call, serves calls of every policy
+    and size in turn on one stream (each call re-initialises what it uses)."""
+    x = synth.generate(3 * 16384 * 4 + 77, "mixed_magnitude", 501)
+    cases = [("pairwise", 0), ("block_dyadic", 16), ("iterated_pairwise", 128),
+             ("block_dyadic", 4096), ("pairwise", 0)]
+    nb = max(canon.scan_workspace_bytes(x.size, p, q, 8) for p, q in cases)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    xd = to_dev(x)
+    for n in (x.size, 1000, x.size // 2 + 3):
+        for p, q in cases:
+            y = to_host(canon.scan(xd[:n], p, q, ws=ws))
+            assert_bit_exact(y, oracle.scan(x[:n], p, q), f"{p}<{q}> n={n}")
+            assert canon.workspace_error(ws) == 0
+
+
+def test_concurrent_streams(canon):
+    """Scans on two streams at once, each with its own workspace, from two
+    host threads: the results are those of the oracle."""
+    import threading
+    xs = [synth.generate((1 << 21) + 5, "mixed_magnitude", 502 + i) for i in range(2)]
+    pols = [("block_dyadic", 256), ("pairwise", 0)]
+    wants = [oracle.scan(xs[i], *pols[i]) for i in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    xd = [to_dev(x) for x in xs]
+    ys = [torch.empty_like(d) for d in xd]
+    wss = [torch.empty(canon.scan_workspace_bytes(xs[i].size, *pols[i], 8), dtype=torch.uint8,
+                       device="cuda") for i in range(2)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(5):
+                    canon.scan(xd[i], *pols[i], out=ys[i], ws=wss[i])
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert_bit_exact(to_host(ys[i]), wants[i], f"stream {i}")
