@@ -1,4 +1,5 @@
-"""CPU oracle for canonical reduction and canonical inclusive scan.
+"""CPU oracle for canonical reduction and canonical scans (inclusive, and with
+an initial value: inclusive, exclusive, include_initial).
 
 TEST INFRASTRUCTURE.  This package is the slow, literal statement of what the
 GPU library computes, and is used only to check it: by the tests, by the
@@ -31,6 +32,9 @@ _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = [os.path.join(_HERE, "canon_oracle.c"), os.path.join(_HERE, "canon_oracle_body.h")]
 
 POLICIES = {"pairwise": 0, "iterated_pairwise": 1, "block_dyadic": 2}
+
+# Which prefix each output of a scan with an initial value observes.
+SCAN_KINDS = {"inclusive": 0, "exclusive": 1, "include_initial": 2}
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
 
@@ -66,6 +70,9 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, f"oracle_scan_{sfx}"); f.argtypes = [P, P, S, I, U]; f.restype = I
             f = getattr(L, f"oracle_reduce_rows_{sfx}"); f.argtypes = [P, S, S, S, U, ct, P]; f.restype = None
             f = getattr(L, f"oracle_scan_rows_{sfx}"); f.argtypes = [P, S, P, S, S, S, I, U]; f.restype = I
+            f = getattr(L, f"oracle_scan_with_init_{sfx}"); f.argtypes = [P, P, S, I, U, I, ct]; f.restype = I
+            f = getattr(L, f"oracle_scan_rows_with_init_{sfx}")
+            f.argtypes = [P, S, P, S, S, S, I, U, I, ct]; f.restype = I
         _lib = L
     return _lib
 
@@ -177,6 +184,48 @@ def scan_rows(X: np.ndarray, policy, param: int = 0, cols: int | None = None) ->
     Y = np.zeros_like(X)
     ok = getattr(lib(), f"oracle_scan_rows_{_sfx(X)}")(
         _ptr(X), ld, _ptr(Y), ld, rows, cols, p, param)
+    if not ok:
+        raise ValueError("bad scan arguments")
+    return Y
+
+
+def _kind(kind) -> int:
+    return SCAN_KINDS[kind] if isinstance(kind, str) else int(kind)
+
+
+def scan_with_init(x: np.ndarray, policy, param: int = 0, init=-0.0,
+                   kind="inclusive") -> np.ndarray:
+    """Scan with an initial value: output k is init + E(x[0..m)), init alone
+    when m == 0, where m = k + 1 (inclusive) or k (exclusive,
+    include_initial); include_initial has len(x) + 1 outputs.  The default
+    init, -0.0, is the exact identity of IEEE addition."""
+    x = _c(x)
+    p = _policy(policy)
+    _check_param(p, param)
+    k = _kind(kind)
+    y = np.empty(x.size + (1 if k == 2 else 0), x.dtype)
+    ok = getattr(lib(), f"oracle_scan_with_init_{_sfx(x)}")(
+        _ptr(x), _ptr(y), x.size, p, param, k, x.dtype.type(init))
+    if not ok:
+        raise ValueError("bad scan arguments")
+    return y
+
+
+def scan_rows_with_init(X: np.ndarray, policy, param: int = 0, init=-0.0, kind="inclusive",
+                        cols: int | None = None) -> np.ndarray:
+    """Per-row scan_with_init of a 2-D array (``cols`` as in scan_rows).  The
+    result has X.shape[1] columns, or X.shape[1] + 1 for include_initial;
+    entries past a row's outputs are left 0."""
+    X = np.ascontiguousarray(X)
+    rows, ld = X.shape
+    cols = ld if cols is None else cols
+    p = _policy(policy)
+    _check_param(p, param)
+    k = _kind(kind)
+    ldy = ld + (1 if k == 2 else 0)
+    Y = np.zeros((rows, ldy), X.dtype)
+    ok = getattr(lib(), f"oracle_scan_rows_with_init_{_sfx(X)}")(
+        _ptr(X), ld, _ptr(Y), ldy, rows, cols, p, param, k, X.dtype.type(init))
     if not ok:
         raise ValueError("bad scan arguments")
     return Y

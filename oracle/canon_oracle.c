@@ -16,7 +16,10 @@
  *     lane j = (x_j, x_{j+L}, ...), m = min(n, L);  init alone when n = 0;
  *   - inclusive scans that return the value of a named expression on every
  *     prefix: pairwise, iterated_pairwise<L>, block_dyadic<B>;
- *   - row-batched versions of both.
+ *   - scans with an initial value (inclusive, exclusive, include_initial):
+ *     every output is init + the policy's expression over the prefix it
+ *     observes, init alone for the empty prefix;
+ *   - row-batched versions of all of these.
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (x86-64 SSE2
  * arithmetic: every float operation is one IEEE-754 operation in its own
  * type, round to nearest even, no flush of subnormals).

@@ -226,6 +226,36 @@ int FN(oracle_scan)(const T* x, T* y, size_t n, int policy, uint32_t param)
     return 0;
 }
 
+/* ---- scan with an initial value ------------------------------------------ */
+/* Every output observes one prefix x[0..m) of the input and takes the value  */
+/* init + E(x[0..m)): init is combined once, on the left, after the policy's  */
+/* whole expression, exactly as the reduction places it (P4016R0 "Key Design  */
+/* Points", init placement); the empty prefix (m = 0) observes init alone.    */
+/* Which prefix output k observes follows the inclusive/exclusive duality of  */
+/* the gt4py scan-redesign research page, B.2 "Array API standard / NumPy":   */
+/*   kind 0  inclusive          m = k + 1,  k < n   (n outputs)              */
+/*   kind 1  exclusive          m = k,      k < n   (n outputs)              */
+/*   kind 2  include_initial    m = k,      k <= n  (n + 1 outputs)          */
+/* y may equal x.  Returns 0 on a bad argument, 1 otherwise.                 */
+int FN(oracle_scan_with_init)(const T* x, T* y, size_t n, int policy, uint32_t param, int kind,
+                              T init)
+{
+    if (kind < 0 || kind > 2) return 0;
+    T* s = (T*)malloc((n ? n : 1) * sizeof(T));
+    if (!s) abort();
+    if (!FN(oracle_scan)(x, s, n, policy, param)) {
+        free(s);
+        return 0;
+    }
+    const size_t nout = kind == 2 ? n + 1 : n;
+    for (size_t k = 0; k < nout; ++k) {
+        const size_t m = kind == 0 ? k + 1 : k;
+        y[k] = m == 0 ? init : init + s[m - 1];
+    }
+    free(s);
+    return 1;
+}
+
 /* ---- batched rows: every row is an independent sequence ----------------- */
 void FN(oracle_reduce_rows)(const T* x, size_t rows, size_t cols, size_t ldx, uint32_t L,
                             T init, T* out)
@@ -238,6 +268,17 @@ int FN(oracle_scan_rows)(const T* x, size_t ldx, T* y, size_t ldy, size_t rows, 
 {
     for (size_t r = 0; r < rows; ++r)
         if (!FN(oracle_scan)(x + r * ldx, y + r * ldy, cols, policy, param)) return 0;
+    return 1;
+}
+
+/* Row r of y (pitch ldy) is oracle_scan_with_init of row r of x; an        */
+/* include_initial row has cols + 1 outputs (ldy >= cols + 1).               */
+int FN(oracle_scan_rows_with_init)(const T* x, size_t ldx, T* y, size_t ldy, size_t rows,
+                                   size_t cols, int policy, uint32_t param, int kind, T init)
+{
+    for (size_t r = 0; r < rows; ++r)
+        if (!FN(oracle_scan_with_init)(x + r * ldx, y + r * ldy, cols, policy, param, kind, init))
+            return 0;
     return 1;
 }
 

@@ -78,6 +78,17 @@ def scan_tree(i: int, policy: str, param: int = 0):
     raise ValueError(policy)
 
 
+def scan_with_init_tree(k: int, policy: str, param: int = 0, kind: str = "inclusive"):
+    """Output k of a scan with an initial value: init + (the policy's tree over
+    the prefix it observes), or init alone for the empty prefix.  Inclusive
+    output k observes x[0..k]; exclusive and include_initial output k observe
+    x[0..k-1]."""
+    m = k + 1 if kind == "inclusive" else k
+    if kind not in ("inclusive", "exclusive", "include_initial"):
+        raise ValueError(kind)
+    return "I" if m == 0 else ("I", scan_tree(m - 1, policy, param))
+
+
 def halving_tree(n: int):
     """Futhark blog's sum_tree on a power-of-two n: pair element k with k + n/2,
     repeatedly.  A different exact tree, used as a contrast."""
