@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CANON_ABI_VERSION 1
+#define CANON_ABI_VERSION 2 /* 2: scans with an initial value */
 
 /* Largest lane count L for reduce and iterated_pairwise, and largest block
  * size B for block_dyadic.  Larger values return CANON_EUNSUPPORTED. */
@@ -84,6 +84,13 @@ typedef enum {
     CANON_ITERATED_PAIRWISE = 1, /* param = L, 1 <= L <= CANON_MAX_IP_L */
     CANON_BLOCK_DYADIC = 2       /* param = B, power of two, 1 <= B <= CANON_MAX_B */
 } canon_policy_t;
+
+/* Which prefix each output of a scan with an initial value observes. */
+typedef enum {
+    CANON_SCAN_INCLUSIVE = 0,      /* output i observes x[0..i]             */
+    CANON_SCAN_EXCLUSIVE = 1,      /* output i observes x[0..i-1]           */
+    CANON_SCAN_INCLUDE_INITIAL = 2 /* as exclusive, with n + 1 outputs      */
+} canon_scan_kind_t;
 
 /* ABI version of the loaded library (CANON_ABI_VERSION). */
 int canon_abi_version(void);
@@ -142,6 +149,45 @@ canon_status_t canon_scan_rows_f64(const double* x, size_t ldx, double* y, size_
 canon_status_t canon_scan_rows_f32(const float* x, size_t ldx, float* y, size_t ldy,
                                    size_t rows, size_t cols, int policy, uint32_t param,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------- scan with an initial value */
+/* Every output is init + E(prefix it observes), and init itself for the
+ * empty prefix: init is combined once, on the left, after the policy's whole
+ * expression, as the reduction places it (P4016R0 "Key Design Points", init
+ * placement), so an inclusive output equals the reduction with init of the
+ * same prefix.  With S_i = scan<E>(x)[i] (and S_{-1} the empty prefix):
+ *   CANON_SCAN_INCLUSIVE        y[i] = init + S_i,      i < n   (n outputs)
+ *   CANON_SCAN_EXCLUSIVE        y[i] = init + S_{i-1},  i < n   (n outputs)
+ *   CANON_SCAN_INCLUDE_INITIAL  y[i] = init + S_{i-1},  i <= n  (n + 1)
+ * so y[0] = init for the last two.  The inclusive/exclusive duality and
+ * include_initial are those of the array API's cumulative_sum (gt4py
+ * scan-redesign research page, B.2 "Array API standard / NumPy").
+ *   x     device, n elements (may be NULL when n == 0)
+ *   y     device, n outputs (n + 1 for include_initial); y == x (in place)
+ *         is allowed, any other overlap is undefined
+ *   kind  a canon_scan_kind_t; anything else returns CANON_EINVAL
+ * The workspace is the plain scan's (canon_scan_workspace_bytes).  With init
+ * = -0.0 and CANON_SCAN_INCLUSIVE the result is bit-identical to
+ * canon_scan_*: -0.0 is the exact identity of IEEE addition. */
+canon_status_t canon_scan_with_init_f64(const double* x, double* y, size_t n, int policy,
+                                       uint32_t param, int kind, double init, void* ws,
+                                       size_t ws_bytes, void* stream);
+canon_status_t canon_scan_with_init_f32(const float* x, float* y, size_t n, int policy,
+                                       uint32_t param, int kind, float init, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+/* Row-batched scan with an initial value: row r of y (pitch ldy) is
+ * canon_scan_with_init of row r of x.  ldx >= cols; ldy >= cols, or cols + 1
+ * for include_initial.  y == x with ldy == ldx is allowed.  Workspace:
+ * canon_scan_rows_workspace_bytes. */
+canon_status_t canon_scan_rows_with_init_f64(const double* x, size_t ldx, double* y, size_t ldy,
+                                            size_t rows, size_t cols, int policy, uint32_t param,
+                                            int kind, double init, void* ws, size_t ws_bytes,
+                                            void* stream);
+canon_status_t canon_scan_rows_with_init_f32(const float* x, size_t ldx, float* y, size_t ldy,
+                                            size_t rows, size_t cols, int policy, uint32_t param,
+                                            int kind, float init, void* ws, size_t ws_bytes,
+                                            void* stream);
 
 /* -------------------------------------------------------------- checking */
 /* Every scan workspace begins with a 32-bit error word.  The single-pass

@@ -13,6 +13,11 @@ same names without the ``canon_`` prefix:
     scan(x, policy, param=0)           -> tensor of prefix values
     reduce_rows(X, L, init)            -> 1-d tensor, one value per row
     scan_rows(X, policy, param=0)      -> tensor shaped like X
+    scan_with_init(x, policy, param, kind, init)
+                                       -> init + each prefix value: "inclusive",
+                                          "exclusive" or "include_initial"
+                                          (len(x) + 1 outputs)
+    scan_rows_with_init(X, policy, param, kind, init)
 
 ``policy`` is "pairwise", "iterated_pairwise" (param = L) or "block_dyadic"
 (param = B, a power of two).
@@ -28,6 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcanon.so")
 
 POLICIES = {"pairwise": 0, "iterated_pairwise": 1, "block_dyadic": 2}
+SCAN_KINDS = {"inclusive": 0, "exclusive": 1, "include_initial": 2}
 STATUS = {0: "CANON_OK", 1: "CANON_EINVAL", 2: "CANON_EUNSUPPORTED", 3: "CANON_EWORKSPACE",
           4: "CANON_EHIP"}
 
@@ -37,6 +43,8 @@ EXPORTS = [
     "canon_reduce_rows_workspace_bytes", "canon_reduce_rows_f64", "canon_reduce_rows_f32",
     "canon_scan_workspace_bytes", "canon_scan_f64", "canon_scan_f32",
     "canon_scan_rows_workspace_bytes", "canon_scan_rows_f64", "canon_scan_rows_f32",
+    "canon_scan_with_init_f64", "canon_scan_with_init_f32",
+    "canon_scan_rows_with_init_f64", "canon_scan_rows_with_init_f32",
     "canon_workspace_error",
 ]
 
@@ -78,12 +86,16 @@ def lib() -> ctypes.CDLL:
     L.canon_scan_rows_workspace_bytes.restype = S
     L.canon_scan_rows_f64.argtypes = [P, S, P, S, S, S, I, U, P, S, P]
     L.canon_scan_rows_f32.argtypes = [P, S, P, S, S, S, I, U, P, S, P]
+    L.canon_scan_with_init_f64.argtypes = [P, P, S, I, U, I, D, P, S, P]
+    L.canon_scan_with_init_f32.argtypes = [P, P, S, I, U, I, F, P, S, P]
+    L.canon_scan_rows_with_init_f64.argtypes = [P, S, P, S, S, S, I, U, I, D, P, S, P]
+    L.canon_scan_rows_with_init_f32.argtypes = [P, S, P, S, S, S, I, U, I, F, P, S, P]
     L.canon_workspace_error.argtypes = [P, ctypes.POINTER(U), P]
     for name in EXPORTS:
         if name not in ("canon_abi_version", "canon_status_str", "canon_last_hip_error") and \
                 not name.endswith("workspace_bytes"):
             getattr(L, name).restype = I
-    if L.canon_abi_version() != 1:
+    if L.canon_abi_version() != 2:
         raise CanonError("libcanon ABI version mismatch")
     _lib = L
     return L
@@ -122,6 +134,12 @@ def _policy(p) -> int:
     if isinstance(p, str):
         return POLICIES[p]
     return int(p)
+
+
+def _kind(k) -> int:
+    if isinstance(k, str):
+        return SCAN_KINDS[k]
+    return int(k)
 
 
 def _ws(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor | None:
@@ -223,6 +241,59 @@ def scan_rows(X: torch.Tensor, policy="pairwise", param: int = 0,
         _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, _ptr(w),
         nb if w is None else w.numel(), _stream())
     _check(st, "scan_rows")
+    return out
+
+
+def scan_with_init(x: torch.Tensor, policy="pairwise", param: int = 0, kind="inclusive",
+                   init: float = -0.0, out: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Scan with an initial value: each output is init + the policy's value on
+    the prefix it observes (x[0..i] for "inclusive", x[0..i-1] for
+    "exclusive" and "include_initial", init alone for the empty prefix);
+    "include_initial" has len(x) + 1 outputs.  out may be x (in place; for
+    include_initial a buffer of len(x) + 1 whose head is x)."""
+    _need_gpu(x)
+    if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
+        raise ValueError("scan_with_init takes a contiguous 1-d tensor")
+    sfx = _sfx(x)
+    k = _kind(kind)
+    m = x.numel() + (1 if k == 2 else 0)
+    if out is None:
+        out = torch.empty(m, dtype=x.dtype, device=x.device)
+    if out.dim() != 1 or out.numel() < m or (m > 0 and out.stride(0) != 1) or out.dtype != x.dtype:
+        raise ValueError(f"scan_with_init: out must be a contiguous {x.dtype} tensor of {m}")
+    p = _policy(policy)
+    nb = lib().canon_scan_workspace_bytes(x.numel(), p, param, x.element_size())
+    w = _ws(nb, x.device, ws)
+    st = getattr(lib(), f"canon_scan_with_init_{sfx}")(
+        _ptr(x), out.data_ptr(), x.numel(), p, param, k, float(init), _ptr(w),
+        nb if w is None else w.numel(), _stream())
+    _check(st, "scan_with_init")
+    return out
+
+
+def scan_rows_with_init(X: torch.Tensor, policy="pairwise", param: int = 0, kind="inclusive",
+                        init: float = -0.0, out: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None) -> torch.Tensor:
+    """scan_with_init of every row of a 2-d tensor; the result has one more
+    column for include_initial."""
+    _need_gpu(X)
+    sfx = _sfx(X)
+    rows, cols, ldx = _rows_view(X)
+    k = _kind(kind)
+    ycols = cols + (1 if k == 2 else 0)
+    if out is None:
+        out = torch.empty((rows, ycols), dtype=X.dtype, device=X.device)
+    if out.dim() != 2 or out.shape[0] != rows or out.shape[1] < ycols or out.dtype != X.dtype:
+        raise ValueError(f"scan_rows_with_init: out must be {X.dtype} of shape ({rows}, >= {ycols})")
+    _, _, ldy = _rows_view(out)
+    p = _policy(policy)
+    nb = lib().canon_scan_rows_workspace_bytes(rows, cols, p, param, X.element_size())
+    w = _ws(nb, X.device, ws)
+    st = getattr(lib(), f"canon_scan_rows_with_init_{sfx}")(
+        _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, k, float(init), _ptr(w),
+        nb if w is None else w.numel(), _stream())
+    _check(st, "scan_rows_with_init")
     return out
 
 

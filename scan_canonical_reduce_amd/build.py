@@ -14,7 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libcanon.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libcanon")
 
-SOURCES = ["api.cpp", "reduce.hip", "scan.hip", "scan_rows.hip", "scan_ip.hip"]
+SOURCES = [
+    "api.cpp", "reduce.hip", "scan.hip", "scan_with_init.hip", "scan_rows.hip", "scan_ip.hip",
+]
 
 # -ffp-contract=off: no FMA contraction; no fast-math; packed FP32 disabled.
 HIPFLAGS = [

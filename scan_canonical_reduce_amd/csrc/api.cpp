@@ -153,19 +153,27 @@ size_t scan_rows_ws(uint64_t rows, uint64_t cols, int policy, uint32_t param, si
     return kWsAlign + round_up((a > b ? a : b) * es, kWsAlign);
 }
 
+// out == null: the plain inclusive scan; else the scan with an initial value.
 template <typename T>
-canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param, void* ws,
-                         size_t ws_bytes, void* stream)
+canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
+                         const ScanOut<T>* out, void* ws, size_t ws_bytes, void* stream)
 {
     if (canon_status_t s = check_policy(policy, param)) return s;
+    if (out && (out->kind < CANON_SCAN_INCLUSIVE || out->kind > CANON_SCAN_INCLUDE_INITIAL))
+        return CANON_EINVAL;
     if (n > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
-    if (n == 0) return CANON_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n == 0) {
+        if (!out || out->kind != CANON_SCAN_INCLUDE_INITIAL) return CANON_OK;
+        if (y == nullptr) return CANON_EINVAL;
+        return hip_status(launch_put_column<T>(y, 1, 1, out->init, st));
+    }
     if (is_ip(policy, param)) {
         const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), aligned16(x) && aligned16(y));
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
             return s;
         return hip_status(launch_scan_ip<T>(x, n, y, n, 1, n, static_cast<uint32_t*>(ws),
-                                            ip_nodes<T>(ws), ip, static_cast<hipStream_t>(stream)));
+                                            ip_nodes<T>(ws), ip, out, st));
     }
     const ScanLayout lay = scan_layout<T>(n, policy, param);
     if (lay.ntiles > 0xFFFFFFFFull) return CANON_EUNSUPPORTED;
@@ -174,20 +182,28 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
     const bool pairwise = policy != CANON_BLOCK_DYADIC;  // pairwise, or iterated_pairwise<1>
     const int b_log = pairwise ? 0 : log2_exact(param);
     const bool al = aligned16(x) && aligned16(y);
-    return hip_status(launch_scan<T>(x, y, n, pairwise, b_log, al, static_cast<uint64_t*>(ws), lay,
-                                     static_cast<hipStream_t>(stream)));
+    if (out)
+        return hip_status(launch_scan_with_init<T>(x, y, n, pairwise, b_log, al,
+                                                   static_cast<uint64_t*>(ws), lay, *out, st));
+    return hip_status(
+        launch_scan<T>(x, y, n, pairwise, b_log, al, static_cast<uint64_t*>(ws), lay, st));
 }
 
 template <typename T>
 canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t rows, size_t cols,
-                              int policy, uint32_t param, void* ws, size_t ws_bytes, void* stream)
+                              int policy, uint32_t param, const ScanOut<T>* out, void* ws,
+                              size_t ws_bytes, void* stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     if (canon_status_t s = check_policy(policy, param)) return s;
-    if (ldx < cols || ldy < cols) return CANON_EINVAL;
-    if (rows > 0 && cols > 0 && (x == nullptr || y == nullptr)) return CANON_EINVAL;
-    if (rows == 0 || cols == 0) return CANON_OK;
+    if (out && (out->kind < CANON_SCAN_INCLUSIVE || out->kind > CANON_SCAN_INCLUDE_INITIAL))
+        return CANON_EINVAL;
+    const size_t ycols = out && out->kind == CANON_SCAN_INCLUDE_INITIAL ? cols + 1 : cols;
+    if (ldx < cols || ldy < ycols) return CANON_EINVAL;
+    if (rows > 0 && cols > 0 && x == nullptr) return CANON_EINVAL;
+    if (rows > 0 && ycols > 0 && y == nullptr) return CANON_EINVAL;
+    if (rows == 0 || ycols == 0) return CANON_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (cols == 0) return hip_status(launch_put_column<T>(y, ldy, rows, out->init, st));
     if (is_ip(policy, param)) {
         const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                         (ldy * sizeof(T)) % 16 == 0;
@@ -196,15 +212,15 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
                 check_ws(ws, ws_bytes, scan_rows_ws(rows, cols, policy, param, sizeof(T))))
             return s;
         return hip_status(launch_scan_ip<T>(x, ldx, y, ldy, rows, cols,
-                                            static_cast<uint32_t*>(ws), ip_nodes<T>(ws), ip,
-                                            static_cast<hipStream_t>(stream)));
+                                            static_cast<uint32_t*>(ws), ip_nodes<T>(ws), ip, out,
+                                            st));
     }
     const bool pairwise = policy != CANON_BLOCK_DYADIC;
     const int b_log = pairwise ? 0 : log2_exact(param);
     const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                     (ldy * sizeof(T)) % 16 == 0;
-    return hip_status(launch_scan_rows<T>(x, ldx, y, ldy, rows, cols, pairwise, b_log, al,
-                                          static_cast<hipStream_t>(stream)));
+    return hip_status(
+        launch_scan_rows<T>(x, ldx, y, ldy, rows, cols, pairwise, b_log, al, out, st));
 }
 
 }  // namespace
@@ -275,13 +291,13 @@ size_t canon_scan_workspace_bytes(size_t n, int policy, uint32_t param, size_t e
 canon_status_t canon_scan_f64(const double* x, double* y, size_t n, int policy, uint32_t param,
                               void* ws, size_t ws_bytes, void* stream)
 {
-    return scan_impl<double>(x, y, n, policy, param, ws, ws_bytes, stream);
+    return scan_impl<double>(x, y, n, policy, param, nullptr, ws, ws_bytes, stream);
 }
 
 canon_status_t canon_scan_f32(const float* x, float* y, size_t n, int policy, uint32_t param,
                               void* ws, size_t ws_bytes, void* stream)
 {
-    return scan_impl<float>(x, y, n, policy, param, ws, ws_bytes, stream);
+    return scan_impl<float>(x, y, n, policy, param, nullptr, ws, ws_bytes, stream);
 }
 
 size_t canon_scan_rows_workspace_bytes(size_t rows, size_t cols, int policy, uint32_t param,
@@ -294,14 +310,52 @@ canon_status_t canon_scan_rows_f64(const double* x, size_t ldx, double* y, size_
                                    size_t rows, size_t cols, int policy, uint32_t param,
                                    void* ws, size_t ws_bytes, void* stream)
 {
-    return scan_rows_impl<double>(x, ldx, y, ldy, rows, cols, policy, param, ws, ws_bytes, stream);
+    return scan_rows_impl<double>(x, ldx, y, ldy, rows, cols, policy, param, nullptr, ws, ws_bytes,
+                                  stream);
 }
 
 canon_status_t canon_scan_rows_f32(const float* x, size_t ldx, float* y, size_t ldy, size_t rows,
                                    size_t cols, int policy, uint32_t param, void* ws,
                                    size_t ws_bytes, void* stream)
 {
-    return scan_rows_impl<float>(x, ldx, y, ldy, rows, cols, policy, param, ws, ws_bytes, stream);
+    return scan_rows_impl<float>(x, ldx, y, ldy, rows, cols, policy, param, nullptr, ws, ws_bytes,
+                                 stream);
+}
+
+canon_status_t canon_scan_with_init_f64(const double* x, double* y, size_t n, int policy,
+                                       uint32_t param, int kind, double init, void* ws,
+                                       size_t ws_bytes, void* stream)
+{
+    const ScanOut<double> out{init, kind};
+    return scan_impl<double>(x, y, n, policy, param, &out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_with_init_f32(const float* x, float* y, size_t n, int policy,
+                                       uint32_t param, int kind, float init, void* ws,
+                                       size_t ws_bytes, void* stream)
+{
+    const ScanOut<float> out{init, kind};
+    return scan_impl<float>(x, y, n, policy, param, &out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_rows_with_init_f64(const double* x, size_t ldx, double* y, size_t ldy,
+                                            size_t rows, size_t cols, int policy, uint32_t param,
+                                            int kind, double init, void* ws, size_t ws_bytes,
+                                            void* stream)
+{
+    const ScanOut<double> out{init, kind};
+    return scan_rows_impl<double>(x, ldx, y, ldy, rows, cols, policy, param, &out, ws, ws_bytes,
+                                  stream);
+}
+
+canon_status_t canon_scan_rows_with_init_f32(const float* x, size_t ldx, float* y, size_t ldy,
+                                            size_t rows, size_t cols, int policy, uint32_t param,
+                                            int kind, float init, void* ws, size_t ws_bytes,
+                                            void* stream)
+{
+    const ScanOut<float> out{init, kind};
+    return scan_rows_impl<float>(x, ldx, y, ldy, rows, cols, policy, param, &out, ws, ws_bytes,
+                                 stream);
 }
 
 canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream)

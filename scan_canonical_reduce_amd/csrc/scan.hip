@@ -1,646 +1,16 @@
-// Canonical inclusive scan, single pass over one sequence (gfx950):
-// policies pairwise and block_dyadic<B> (canonical-reduce README, P4229R0
-// "Summary" / "Key Design Points").  The in-tile network is ScanTile
-// (scan_tile.hpp); this file carries values across tiles.
-//
-// Tile-level node (k, u) covers tiles [u 2^k, (u+1) 2^k) and is the complete
-// pairwise tree over them.  Tile t needs node (k, (t >> k) - 1) for every set
-// bit k of t, and applies them as merge levels above the tile.  Every value
-// is fixed by position only, never by arrival order.  Tile numbers come from
-// an atomic counter, so every tile waited on belongs to a workgroup that is
-// already running.
-#include "device.hpp"
-#include "launch.hpp"
-#include "scan.hpp"
-#include "scan_tile.hpp"
+// Canonical inclusive scan, single pass (pairwise, block_dyadic<B>): the
+// kernels of scan_kernels.hpp with the plain inclusive output.
+#include "scan_kernels.hpp"
 
 namespace canon {
-
-// Tile-level look-back.  Tile t, in group G = t >> 6 at position r = t & 63,
-// needs node (k, (t >> k) - 1) for every set bit k of t.
-//
-//   k < 6:  rebuilt from the totals of the r tiles before t in its group
-//           (wave 0: one total per lane, butterfly in fixed lane order).
-//   k >= 6: the lowest such bit k0 names the node that ends at the most
-//           recent group G - 1.  Nodes that end within the last two groups
-//           are rebuilt from published tile totals: node (6, G-1) by wave 1
-//           and node (6, G-2) by wave 2 (64 totals each).  Then
-//             k0 == 6:  node (6, G-1)
-//             k0 >= 7:  node (k0-1, ..) + (node (k0-2, ..) + ... +
-//                       (node (7, (t >> 7) - 2) + (node (6, G-2) + node (6, G-1))))
-//           i.e. the right spine of the node, whose left siblings end at least
-//           two groups back and are read as published nodes (wave 3), as are
-//           the nodes of the bits above k0.
-// Published nodes: the last tile of each odd group forms node (6, G) from
-// its rebuilt low nodes and its own total (node (6, G) itself is never read:
-// later tiles rebuild it) and climbs, publishing node (k+1, t >> (k+1)) =
-// node (k, (t >> k) - 1) + node (k, t >> k) while bit k of t is set.  The
-// published nodes a tile reads all end before group G-1, and a climb to
-// level k waits only on one node of each lower level, so no wait is ever
-// on a chain of look-backs that grows with the number of tiles.  Every value
-// is fixed by position only.
-//
-// The words are read once right after the loads of the workgroup's next
-// tile are issued (lookback_issue), so that they arrive with that data;
-// words not ready then are polled in lookback_collect.
-struct LookbackWords {
-    uint64_t w;  // the word this lane of this wave reads (see lookback_slot)
-};
-
-// Address of the word lane `lane` of wave `wave` needs for tile t, or null.
-__device__ __forceinline__ uint64_t* lookback_slot(uint64_t t, uint64_t* __restrict__ ws,
-                                                   const ScanLayout& lay, int wave, int lane)
-{
-    const uint64_t G = t >> kGroupLog;
-    const int r = (int)(t & 63);
-    if (wave == 0) return lane < r ? ws + lay.tiles_off + (G << kGroupLog) + lane : nullptr;
-    if (wave == 1) return G >= 1 ? ws + lay.tiles_off + ((G - 1) << kGroupLog) + lane : nullptr;
-    if (wave == 2) return G >= 2 ? ws + lay.tiles_off + ((G - 2) << kGroupLog) + lane : nullptr;
-    const int k = kGroupLog + lane;
-    if (G == 0 || k >= kMaxLevels) return nullptr;
-    const int k0 = kGroupLog + __builtin_ctzll(G);
-    if (k > k0 && ((t >> k) & 1)) return ws + lay.level_off[k] + ((t >> k) - 1);
-    if (k >= kGroupLog + 1 && k < k0) return ws + lay.level_off[k] + ((t >> k) - 2);
-    return nullptr;
-}
-
-template <typename T>
-__device__ __forceinline__ LookbackWords lookback_issue(uint64_t t, uint64_t* __restrict__ ws,
-                                                        const ScanLayout& lay, int wave, int lane)
-{
-    LookbackWords w;
-    w.w = not_ready_word<T>();
-    uint64_t* slot = lookback_slot(t, ws, lay, wave, lane);
-    if (slot) w.w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return w;
-}
-
-// Complete tree over the 64 lane values, lower lanes on the left; node[k]
-// receives the value of the aligned 2^k group starting at lane
-// (r >> (k+1)) << (k+1) when bit k of r is set (r < 64), and the full tree
-// is returned.
-template <typename T>
-__device__ __forceinline__ T wave_tree(T a, int lane, int r, T (&node)[kGroupLog])
-{
-    node[0] = (r & 1) ? readlane(a, r - 1) : neg_zero<T>();
-#define CANON_BUTTERFLY(K)                                                         \
-    {                                                                              \
-        const T o = shfl_xor<(1 << ((K)-1))>(a);                                   \
-        a = ((lane >> ((K)-1)) & 1) ? (o + a) : (a + o);                           \
-        if ((K) < kGroupLog)                                                       \
-            node[(K) % kGroupLog] = ((r >> (K)) & 1)                               \
-                                        ? readlane(a, (r >> ((K) + 1)) << ((K) + 1)) \
-                                        : neg_zero<T>();                           \
-    }
-    CANON_BUTTERFLY(1)
-    CANON_BUTTERFLY(2)
-    CANON_BUTTERFLY(3)
-    CANON_BUTTERFLY(4)
-    CANON_BUTTERFLY(5)
-    CANON_BUTTERFLY(6)
-#undef CANON_BUTTERFLY
-    return readlane(a, 0);
-}
-
-// Waves 0-2 resolve their words and reduce them: s_low[0..5] = low nodes
-// (wave 0), s_g6[0] = node (6, G-1) (wave 1), s_g6[1] = node (6, G-2)
-// (wave 2).
-template <typename T>
-__device__ __forceinline__ void lookback_collect(uint64_t t, LookbackWords lw,
-                                                 uint64_t* __restrict__ ws, const ScanLayout& lay,
-                                                 uint32_t* err, T* s_low, T* s_g6, int wave,
-                                                 int lane)
-{
-    uint64_t* slot = lookback_slot(t, ws, lay, wave, lane);
-    const T a = slot ? ready_or_wait<T>(lw.w, slot, err) : neg_zero<T>();
-    T node[kGroupLog];
-    const T total = wave_tree(a, lane, wave == 0 ? (int)(t & 63) : 0, node);
-    if (lane == 0) {
-        if (wave == 0) {
-#pragma unroll
-            for (int k = 0; k < kGroupLog; ++k) s_low[k] = node[k];
-        } else {
-            s_g6[wave - 1] = total;
-        }
-    }
-}
-
-// Wave 3 resolves the published nodes of levels klo <= k < khi (lane
-// k - 6) into s_w3[k - 6].
-template <typename T>
-__device__ __forceinline__ void lookback_collect_high(uint64_t t, LookbackWords lw,
-                                                      uint64_t* __restrict__ ws,
-                                                      const ScanLayout& lay, uint32_t* err,
-                                                      T* s_w3, int lane, int klo, int khi)
-{
-    const int k = kGroupLog + lane;
-    if (k < klo || k >= khi) return;
-    uint64_t* slot = lookback_slot(t, ws, lay, 3, lane);
-    const T a = slot ? ready_or_wait<T>(lw.w, slot, err) : neg_zero<T>();
-    if (lane < kMaxLevels - kGroupLog) s_w3[lane] = a;
-}
-
-// Tiles that publish: the last tile of an odd group (bits 0..6 of t set).
-// It publishes node (k+1, t >> (k+1)) for 6 <= k < climb_top(t), the first
-// clear bit of t above bit 5; other tiles get climb_top == 6.
-__device__ __forceinline__ int climb_top(uint64_t t)
-{
-    if ((t & 127) != 127) return kGroupLog;
-    const int top = kGroupLog + __builtin_ctzll(~(t >> kGroupLog));
-    return top < kMaxLevels - 1 ? top : kMaxLevels - 1;
-}
-
-// One thread of a publishing tile: node (6, G) from the low nodes and the
-// tile's own total, then node (k+1) = node (k, (t >> k) - 1) + node (k, t >> k)
-// for k = 6 .. top-1.  Uses only the values this climb needs, so a publish
-// never waits on nodes of the bits above the climb.
-template <typename T>
-__device__ __forceinline__ void lookback_climb(uint64_t t, int top, T tile_total,
-                                               uint64_t* __restrict__ ws, const ScanLayout& lay,
-                                               const T* s_low, const T* s_g6, const T* s_w3)
-{
-    T acc = tile_total;
-    for (int k = 0; k < kGroupLog; ++k) acc = s_low[k] + acc;
-    acc = s_g6[0] + acc;
-    publish(ws + lay.level_off[kGroupLog + 1] + (t >> (kGroupLog + 1)), acc);
-    for (int k = kGroupLog + 1; k < top; ++k) {
-        acc = s_w3[k - kGroupLog] + acc;
-        publish(ws + lay.level_off[k + 1] + (t >> (k + 1)), acc);
-    }
-}
-
-// One thread: the node of every set bit of t into s_h[k].
-template <typename T>
-__device__ __forceinline__ void lookback_combine(uint64_t t, const T* s_low, const T* s_g6,
-                                                 const T* s_w3, T* s_h)
-{
-    const uint64_t G = t >> kGroupLog;
-    for (int k = 0; k < kGroupLog; ++k) s_h[k] = s_low[k];
-    if (G > 0) {
-        const int k0 = kGroupLog + __builtin_ctzll(G);
-        T acc;
-        if (k0 == kGroupLog) {
-            acc = s_g6[0];
-        } else {
-            acc = s_g6[1] + s_g6[0];
-            for (int k = kGroupLog + 1; k < k0; ++k) acc = s_w3[k - kGroupLog] + acc;
-        }
-        s_h[k0] = acc;
-        for (int k = k0 + 1; k < kMaxLevels; ++k)
-            if ((t >> k) & 1) s_h[k] = s_w3[k - kGroupLog];
-    }
-}
-
-template <typename T>
-__global__ void k_scan_init(uint64_t* __restrict__ ws, uint64_t total)
-{
-    const uint64_t nr = not_ready_word<T>();
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (uint64_t)gridDim.x * blockDim.x)
-        ws[i] = i < 32 ? 0ull : nr;
-}
-
-// Every thread of the workgroup of tile t > 0: resolves the look-back into
-// s_h[k] = node (k, (t >> k) - 1) for every set bit k of t.  A publishing
-// tile first resolves what its climb needs, publishes, and only then waits
-// for the rest.
-template <typename T>
-__device__ __forceinline__ void run_lookback(uint64_t t, T tile_total, LookbackWords lw,
-                                             uint64_t* __restrict__ ws, const ScanLayout& lay,
-                                             uint32_t* err, T* s_low, T* s_g6, T* s_w3, T* s_h,
-                                             int w, int lane)
-{
-    const int top = climb_top(t);
-    if (w < 3)
-        lookback_collect<T>(t, lw, ws, lay, err, s_low, s_g6, w, lane);
-    else if (w == 3)
-        lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, 0, top);
-    if (top > kGroupLog) {
-        __syncthreads();
-        if (threadIdx.x == 0) lookback_climb<T>(t, top, tile_total, ws, lay, s_low, s_g6, s_w3);
-    }
-    if (w == 3) lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, top, 1 << 30);
-    __syncthreads();
-    if (threadIdx.x == 0) lookback_combine<T>(t, s_low, s_g6, s_w3, s_h);
-    __syncthreads();
-}
-
-// Shared memory of the look-back.
-template <typename T>
-struct LookbackShared {
-    T h[kMaxLevels];
-    T low[kGroupLog];
-    T g6[2];
-    T w3[kMaxLevels - kGroupLog];
-};
-
-// Shared memory of a single-pass scan workgroup (the block values of
-// block_dyadic with B < tile are in dynamic shared memory).
-template <typename T>
-struct ScanShared {
-    uint32_t tile;
-    T tot[kScanWaves];
-    T tt;
-    LookbackShared<T> lb;
-};
-
-// What every phase of a single-pass scan workgroup needs.
-template <typename T>
-struct ScanCtx {
-    const T* x;
-    T* y;
-    uint64_t n;
-    int b_log;
-    uint64_t* ws;
-    const ScanLayout* lay;
-    uint32_t* err;
-    ScanShared<T>* sh;
-    T* blk;  // block values (B < tile)
-    int lane, w;
-};
-
-// Next tile number from the ticket counter, for the whole workgroup.  The
-// shared slot is rewritten only after a later barrier of the caller.
-template <typename T>
-__device__ __forceinline__ uint64_t next_ticket(const ScanCtx<T>& c)
-{
-    if (threadIdx.x == 0)
-        c.sh->tile = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(c.ws + 1), 1u,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    return c.sh->tile;
-}
-
-// Pairwise (MODE 0) and block_dyadic with B = 2 in float (MODE 2): the tile
-// network through every level, the tile-level nodes applied to every element.
-template <typename T, int MODE, bool ALIGNED, int LOGV>
-struct FullTile {
-    using ST = ScanTile<T, MODE, LOGV>;
-    struct State {
-        ST st;
-    };
-    static constexpr int LOG_S = ST::LOG_S;
-    // aligned f64 pairwise: hold the two tiles in at most 168 VGPRs (3 waves
-    // per SIMD), which they fit without spilling (measured 2-10% faster;
-    // float pairwise is there without the bound, and slower with it)
-    static constexpr int kMinWavesPerEu = (MODE == 0 && ALIGNED && sizeof(T) == 8) ? 3 : 1;
-
-    static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
-    {
-        return (t << LOG_S) + ((uint64_t)c.w << ST::LOG_WSPAN) + (uint64_t)c.lane * ST::E;
-    }
-    static __device__ __forceinline__ void load(State& s, uint64_t t, const ScanCtx<T>& c)
-    {
-        s.st.template load<ALIGNED>(c.x, c.n, g0(t, c));
-    }
-    // in-tile scan; publishes and returns the tile total
-    static __device__ __forceinline__ T front(State& s, uint64_t t, const ScanCtx<T>& c)
-    {
-        s.st.begin(c.b_log, g0(t, c));
-        s.st.in_wave(c.lane);
-        if (c.lane == 63) c.sh->tot[c.w] = s.st.last(ST::V - 1);
-        __syncthreads();
-        const T t0 = c.sh->tot[0], t1 = c.sh->tot[1], t2 = c.sh->tot[2], t3 = c.sh->tot[3];
-        const T t01 = t0 + t1;
-        const T total = t01 + (t2 + t3);
-        if (threadIdx.x == 0) publish(c.ws + c.lay->tiles_off + t, total);
-        s.st.across_waves(c.w, t0, t01, t2);
-        return total;
-    }
-    // the tile-level nodes (in c.sh->lb.h when t > 0), then the stores
-    static __device__ __forceinline__ void back(State& s, uint64_t t, const ScanCtx<T>& c)
-    {
-        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
-            if ((t >> k) & 1) s.st.apply_all(LOG_S + 1 + k, c.sh->lb.h[k]);
-        s.st.template store<ALIGNED>(c.y, c.n, g0(t, c));
-    }
-};
-
-// Canonical inclusive pairwise scan of a tile's block totals, one value
-// per block: thread tau holds blocks tau*m .. tau*m + m - 1 (m = 2^lm, at
-// most 2^LMX), the same network as the elements' (levels inside a thread,
-// across lanes, across the 4 waves), so a[k] ends as the pairwise value
-// of the block totals up to and including its block.
-template <typename T, int LMX>
-struct BlockScan {
-    static constexpr int M = 1 << LMX;
-    T a[M];
-    T tot;  // value of the thread's last block
-
-    __device__ __forceinline__ void load(const T* s, int tau, int lm, int nblk)
-    {
-        const int m = 1 << lm;
-#pragma unroll
-        for (int k = 0; k < M; ++k) {
-            const int j = tau * m + k;
-            a[k] = (k < m && j < nblk) ? s[j] : neg_zero<T>();
-        }
-    }
-
-    __device__ __forceinline__ void receive(T s)
-    {
-#pragma unroll
-        for (int k = 0; k < M; ++k) a[k] = s + a[k];
-        tot = s + tot;
-    }
-
-    template <int K>
-    __device__ __forceinline__ void lane_level(int lane)
-    {
-        const T src = from_lower_half_end<(1 << K)>(tot);
-        receive(((lane >> K) & 1) ? src : neg_zero<T>());
-    }
-
-    __device__ __forceinline__ void scan(int lm, int lane, int w, T* s_wt)
-    {
-        // levels inside the thread; entries k >= m stay -0.0
-#pragma unroll
-        for (int l = 1; l <= LMX; ++l) {
-            if (l <= lm) {
-#pragma unroll
-                for (int k = 0; k < M; ++k)
-                    if ((k >> (l - 1)) & 1) a[k] = a[((k >> l) << l) + (1 << (l - 1)) - 1] + a[k];
-            }
-        }
-        tot = a[0];
-#pragma unroll
-        for (int l = 1; l <= LMX; ++l)
-            if (l == lm) tot = a[(1 << l) - 1];
-        lane_level<0>(lane);
-        lane_level<1>(lane);
-        lane_level<2>(lane);
-        lane_level<3>(lane);
-        lane_level<4>(lane);
-        lane_level<5>(lane);
-        if (lane == 63) s_wt[w] = tot;
-        __syncthreads();
-        const T w0 = s_wt[0], w1 = s_wt[1], w2 = s_wt[2];
-        if (w & 1) receive((w & 2) ? w2 : w0);
-        if (w & 2) receive(w0 + w1);
-    }
-};
-
-// Block_dyadic with B >= E.  With n = qB + r, the value at a block's
-// interior is C + W, C = PW(x[0..qB)) the pairwise value at the end of the
-// previous block, W the pairwise prefix inside the block; at a block end it
-// is the pairwise value there.  So the levels above b reduce to one pairwise
-// scan over block totals:
-//   B < tile (BIG false): the in-tile network stops at level b (W in every
-//              element, the block total at every block end); the block totals
-//              go through BlockScan (levels above b inside the tile), then the
-//              tile-level nodes are added on the left of each block value
-//              (right-nested, lowest level first), giving G(P_j) for every
-//              block j and G(-0.0) in front of block 0; an element outputs
-//              G(P_{j-1}) + W, a block end G(P_j).
-//   B >= tile (BIG):  the whole tile lies in one block, the in-tile network is
-//              pairwise; tile-level nodes up to level b go to every element,
-//              those above b into one carry c (every element outputs c + W)
-//              and, at a tile that closes a block, into its last element.
-// LMX bounds log2 of the blocks each thread holds in BlockScan.
-template <typename T, bool ALIGNED, int LOGV, bool BIG, int LMX>
-struct SplitTile {
-    using ST = ScanTile<T, 3, LOGV>;
-    static constexpr int E = ST::E;
-    static constexpr int LOG_S = ST::LOG_S;
-    static constexpr int kMinWavesPerEu = 1;  // a tighter bound spills
-    struct State {
-        ST st;
-        BlockScan<T, LMX> bs;
-    };
-
-    static __device__ __forceinline__ int off0(const ScanCtx<T>& c)
-    {
-        return (c.w << ST::LOG_WSPAN) + c.lane * E;  // in the tile
-    }
-    static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
-    {
-        return (t << LOG_S) + (uint64_t)off0(c);
-    }
-    static __device__ __forceinline__ void load(State& s, uint64_t t, const ScanCtx<T>& c)
-    {
-        s.st.template load<ALIGNED>(c.x, c.n, g0(t, c));
-    }
-
-    static __device__ __forceinline__ T front(State& s, uint64_t t, const ScanCtx<T>& c)
-    {
-        s.st.begin(c.b_log, g0(t, c));
-        s.st.in_wave(c.lane);  // levels <= b
-        if (c.lane == 63) c.sh->tot[c.w] = s.st.last(ST::V - 1);
-        __syncthreads();
-        const T t0 = c.sh->tot[0], t1 = c.sh->tot[1], t2 = c.sh->tot[2], t3 = c.sh->tot[3];
-        const T t01 = t0 + t1;
-        s.st.across_waves(c.w, t0, t01, t2);  // levels <= b
-        T total;
-        if constexpr (BIG) {
-            total = t01 + (t2 + t3);
-        } else {
-            const int nb_log = LOG_S - c.b_log;  // log2 of the blocks in the tile
-            const int nblk = 1 << nb_log;
-            const int lm = nb_log > 8 ? nb_log - 8 : 0;
-            const int bmask = (1 << c.b_log) - 1;
-            const int o0 = off0(c);
-#pragma unroll
-            for (int u = 0; u < ST::V; ++u) {
-                const int end = o0 + u * 64 * E + E;  // one past the vector
-                if ((end & bmask) == 0) c.blk[(end >> c.b_log) - 1] = s.st.v[u][E - 1];
-            }
-            __syncthreads();
-            s.bs.load(c.blk, threadIdx.x, lm, nblk);
-            s.bs.scan(lm, c.lane, c.w, c.sh->tot);
-            if ((int)threadIdx.x == (nblk >> lm) - 1) c.sh->tt = s.bs.tot;  // complete tree
-            __syncthreads();
-            total = c.sh->tt;
-        }
-        if (threadIdx.x == 0) publish(c.ws + c.lay->tiles_off + t, total);
-        return total;
-    }
-
-    static __device__ __forceinline__ void back(State& s, uint64_t t, const ScanCtx<T>& c)
-    {
-        const T* h = c.sh->lb.h;
-        if constexpr (BIG) {
-            T cr = neg_zero<T>();
-            bool forked = false;
-            const bool closes = threadIdx.x == kScanThreads - 1 &&
-                                (((t + 1) << LOG_S) & ((1ull << c.b_log) - 1)) == 0;
-            // levels up to b (every element), then the levels above b
-            int k = 0;
-#pragma unroll 1
-            for (; k < kMaxLevels && (t >> k) != 0 && LOG_S + 1 + k <= c.b_log; ++k)
-                if ((t >> k) & 1) s.st.apply_all(LOG_S + 1 + k, h[k]);
-#pragma unroll 1
-            for (; k < kMaxLevels && (t >> k) != 0; ++k) {
-                if (!((t >> k) & 1)) continue;
-                forked = true;
-                cr = h[k] + cr;
-                if (closes) s.st.v[ST::V - 1][E - 1] = h[k] + s.st.v[ST::V - 1][E - 1];
-            }
-            if (!forked) {
-                s.st.template store<ALIGNED>(c.y, c.n, g0(t, c));
-                return;
-            }
-#pragma unroll
-            for (int u = 0; u < ST::V; ++u) {
-                T o[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    o[e] = (closes && u == ST::V - 1 && e == E - 1) ? s.st.v[u][e]
-                                                                    : cr + s.st.v[u][e];
-                s.st.template put<ALIGNED>(c.y, c.n, g0(t, c), u, o);
-            }
-        } else {
-            const int nb_log = LOG_S - c.b_log;
-            const int nblk = 1 << nb_log;
-            const int lm = nb_log > 8 ? nb_log - 8 : 0;
-            T g = neg_zero<T>();
-            for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
-                if ((t >> k) & 1) {
-                    s.bs.receive(h[k]);
-                    g = h[k] + g;
-                }
-            // c.blk[j + 1] = G(P_j), c.blk[0] = G(-0.0); every read of the
-            // block totals happened before a barrier since
-            const int m = 1 << lm;
-#pragma unroll
-            for (int k = 0; k < BlockScan<T, LMX>::M; ++k) {
-                const int j = (int)threadIdx.x * m + k;
-                if (k < m && j < nblk) c.blk[j + 1] = s.bs.a[k];
-            }
-            if (threadIdx.x == 0) c.blk[0] = g;
-            __syncthreads();
-            const int bmask = (1 << c.b_log) - 1;
-            const int o0 = off0(c);
-#pragma unroll
-            for (int u = 0; u < ST::V; ++u) {
-                const int off = o0 + u * 64 * E;
-                const int j = off >> c.b_log;
-                const bool end = ((off + E) & bmask) == 0;
-                const T cj = c.blk[j];
-                T o[E];
-#pragma unroll
-                for (int e = 0; e < E - 1; ++e) o[e] = cj + s.st.v[u][e];
-                o[E - 1] = end ? c.blk[j + 1] : cj + s.st.v[u][E - 1];
-                s.st.template put<ALIGNED>(c.y, c.n, g0(t, c), u, o);
-            }
-        }
-    }
-};
-
-// One pipeline step of a persistent workgroup: tile t is in `cur` with its
-// front done (total published).  Takes the next ticket and issues its loads
-// into `nxt`, reads t's look-back words afresh right behind them, runs the
-// next tile's front (so a tile's total never waits for another tile's
-// look-back), then resolves t's look-back (its words have had the whole
-// front to arrive) and finishes t.  Returns false when no tile is left.
-template <class P, typename T>
-__device__ __forceinline__ bool pipe_step(typename P::State& cur, typename P::State& nxt,
-                                          uint64_t& t, T& total, const ScanCtx<T>& c)
-{
-    const uint64_t tn = next_ticket(c);
-    const bool more = tn < c.lay->ntiles;
-    if (more) P::load(nxt, tn, c);
-    LookbackWords lw{};
-    if (t > 0) lw = lookback_issue<T>(t, c.ws, *c.lay, c.w, c.lane);
-    T totn = total;
-    if (more) totn = P::front(nxt, tn, c);
-    if (t > 0)
-        run_lookback<T>(t, total, lw, c.ws, *c.lay, c.err, c.sh->lb.low, c.sh->lb.g6,
-                        c.sh->lb.w3, c.sh->lb.h, c.w, c.lane);
-    P::back(cur, t, c);
-    t = tn;
-    total = totn;
-    return more;
-}
-
-// Single-pass scan kernel: a persistent grid (about as many workgroups as
-// fit at once); each workgroup walks tiles in ticket order, two at a time
-// (pipe_step).  Tile numbers come from an atomic ticket counter in the order
-// workgroups ask, so every tile waited on belongs to a workgroup that is
-// running; no front waits for anything, so every published total arrives.
-template <class P, typename T>
-__global__ __launch_bounds__(kScanThreads)
-__attribute__((amdgpu_waves_per_eu(P::kMinWavesPerEu))) void k_scan(const T* x, T* y, uint64_t n, int b_log,
-                                                       uint64_t* __restrict__ ws, ScanLayout lay)
-{
-    __shared__ ScanShared<T> sh;
-    extern __shared__ __align__(16) unsigned char s_dyn[];
-    const ScanCtx<T> c{x,   y,  n, b_log, ws, &lay, reinterpret_cast<uint32_t*>(ws), &sh,
-                       reinterpret_cast<T*>(s_dyn), (int)(threadIdx.x & 63),
-                       (int)(threadIdx.x >> 6)};
-    uint64_t t = next_ticket(c);
-    if (t >= lay.ntiles) return;
-    typename P::State a, b;
-    P::load(a, t, c);
-    T total = P::front(a, t, c);
-    for (;;) {
-        if (!pipe_step<P, T>(a, b, t, total, c)) break;
-        if (!pipe_step<P, T>(b, a, t, total, c)) break;
-    }
-}
-
-// ---------------------------------------------------------------- launchers
-template <class P, typename T>
-static hipError_t launch_k(const T* x, T* y, uint64_t n, int b_log, uint64_t* ws,
-                           const ScanLayout& lay, size_t shmem, hipStream_t s)
-{
-    constexpr auto kern = k_scan<P, T>;
-    uint64_t grid = resident_grid<kern>(kScanThreads, shmem);
-    if (grid > lay.ntiles) grid = lay.ntiles;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), shmem, s, x, y, n, b_log,
-                       ws, lay);
-    return hipGetLastError();
-}
-
-template <typename T, int MODE>
-static hipError_t launch_full(const T* x, T* y, uint64_t n, int b_log, bool aligned,
-                              uint64_t* ws, const ScanLayout& lay, hipStream_t s)
-{
-    if (aligned)
-        return launch_k<FullTile<T, MODE, true, scan_log_v<T>()>>(x, y, n, b_log, ws, lay, 0, s);
-    return launch_k<FullTile<T, MODE, false, scan_log_v<T>()>>(x, y, n, b_log, ws, lay, 0, s);
-}
-
-template <typename T, bool BIG, int LMX>
-static hipError_t launch_split_k(const T* x, T* y, uint64_t n, int b_log, bool aligned,
-                                 uint64_t* ws, const ScanLayout& lay, hipStream_t s)
-{
-    constexpr int LOG_S = scan_tile_log<T>();
-    const size_t shmem = BIG ? 0 : ((1ull << (LOG_S - b_log)) + 1) * sizeof(T);
-    if (aligned)
-        return launch_k<SplitTile<T, true, scan_log_v<T>(), BIG, LMX>>(x, y, n, b_log, ws, lay,
-                                                                      shmem, s);
-    return launch_k<SplitTile<T, false, scan_log_v<T>(), BIG, LMX>>(x, y, n, b_log, ws, lay,
-                                                                   shmem, s);
-}
-
-template <typename T>
-static hipError_t launch_split(const T* x, T* y, uint64_t n, int b_log, bool aligned,
-                               uint64_t* ws, const ScanLayout& lay, hipStream_t s)
-{
-    // blocks per thread in the block scan: 2^(log2(tile / B) - 8) when that is > 1
-    constexpr int LOG_S = scan_tile_log<T>();
-    if (b_log >= LOG_S) return launch_split_k<T, true, 0>(x, y, n, b_log, aligned, ws, lay, s);
-    const int lm = LOG_S - b_log > 8 ? LOG_S - b_log - 8 : 0;
-    if (lm <= 2) return launch_split_k<T, false, 2>(x, y, n, b_log, aligned, ws, lay, s);
-    return launch_split_k<T, false, 4>(x, y, n, b_log, aligned, ws, lay, s);
-}
 
 template <typename T>
 hipError_t launch_scan(const T* x, T* y, uint64_t n, bool pairwise, int b_log, bool aligned,
                        uint64_t* ws, const ScanLayout& lay, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
-    uint64_t blocks = (lay.total_words + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL((k_scan_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws,
-                       lay.total_words);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (pairwise || b_log == 0) return launch_full<T, 0>(x, y, n, 0, aligned, ws, lay, s);
-    if constexpr (Elem<T>::LOGE >= 2) {
-        if (b_log < Elem<T>::LOGE) return launch_full<T, 2>(x, y, n, b_log, aligned, ws, lay, s);
-    }
-    return launch_split<T>(x, y, n, b_log, aligned, ws, lay, s);
+    return launch_scan_impl<T, false>(x, y, n, pairwise, b_log, aligned, ws, lay, ScanOut<T>{},
+                                      s);
 }
 
 template hipError_t launch_scan<double>(const double*, double*, uint64_t, bool, int, bool,

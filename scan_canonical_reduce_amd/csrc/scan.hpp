@@ -68,13 +68,38 @@ constexpr int scan_tile_log()
     return (sizeof(T) == 8 ? 1 : 2) + 6 + scan_log_v<T>() + 2;  // log2(E * 64 * V * waves)
 }
 
+// Output of a scan with an initial value.  S_i is the policy's value on
+// x[0..i] and S_{-1} the empty prefix:
+//   kScanInclusive       y[i] = init + S_i        (n outputs)
+//   kScanExclusive       y[i] = init + S_{i-1}    (n outputs; y[0] = init)
+//   kScanIncludeInitial  the same for i <= n      (n + 1 outputs)
+enum ScanKind : int { kScanInclusive = 0, kScanExclusive = 1, kScanIncludeInitial = 2 };
+
+template <typename T>
+struct ScanOut {
+    T init;
+    int kind;
+};
+
 template <typename T>
 hipError_t launch_scan(const T* x, T* y, uint64_t n, bool pairwise, int b_log, bool aligned,
                        uint64_t* ws, const ScanLayout& lay, hipStream_t s);
 
 template <typename T>
+hipError_t launch_scan_with_init(const T* x, T* y, uint64_t n, bool pairwise, int b_log,
+                                 bool aligned, uint64_t* ws, const ScanLayout& lay,
+                                 const ScanOut<T>& out, hipStream_t s);
+
+// y[r * ldy] = v for r < rows, on stream s.
+template <typename T>
+hipError_t launch_put_column(T* y, uint64_t ldy, uint64_t rows, T v, hipStream_t s);
+
+// out == null: the plain inclusive scan of every row; else the scan with an
+// initial value that *out describes.
+template <typename T>
 hipError_t launch_scan_rows(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
-                            uint64_t cols, bool pairwise, int b_log, bool aligned, hipStream_t s);
+                            uint64_t cols, bool pairwise, int b_log, bool aligned,
+                            const ScanOut<T>* out, hipStream_t s);
 
 
 }  // namespace canon

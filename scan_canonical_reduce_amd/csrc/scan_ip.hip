@@ -114,11 +114,11 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_nodes(T* __restrict__ nodes, 
 // Kernel 3: the scan.  LDS holds one tree per row for rows -1 .. R-1 of the
 // tile: tree ri (row ri - 1) has Lp leaves at [ri * 2Lp, ri * 2Lp + Lp) and
 // level l at offset 2Lp - (2Lp >> l).
-template <typename T>
+template <typename T, bool OUTX>
 __global__ __launch_bounds__(kIpThreads) void k_ip_scan(const T* __restrict__ x, uint64_t ldx,
                                                         T* __restrict__ y, uint64_t ldy,
                                                         uint64_t cols, const T* __restrict__ nodes,
-                                                        IpLayout lay)
+                                                        IpLayout lay, T init, int kind)
 {
     extern __shared__ unsigned char ip_smem[];
     T* tree = reinterpret_cast<T*>(ip_smem);
@@ -167,12 +167,7 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan(const T* __restrict__ x,
         }
 
         // the walk from each lane to the root
-        const uint64_t elems = (uint64_t)R * L;
-        for (uint64_t e = threadIdx.x; e < elems; e += kIpThreads) {
-            const int r = (int)(e / L);
-            const uint64_t i = e % L;
-            const uint64_t gi = (t * R + r) * L + i;
-            if (gi >= cols) continue;
+        auto walk = [&](int r, uint64_t i) {
             T val = lvl(r + 1, 0)[i];
             for (int l = 1; l <= lay.lp_log; ++l) {
                 const uint64_t pos = i >> (l - 1);
@@ -180,7 +175,26 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan(const T* __restrict__ x,
                 if (pos & 1) val = lvl(r + 1, l - 1)[sib] + val;  // left sibling: A values
                 else val = val + lvl(r, l - 1)[sib];              // right sibling: B values
             }
-            ys[gi] = val;
+            return val;
+        };
+        const uint64_t elems = (uint64_t)R * L;
+        for (uint64_t e = threadIdx.x; e < elems; e += kIpThreads) {
+            const int r = (int)(e / L);
+            const uint64_t i = e % L;
+            const uint64_t gi = (t * R + r) * L + i;
+            if (gi >= cols) continue;
+            if constexpr (!OUTX) {
+                ys[gi] = walk(r, i);
+            } else if (kind == kScanInclusive) {
+                ys[gi] = init + walk(r, i);
+            } else {
+                // the value before element (r, i): lane i - 1 of the same
+                // row, or at lane 0 the end of the previous row, which is the
+                // root of that row's tree (the B tree of row r; -0.0 before
+                // the first element)
+                ys[gi] = init + (i > 0 ? walk(r, i - 1) : lvl(r, lay.lp_log)[0]);
+                if (kind == kScanIncludeInitial && gi + 1 == cols) ys[cols] = init + walk(r, i);
+            }
         }
         __syncthreads();  // the trees are rebuilt for the next tile
     }
@@ -278,6 +292,7 @@ struct IpRowTree {
     T sv[LOGE][RV][E];
     T o[6][RV];
     T pv[LOGRV > 0 ? LOGRV : 1][RV];
+    T root;  // the complete tree over the whole row (the same in every lane)
 
     // row = vectors rows[v0 .. v0 + RV)
     template <int NV>
@@ -322,6 +337,7 @@ struct IpRowTree {
 #pragma unroll
             for (int i = 0; i < RV / (2 * h); ++i) p[2 * i * h] = p[2 * i * h] + p[(2 * i + 1) * h];
         }
+        root = p[0];
     }
 };
 
@@ -412,12 +428,12 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_totals_fast(const T* __restri
 }
 
 // Kernel 3 (fast): the scan.
-template <typename T, int LOGRV>
+template <typename T, int LOGRV, bool OUTX>
 __global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict__ x, uint64_t ldx,
                                                              T* __restrict__ y, uint64_t ldy,
                                                              uint64_t cols,
                                                              const T* __restrict__ nodes,
-                                                             IpLayout lay)
+                                                             IpLayout lay, T init, int kind)
 {
     using F = IpFast<T, LOGRV>;
     constexpr int E = F::E, RV = F::RV, RW = F::RW;
@@ -511,6 +527,37 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict
             ip_walk<T, LOGRV>(a, r * RV, ta, tb, lane, val);
             // store row r
             const uint64_t row = row0 + (uint64_t)w * RW + r;
+            if constexpr (OUTX) {
+                if (kind != kScanInclusive) {
+                    // one position up: the value before lane slot 0 of a
+                    // vector comes from lane - 1, from lane 63 of the
+                    // previous vector, or, at the row's start, from the end
+                    // of the previous row (the root of the B tree; -0.0
+                    // before the first element)
+                    if (kind == kScanIncludeInitial) {
+#pragma unroll
+                        for (int q = 0; q < RV; ++q)
+#pragma unroll
+                            for (int e = 0; e < E; ++e)
+                                if (row * F::L + (uint64_t)(q * 64 + lane) * E + e + 1 == cols)
+                                    ys[cols] = init + val[q][e];
+                    }
+                    T prev = tb.root;
+#pragma unroll
+                    for (int q = 0; q < RV; ++q) {
+                        const T up = shfl_up1(val[q][E - 1]);
+                        const T before = lane == 0 ? prev : up;
+                        prev = readlane(val[q][E - 1], 63);
+#pragma unroll
+                        for (int e = E - 1; e > 0; --e) val[q][e] = val[q][e - 1];
+                        val[q][0] = before;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < RV; ++q)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) val[q][e] = init + val[q][e];
+            }
 #pragma unroll
             for (int q = 0; q < RV; ++q) {
                 const uint64_t gi = row * F::L + (uint64_t)(q * 64 + lane) * E;
@@ -529,9 +576,10 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan_fast(const T* __restrict
 }
 
 // ---------------------------------------------------------------- launcher
-template <typename T, int LOGRV>
+template <typename T, int LOGRV, bool OUTX>
 static hipError_t launch_ip_fast(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
-                                 uint32_t* err, T* nodes, const IpLayout& lay, hipStream_t s)
+                                 uint32_t* err, T* nodes, const IpLayout& lay,
+                                 const ScanOut<T>& out, hipStream_t s)
 {
     const uint64_t items = lay.nseg * lay.tps;
     const unsigned grid = (unsigned)(items < kIpMaxGrid ? items : kIpMaxGrid);
@@ -541,23 +589,23 @@ static hipError_t launch_ip_fast(const T* x, uint64_t ldx, T* y, uint64_t ldy, u
     if (e != hipSuccess) return e;
     e = launch_ip_nodes<T>(nodes, lay, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ip_scan_fast<T, LOGRV>), dim3(grid), dim3(kIpThreads), 0, s, x, ldx, y,
-                       ldy, cols, nodes, lay);
+    hipLaunchKernelGGL((k_ip_scan_fast<T, LOGRV, OUTX>), dim3(grid), dim3(kIpThreads), 0, s, x,
+                       ldx, y, ldy, cols, nodes, lay, out.init, out.kind);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,
-                          uint64_t cols, uint32_t* err, T* nodes, const IpLayout& lay,
-                          hipStream_t s)
+template <typename T, bool OUTX>
+static hipError_t launch_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                            uint32_t* err, T* nodes, const IpLayout& lay, const ScanOut<T>& out,
+                            hipStream_t s)
 {
-    if (nseg == 0 || cols == 0) return hipSuccess;
     if (lay.fast_logrv >= 0) {
         switch (lay.fast_logrv) {
-            case 0: return launch_ip_fast<T, 0>(x, ldx, y, ldy, cols, err, nodes, lay, s);
-            case 1: return launch_ip_fast<T, 1>(x, ldx, y, ldy, cols, err, nodes, lay, s);
-            case 2: return launch_ip_fast<T, 2>(x, ldx, y, ldy, cols, err, nodes, lay, s);
-            default: return launch_ip_fast<T, 3>(x, ldx, y, ldy, cols, err, nodes, lay, s);
+            case 0: return launch_ip_fast<T, 0, OUTX>(x, ldx, y, ldy, cols, err, nodes, lay, out, s);
+            case 1: return launch_ip_fast<T, 1, OUTX>(x, ldx, y, ldy, cols, err, nodes, lay, out, s);
+            case 2: return launch_ip_fast<T, 2, OUTX>(x, ldx, y, ldy, cols, err, nodes, lay, out, s);
+            default:
+                return launch_ip_fast<T, 3, OUTX>(x, ldx, y, ldy, cols, err, nodes, lay, out, s);
         }
     }
     const uint64_t items = lay.nseg * lay.tps;
@@ -569,16 +617,31 @@ hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t
     e = launch_ip_nodes<T>(nodes, lay, s);
     if (e != hipSuccess) return e;
     const size_t lds = ip_lds_bytes(lay, sizeof(T));
-    hipLaunchKernelGGL((k_ip_scan<T>), dim3(grid), dim3(kIpThreads), lds, s, x, ldx, y, ldy, cols,
-                       nodes, lay);
+    hipLaunchKernelGGL((k_ip_scan<T, OUTX>), dim3(grid), dim3(kIpThreads), lds, s, x, ldx, y, ldy,
+                       cols, nodes, lay, out.init, out.kind);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,
+                          uint64_t cols, uint32_t* err, T* nodes, const IpLayout& lay,
+                          const ScanOut<T>* out, hipStream_t s)
+{
+    if (nseg == 0) return hipSuccess;
+    if (cols == 0) {
+        if (out && out->kind == kScanIncludeInitial)
+            return launch_put_column(y, ldy, nseg, out->init, s);
+        return hipSuccess;
+    }
+    if (out) return launch_ip<T, true>(x, ldx, y, ldy, cols, err, nodes, lay, *out, s);
+    return launch_ip<T, false>(x, ldx, y, ldy, cols, err, nodes, lay, ScanOut<T>{}, s);
 }
 
 template hipError_t launch_scan_ip<double>(const double*, uint64_t, double*, uint64_t, uint64_t,
                                            uint64_t, uint32_t*, double*, const IpLayout&,
-                                           hipStream_t);
+                                           const ScanOut<double>*, hipStream_t);
 template hipError_t launch_scan_ip<float>(const float*, uint64_t, float*, uint64_t, uint64_t,
                                           uint64_t, uint32_t*, float*, const IpLayout&,
-                                          hipStream_t);
+                                          const ScanOut<float>*, hipStream_t);
 
 }  // namespace canon

@@ -75,9 +75,14 @@ inline size_t ip_lds_bytes(const IpLayout& lay, size_t elem_size)
     return (size_t)((1ull << lay.r_log) + 1) * 2 * (1ull << lay.lp_log) * elem_size;
 }
 
+// out == null: the plain inclusive scan; else the scan with an initial
+// value that *out describes (ScanOut, scan.hpp).
+template <typename T>
+struct ScanOut;
+
 template <typename T>
 hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,
                           uint64_t cols, uint32_t* err, T* nodes, const IpLayout& lay,
-                          hipStream_t s);
+                          const ScanOut<T>* out, hipStream_t s);
 
 }  // namespace canon

@@ -267,26 +267,88 @@ struct ScanTile {
         }
     }
 
+    // Final inclusive values o[0..E) of vector u (block_dyadic: C + W off
+    // the block ends).
+    __device__ __forceinline__ void final_vec(int u, T (&o)[E]) const
+    {
+        if (!BD || !forked) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = v[u][e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                constexpr int BS = E / NB;  // slots per block inside a vector
+                const int k = e / BS;
+                const bool end = (MODE == 2) ? ((e % BS) == BS - 1)
+                                             : (e == E - 1 && ((endm >> u) & 1));
+                o[e] = end ? v[u][e] : c[u][k] + v[u][e];
+            }
+        }
+    }
+
     template <bool ALIGNED>
     __device__ __forceinline__ void store(T* __restrict__ y, uint64_t n, uint64_t g0) const
     {
 #pragma unroll
         for (int u = 0; u < V; ++u) {
             T o[E];
-            if (!BD || !forked) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) o[e] = v[u][e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    constexpr int BS = E / NB;  // slots per block inside a vector
-                    const int k = e / BS;
-                    const bool end = (MODE == 2) ? ((e % BS) == BS - 1)
-                                                 : (e == E - 1 && ((endm >> u) & 1));
-                    o[e] = end ? v[u][e] : c[u][k] + v[u][e];
-                }
-            }
+            final_vec(u, o);
             put<ALIGNED>(y, n, g0, u, o);
+        }
+    }
+
+    // Output stage of a scan with an initial value.  fin(u, o) gives the
+    // final inclusive values S of vector u (sequence indices g0 + u*64*E +
+    // e).  kind 0 writes y[i] = init + S_i.  Kinds 1 and 2 write y[i] = init
+    // + S_{i-1}: the value before a thread's first element comes from lane
+    // l - 1, from lane 63 of the previous vector, from the previous wave's
+    // last element (exchanged in s_wend) or, for the tile's first element,
+    // `pre`, the value of the element before the tile (-0.0, the empty
+    // prefix, before the sequence's first element, so that y[0] = init +
+    // -0.0 = init).  Every write stays inside the tile's own positions
+    // (clipped to n), so the scan may run in place; with kind 2 the holder of
+    // element n - 1 also writes y[n] = init + S_{n-1}.  Every thread of the
+    // workgroup calls this (one barrier inside for kinds 1 and 2).
+    template <bool ALIGNED, class F>
+    __device__ __forceinline__ void emit(T* __restrict__ y, uint64_t n, uint64_t g0, T init,
+                                         int kind, T pre, T* s_wend, int w, int lane,
+                                         F&& fin) const
+    {
+        if (kind == 0) {
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                T o[E];
+                fin(u, o);
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = init + o[e];
+                put<ALIGNED>(y, n, g0, u, o);
+            }
+            return;
+        }
+        {
+            T o[E];
+            fin(V - 1, o);
+            if (lane == 63) s_wend[w] = o[E - 1];
+        }
+        __syncthreads();
+        T carry = w == 0 ? pre : s_wend[w - 1];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            T o[E];
+            fin(u, o);
+            const T up = shfl_up1(o[E - 1]);
+            T s[E];
+            s[0] = init + (lane == 0 ? carry : up);
+#pragma unroll
+            for (int e = 1; e < E; ++e) s[e] = init + o[e - 1];
+            carry = readlane(o[E - 1], 63);
+            if (kind == 2) {
+                const uint64_t gi = g0 + (uint64_t)u * 64 * E;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (gi + e == n - 1) y[n] = init + o[e];
+            }
+            put<ALIGNED>(y, n, g0, u, s);
         }
     }
 };

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(canon):
 
 def test_version_and_status_strings(canon):
     L = canon.lib()
-    assert L.canon_abi_version() == 1
+    assert L.canon_abi_version() == 2
     for s in range(5):
         assert L.canon_status_str(s).decode().startswith("CANON_")
     assert L.canon_last_hip_error() == 0
@@ -103,6 +103,30 @@ def test_scan_argument_errors(canon):
     assert L.canon_scan_rows_f64(fake, 5, fake, 10, 3, 10, 0, 0, None, 0, None) == 1
     assert L.canon_scan_rows_f64(fake, 10, fake, 5, 3, 10, 0, 0, None, 0, None) == 1
     assert L.canon_workspace_error(None, None, None) == 1
+
+
+def test_scan_with_init_argument_errors(canon):
+    L = canon.lib()
+    fake = ctypes.c_void_p(0x1000)
+    f = L.canon_scan_with_init_f64
+    assert f(fake, fake, 10, 0, 0, 3, 1.0, None, 0, None) == 1       # bad kind
+    assert f(fake, fake, 10, 0, 0, -1, 1.0, None, 0, None) == 1      # bad kind
+    assert f(fake, fake, 10, 7, 0, 0, 1.0, None, 0, None) == 1       # bad policy
+    assert f(None, fake, 10, 0, 0, 1, 1.0, None, 0, None) == 1       # no input
+    assert f(fake, fake, 1 << 20, 0, 0, 1, 1.0, None, 0, None) == 3  # no workspace
+    assert f(fake, fake, 1 << 20, 1, 128, 2, 1.0, None, 0, None) == 3
+    assert f(None, None, 0, 0, 0, 0, 1.0, None, 0, None) == 0        # nothing to do
+    assert f(None, None, 0, 0, 0, 1, 1.0, None, 0, None) == 0
+    assert f(None, None, 0, 0, 0, 2, 1.0, None, 0, None) == 1        # include_initial needs y
+    assert L.canon_scan_with_init_f32(fake, fake, 10, 2, 12, 0, 1.0, None, 0, None) == 1
+    g = L.canon_scan_rows_with_init_f64
+    # include_initial needs ldy >= cols + 1
+    assert g(fake, 10, fake, 10, 3, 10, 0, 0, 2, 0.0, None, 0, None) == 1
+    assert g(fake, 10, fake, 10, 3, 10, 0, 0, 5, 0.0, None, 0, None) == 1
+    assert g(fake, 10, fake, 11, 3, 10, 1, 16, 2, 0.0, None, 0, None) == 3  # no workspace
+    assert g(None, 10, None, 11, 0, 10, 0, 0, 2, 0.0, None, 0, None) == 0   # no rows
+    assert g(None, 1, None, 1, 3, 0, 0, 0, 2, 0.0, None, 0, None) == 1      # cols 0: y needed
+    assert g(None, 1, None, 1, 3, 0, 0, 0, 1, 0.0, None, 0, None) == 0      # nothing to write
 
 
 def test_binding_refuses_cpu_tensors(canon):
