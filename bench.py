@@ -379,6 +379,35 @@ def run_configs(torch, canon, synth, dev, reps=20):
                                      ("block_dyadic", 256)), False)
     scan_cfg("C5", "scan_2e28_f32", (("block_dyadic", 256),), False)
 
+    def scan_init_cfg(cfg, name, cases):
+        """Scans with an initial value on a workload's input: 34 sampled
+        outputs (first, last and random) evaluated from scratch."""
+        xn = synth.config_input(name)
+        x = torch.from_numpy(xn).to(dev)
+        y = torch.empty(xn.size + 1, dtype=x.dtype, device=dev)
+        for pol, q, kind, init in cases:
+            m = xn.size + (1 if kind == "include_initial" else 0)
+            ws = torch.empty(max(canon.scan_workspace_bytes(xn.size, pol, q, xn.itemsize), 1),
+                             dtype=torch.uint8, device=dev)
+            canon.scan_with_init(x, pol, q, kind, init, out=y[:m], ws=ws)
+            ok = canon.workspace_error(ws) == 0
+            idx = np.unique(np.concatenate([[0, 1, m - 1], rng.integers(0, m, 31)]))
+            got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
+            want = [oracle.scan_with_init_output(xn, int(k), pol, q, init, kind) for k in idx]
+            ok = ok and same(got, want)
+            us = timed(lambda: canon.scan_with_init(x, pol, q, kind, init, out=y[:m], ws=ws))
+            label = pol if pol == "pairwise" else f"{pol}<{q}>"
+            add(cfg, f"scan {kind} init={init} {label}", str(xn.dtype), xn.size,
+                xn.nbytes + m * xn.itemsize, us, ok)
+
+    scan_init_cfg("C5 with init", "scan_2e27_f64",
+                  (("block_dyadic", 16, "exclusive", 1.0),
+                   ("block_dyadic", 256, "include_initial", 1.0),
+                   ("pairwise", 0, "exclusive", 1.0),
+                   ("iterated_pairwise", 128, "exclusive", 1.0),
+                   ("block_dyadic", 16, "inclusive", 1.0)))
+    scan_init_cfg("C5 with init", "scan_2e28_f32", (("block_dyadic", 256, "exclusive", 1.0),))
+
     print("| config | op | dtype | N | us | GB/s | % of 8 TB/s | elements/s | bit-exact |")
     print("|---|---|---|---|---|---|---|---|---|")
     for cfg, op, dt, n, us, gbs, pct, eps, ok in rows:

@@ -211,6 +211,20 @@ def scan_with_init(x: np.ndarray, policy, param: int = 0, init=-0.0,
     return y
 
 
+def scan_with_init_output(x: np.ndarray, k: int, policy, param: int = 0, init=-0.0,
+                          kind="inclusive"):
+    """Output k of scan_with_init, evaluated from scratch: init + the policy's
+    expression over the prefix it observes (scan_prefix), one addition in
+    x's dtype; init alone for the empty prefix."""
+    x = _c(x)
+    kd = _kind(kind)
+    m = k + 1 if kd == 0 else k
+    if kd not in (0, 1, 2) or k < 0 or m > x.size or (kd != 2 and k >= x.size):
+        raise ValueError("bad output index or kind")
+    t = x.dtype.type
+    return t(init) if m == 0 else t(t(init) + scan_prefix(x, m - 1, policy, param))
+
+
 def scan_rows_with_init(X: np.ndarray, policy, param: int = 0, init=-0.0, kind="inclusive",
                         cols: int | None = None) -> np.ndarray:
     """Per-row scan_with_init of a 2-D array (``cols`` as in scan_rows).  The

@@ -151,6 +151,21 @@ def test_equals_symbolic(dtype, kind, policy, param):
     assert same_bits(got, np.array(want, dtype=dtype))
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 8),
+                                          ("iterated_pairwise", 5)])
+def test_single_output_from_scratch(dtype, kind, policy, param):
+    """The from-scratch single output (literal prefix evaluation) agrees with
+    the streaming form at every position."""
+    x = synth.generate(130, "mixed_magnitude", 22, dtype)
+    y = oracle.scan_with_init(x, policy, param, 0.7, kind)
+    for k in range(y.size):
+        assert same_bits(oracle.scan_with_init_output(x, k, policy, param, 0.7, kind), y[k])
+    with pytest.raises(ValueError):
+        oracle.scan_with_init_output(x, y.size, policy, param, 0.7, kind)
+
+
 def test_symbolic_shapes():
     assert S.to_str(S.scan_with_init_tree(0, "pairwise", 0, "exclusive")) == "I"
     assert S.to_str(S.scan_with_init_tree(0, "pairwise", 0, "inclusive")) == "(Ia)"
