@@ -45,6 +45,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # sources whose kernels the traffic summaries describe
 KERNEL_SOURCES = ["device.hpp", "launch.hpp", "reduce.hpp", "reduce.hip", "scan.hpp",
                   "scan_tile.hpp", "scan_kernels.hpp", "scan.hip", "scan_with_init.hip",
+                  "scan_wide.hip", "scan_wide_init.hip",
                   "scan_rows.hip", "scan_ip.hpp", "scan_ip.hip"]
 
 

@@ -15,7 +15,8 @@ OUT = os.path.join(HERE, "libcanon.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libcanon")
 
 SOURCES = [
-    "api.cpp", "reduce.hip", "scan.hip", "scan_with_init.hip", "scan_rows.hip", "scan_ip.hip",
+    "api.cpp", "reduce.hip", "scan.hip", "scan_with_init.hip", "scan_wide.hip",
+    "scan_wide_init.hip", "scan_rows.hip", "scan_ip.hip",
 ]
 
 # -ffp-contract=off: no FMA contraction; no fast-math; packed FP32 disabled.

@@ -570,6 +570,127 @@ struct SplitTile {
     }
 };
 
+// block_dyadic with whole-vector blocks inside one wave: B = 64 E 2^VLOG
+// with VLOG <= LOGV, so every block is 2^VLOG whole vectors of one wave and
+// a block's value and its carry are the same for all 64 lanes.  The tile
+// network runs the levels <= b (inside a vector, across lanes, and the
+// vector levels below VLOG: the pairwise network, which needs no gating);
+// each wave then moves its NBW = 2^(LOGV - VLOG) block totals into lanes
+// 0..NBW-1 and runs the pairwise scan of the block totals across those
+// lanes; the wave totals (the complete trees of the waves, by closure) merge
+// across the 4 waves as in the pairwise network, one barrier in all.  p
+// (lane j) then holds the pairwise value of the tile's blocks up to block j
+// of this wave, and wpre that of the blocks before the wave.  The back adds
+// the tile-level nodes on the left of both; an element outputs (value at
+// the previous block end) + W, and a block end its own block's value.
+template <typename T, bool ALIGNED, int LOGV, int VLOG, bool OUTX>
+struct WideTile {
+    using ST = ScanTile<T, 0, LOGV>;
+    static constexpr int E = ST::E;
+    static constexpr int LOGE = ST::LOGE;
+    static constexpr int V = ST::V;
+    static constexpr int LOG_S = ST::LOG_S;
+    static constexpr int VPB = 1 << VLOG;             // vectors per block
+    static constexpr int NBW_LOG = LOGV - VLOG;       // log2 blocks per wave
+    static_assert(VLOG >= 0 && VLOG <= LOGV, "blocks of whole vectors inside one wave");
+    static constexpr int kMinWavesPerEu = 1;
+    struct State {
+        ST st;
+        T p;     // lane j < 2^NBW_LOG: pairwise value of the blocks up to block j of this wave
+        T wpre;  // pairwise value of the tile's blocks before this wave (-0.0 for wave 0)
+    };
+
+    static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
+    {
+        return (t << LOG_S) + ((uint64_t)c.w << ST::LOG_WSPAN) + (uint64_t)c.lane * E;
+    }
+    static __device__ __forceinline__ void load(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        s.st.template load<ALIGNED>(c.x, c.n, g0(t, c));
+    }
+
+    static __device__ __forceinline__ T front(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        // levels <= b: W (the pairwise prefix inside the block) in every element
+        s.st.slot_levels();
+        s.st.template lane_level<0>(c.lane);
+        s.st.template lane_level<1>(c.lane);
+        s.st.template lane_level<2>(c.lane);
+        s.st.template lane_level<3>(c.lane);
+        s.st.template lane_level<4>(c.lane);
+        s.st.template lane_level<5>(c.lane);
+        if constexpr (VLOG >= 1) s.st.template vector_level<0>();
+        if constexpr (VLOG >= 2) s.st.template vector_level<1>();
+        if constexpr (VLOG >= 3) s.st.template vector_level<2>();
+        if constexpr (VLOG >= 4) s.st.template vector_level<3>();
+        T p = neg_zero<T>();
+#pragma unroll
+        for (int j = 0; j < (1 << NBW_LOG); ++j) {
+            const T sj = readlane(s.st.v[(j + 1) * VPB - 1][E - 1], 63);  // block j's total
+            p = c.lane == j ? sj : p;
+        }
+#define CANON_WIDE_LANE(K)                                                    \
+    if constexpr ((K) < NBW_LOG) {                                            \
+        const T src = from_lower_half_end<(1 << (K))>(p);                     \
+        p = (((c.lane >> (K)) & 1) ? src : neg_zero<T>()) + p;                \
+    }
+        CANON_WIDE_LANE(0)
+        CANON_WIDE_LANE(1)
+        CANON_WIDE_LANE(2)
+        CANON_WIDE_LANE(3)
+        CANON_WIDE_LANE(4)
+        CANON_WIDE_LANE(5)
+#undef CANON_WIDE_LANE
+        const T wt = readlane(p, (1 << NBW_LOG) - 1);  // complete tree of the wave
+        if (c.lane == 0) c.sh->tot[c.w] = wt;
+        __syncthreads();
+        const T t0 = c.sh->tot[0], t1 = c.sh->tot[1], t2 = c.sh->tot[2], t3 = c.sh->tot[3];
+        const T t01 = t0 + t1;
+        const T total = t01 + (t2 + t3);
+        if (threadIdx.x == 0) publish(c.ws + c.lay->tiles_off + t, total);
+        if (c.w & 1) p = ((c.w & 2) ? t2 : t0) + p;
+        if (c.w & 2) p = t01 + p;
+        s.wpre = c.w == 0 ? neg_zero<T>() : c.w == 1 ? t0 : c.w == 2 ? t01 : t01 + t2;
+        s.p = p;
+        return total;
+    }
+
+    static __device__ __forceinline__ void back(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        const T* h = c.sh->lb.h;
+        T p = s.p, cw = s.wpre;
+        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
+            if ((t >> k) & 1) {
+                p = h[k] + p;
+                cw = h[k] + cw;
+            }
+        // the value at the end of block j - 1 (cw before the wave's first
+        // block) and at the end of block j, for the block of vector u
+        auto fin = [&](int u, T(&o)[E]) {
+            const int j = u / VPB;
+            const T cj = j == 0 ? cw : readlane(p, j - 1);
+#pragma unroll
+            for (int e = 0; e < E - 1; ++e) o[e] = cj + s.st.v[u][e];
+            if ((u + 1) % VPB == 0)
+                o[E - 1] = c.lane == 63 ? readlane(p, j) : cj + s.st.v[u][E - 1];
+            else
+                o[E - 1] = cj + s.st.v[u][E - 1];
+        };
+        if constexpr (OUTX) {
+            // the element before the wave's first one ends the previous
+            // wave's last block (or the tile before): its value is cw
+            s.st.template emit_known<ALIGNED>(c.y, c.n, g0(t, c), c.init, c.kind, cw, c.lane, fin);
+        } else {
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                T o[E];
+                fin(u, o);
+                s.st.template put<ALIGNED>(c.y, c.n, g0(t, c), u, o);
+            }
+        }
+    }
+};
+
 // One pipeline step of a persistent workgroup: tile t is in `cur` with its
 // front done (total published).  Takes the next ticket and issues its loads
 // into `nxt`, reads t's look-back words afresh right behind them, runs the
@@ -673,6 +794,35 @@ static hipError_t launch_split_k(const T* x, T* y, uint64_t n, int b_log, bool a
                                                                           shmem, out, s);
 }
 
+// The WideTile kernels are instantiated in their own translation unit
+// (scan_wide.hip).
+template <typename T, bool OUTX>
+hipError_t launch_wide(const T* x, T* y, uint64_t n, int b_log, bool aligned, uint64_t* ws,
+                       const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s);
+
+template <typename T, bool OUTX>
+hipError_t launch_wide_impl(const T* x, T* y, uint64_t n, int b_log, bool aligned, uint64_t* ws,
+                            const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s)
+{
+    constexpr int LOGV = scan_log_v<T>();
+    const int vlog = b_log - (Elem<T>::LOGE + 6);
+#define CANON_WIDE_CASE(VL)                                                                 \
+    case VL:                                                                                \
+        if (aligned)                                                                        \
+            return launch_k<WideTile<T, true, LOGV, VL, OUTX>>(x, y, n, b_log, ws, lay, 0, out, \
+                                                               s);                          \
+        return launch_k<WideTile<T, false, LOGV, VL, OUTX>>(x, y, n, b_log, ws, lay, 0, out, s);
+    switch (vlog) {
+        CANON_WIDE_CASE(0)
+        CANON_WIDE_CASE(1)
+        CANON_WIDE_CASE(2)
+        CANON_WIDE_CASE(3)
+        CANON_WIDE_CASE(4)
+        default: return hipErrorInvalidValue;
+    }
+#undef CANON_WIDE_CASE
+}
+
 template <typename T, bool OUTX>
 static hipError_t launch_split(const T* x, T* y, uint64_t n, int b_log, bool aligned,
                                uint64_t* ws, const ScanLayout& lay, const ScanOut<T>& out,
@@ -682,6 +832,9 @@ static hipError_t launch_split(const T* x, T* y, uint64_t n, int b_log, bool ali
     constexpr int LOG_S = scan_tile_log<T>();
     if (b_log >= LOG_S)
         return launch_split_k<T, true, 0, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
+    constexpr int LOG_WSPAN = LOG_S - 2;
+    if (b_log >= Elem<T>::LOGE + 6 && b_log <= LOG_WSPAN)
+        return launch_wide<T, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
     const int lm = LOG_S - b_log > 8 ? LOG_S - b_log - 8 : 0;
     if (lm <= 2) return launch_split_k<T, false, 2, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
     return launch_split_k<T, false, 4, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);

@@ -315,14 +315,7 @@ struct ScanTile {
                                          F&& fin) const
     {
         if (kind == 0) {
-#pragma unroll
-            for (int u = 0; u < V; ++u) {
-                T o[E];
-                fin(u, o);
-#pragma unroll
-                for (int e = 0; e < E; ++e) o[e] = init + o[e];
-                put<ALIGNED>(y, n, g0, u, o);
-            }
+            emit_inclusive<ALIGNED>(y, n, g0, init, fin);
             return;
         }
         {
@@ -331,7 +324,39 @@ struct ScanTile {
             if (lane == 63) s_wend[w] = o[E - 1];
         }
         __syncthreads();
-        T carry = w == 0 ? pre : s_wend[w - 1];
+        emit_shifted<ALIGNED>(y, n, g0, init, kind, w == 0 ? pre : s_wend[w - 1], lane, fin);
+    }
+
+    // The same when the caller already knows the value before the wave's
+    // first element (`before`): no exchange, no barrier.
+    template <bool ALIGNED, class F>
+    __device__ __forceinline__ void emit_known(T* __restrict__ y, uint64_t n, uint64_t g0, T init,
+                                               int kind, T before, int lane, F&& fin) const
+    {
+        if (kind == 0) emit_inclusive<ALIGNED>(y, n, g0, init, fin);
+        else emit_shifted<ALIGNED>(y, n, g0, init, kind, before, lane, fin);
+    }
+
+    template <bool ALIGNED, class F>
+    __device__ __forceinline__ void emit_inclusive(T* __restrict__ y, uint64_t n, uint64_t g0,
+                                                   T init, F&& fin) const
+    {
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            T o[E];
+            fin(u, o);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = init + o[e];
+            put<ALIGNED>(y, n, g0, u, o);
+        }
+    }
+
+    // Kinds 1 and 2, given `carry`, the value before the wave's first element.
+    template <bool ALIGNED, class F>
+    __device__ __forceinline__ void emit_shifted(T* __restrict__ y, uint64_t n, uint64_t g0,
+                                                 T init, int kind, T carry, int lane,
+                                                 F&& fin) const
+    {
 #pragma unroll
         for (int u = 0; u < V; ++u) {
             T o[E];
