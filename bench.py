@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the oracle parity gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of ops to run (profiling)")
+    ap.add_argument("--contrast", action="store_true",
+                    help="canonical results against torch.sum / torch.cumsum and the left fold")
     ap.add_argument("--configs", action="store_true",
                     help="time every workload config (parity-checked) and print a table")
     return ap.parse_args()
@@ -120,6 +122,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.configs:
         run_configs(torch, canon, synth, dev)
+        return
+    if args.contrast:
+        run_contrast(torch, canon, synth, dev)
         return
 
     only = set(args.only.split(",")) if args.only else None
@@ -414,6 +419,53 @@ def run_configs(torch, canon, synth, dev, reps=20):
     for cfg, op, dt, n, us, gbs, pct, eps, ok in rows:
         print(f"| {cfg} | {op} | {dt} | {n} | {us:.1f} | {gbs:.0f} | {pct:.1f} | {eps:.3g} | "
               f"{'yes' if ok else 'NO'} |")
+
+
+def run_contrast(torch, canon, synth, dev, repeats=10):
+    """The canonical library next to what a ROCm user reaches for first:
+    torch.sum and torch.cumsum (rocPRIM/hipCUB style reductions and scans) on
+    the GPU, and the sequential left fold (std::accumulate, oracle) on the
+    CPU, on the same inputs.  Counts the scan outputs that differ from the
+    canonical ones, checks each side's scan back element against its own
+    reduce, and repeats every GPU call to see whether its bits ever change.
+    Prints one markdown table."""
+    import oracle
+    cases = (("scan_1m", "uniform [0,1)"), ("scan_2e27_f64", "mixed magnitude"))
+    out = []
+
+    def bits(t):
+        a = t.detach().cpu().numpy()
+        return a.view(np.uint64 if a.dtype == np.float64 else np.uint32)
+
+    for name, dist in cases:
+        xn = synth.config_input(name)
+        if xn.size > (1 << 24):
+            xn = xn[:1 << 24]  # the left fold and the comparisons stay short
+        x = torch.from_numpy(xn).to(dev)
+        n = xn.size
+        ts = bits(torch.cumsum(x, 0))
+        tr = bits(torch.sum(x).reshape(1))
+        t_rep = all(np.array_equal(bits(torch.cumsum(x, 0)), ts) and
+                    np.array_equal(bits(torch.sum(x).reshape(1)), tr) for _ in range(repeats))
+        lf = oracle.left_fold_scan(xn).view(np.uint64)
+        for pol, q in (("pairwise", 0), ("block_dyadic", 256), ("iterated_pairwise", 128)):
+            cs = bits(canon.scan(x, pol, q))
+            L = q if pol == "iterated_pairwise" else 1
+            back_ok = pol != "block_dyadic" or n % q == 0
+            cr = bits(canon.reduce(x, L, -0.0).reshape(1)) if back_ok else None
+            c_rep = all(np.array_equal(bits(canon.scan(x, pol, q)), cs) for _ in range(repeats))
+            label = pol if pol == "pairwise" else f"{pol}<{q}>"
+            out.append((f"{name} ({dist}, n={n})", label,
+                        int(np.count_nonzero(ts != cs)), int(np.count_nonzero(lf != cs)),
+                        bool(ts[-1] == tr[0]),
+                        None if cr is None else bool(cs[-1] == cr[0]), t_rep, c_rep))
+            log(f"[contrast] {out[-1]}")
+    print("| input | canonical policy | torch.cumsum elements differing | left-fold prefixes differing"
+          " | torch cumsum[-1] == torch.sum | canonical scan[-1] == reduce | torch repeatable"
+          " | canonical repeatable |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in out:
+        print("| " + " | ".join("n/a" if v is None else str(v) for v in r) + " |")
 
 
 def cpu_baseline(x_np, X_np, have_ip):

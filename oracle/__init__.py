@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, f"oracle_reduce_rows_{sfx}"); f.argtypes = [P, S, S, S, U, ct, P]; f.restype = None
             f = getattr(L, f"oracle_scan_rows_{sfx}"); f.argtypes = [P, S, P, S, S, S, I, U]; f.restype = I
             f = getattr(L, f"oracle_scan_with_init_{sfx}"); f.argtypes = [P, P, S, I, U, I, ct]; f.restype = I
+            f = getattr(L, f"oracle_left_fold_{sfx}"); f.argtypes = [P, S, ct]; f.restype = ct
+            f = getattr(L, f"oracle_left_fold_scan_{sfx}"); f.argtypes = [P, P, S, ct]; f.restype = None
             f = getattr(L, f"oracle_scan_rows_with_init_{sfx}")
             f.argtypes = [P, S, P, S, S, S, I, U, I, ct]; f.restype = I
         _lib = L
@@ -243,3 +245,20 @@ def scan_rows_with_init(X: np.ndarray, policy, param: int = 0, init=-0.0, kind="
     if not ok:
         raise ValueError("bad scan arguments")
     return Y
+
+
+def left_fold(x: np.ndarray, init=-0.0):
+    """((init + x0) + x1) + ... in x's dtype: the sequential fold the canonical
+    expression replaces.  A contrast, not an expression the library computes."""
+    x = _c(x)
+    return x.dtype.type(getattr(lib(), f"oracle_left_fold_{_sfx(x)}")(
+        _ptr(x), x.size, x.dtype.type(init)))
+
+
+def left_fold_scan(x: np.ndarray, init=-0.0) -> np.ndarray:
+    """Every prefix of the left fold (init in front of each)."""
+    x = _c(x)
+    y = np.empty_like(x)
+    getattr(lib(), f"oracle_left_fold_scan_{_sfx(x)}")(_ptr(x), _ptr(y), x.size,
+                                                       x.dtype.type(init))
+    return y

@@ -256,6 +256,27 @@ int FN(oracle_scan_with_init)(const T* x, T* y, size_t n, int policy, uint32_t p
     return 1;
 }
 
+/* ---- left fold (contrast only) --------------------------------------------- */
+/* The sequential fold ((init + x0) + x1) + ... of std::accumulate, which the */
+/* canonical expression replaces (P4016R0 "Summary": deterministic but       */
+/* sequential); every prefix of it for the scan form (std::partial_sum with  */
+/* init in front).  y may equal x.  Used to contrast, never to check the GPU.*/
+T FN(oracle_left_fold)(const T* x, size_t n, T init)
+{
+    T acc = init;
+    for (size_t i = 0; i < n; ++i) acc = acc + x[i];
+    return acc;
+}
+
+void FN(oracle_left_fold_scan)(const T* x, T* y, size_t n, T init)
+{
+    T acc = init;
+    for (size_t i = 0; i < n; ++i) {
+        acc = acc + x[i];
+        y[i] = acc;
+    }
+}
+
 /* ---- batched rows: every row is an independent sequence ----------------- */
 void FN(oracle_reduce_rows)(const T* x, size_t rows, size_t cols, size_t ldx, uint32_t L,
                             T init, T* out)

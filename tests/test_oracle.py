@@ -418,6 +418,38 @@ def test_left_to_right_fold_differs():
     for v in x:
         acc = acc + float(v)
     assert not same_bits(oracle.pw(x), acc)
+    assert same_bits(oracle.left_fold(x, 0.0), acc)
+
+
+# --------------------------------------------------------------------------
+# The left fold kept for the contrast (P4016R0 "Summary": std::accumulate is
+# deterministic but sequential)
+# --------------------------------------------------------------------------
+def test_left_fold_worked_example():
+    """The Futhark post's three terms: the fold is the left grouping."""
+    x = np.array([0.1, 0.2, 0.3])
+    assert same_bits(oracle.left_fold(x), (0.1 + 0.2) + 0.3)
+    assert same_bits(oracle.left_fold_scan(x)[2], (0.1 + 0.2) + 0.3)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_left_fold_exact_and_prefixes(dtype):
+    rng = np.random.Generator(np.random.PCG64(9))
+    xi = rng.integers(-1000, 1000, 500)
+    x = xi.astype(dtype)
+    assert same_bits(oracle.left_fold(x, 7.0), dtype(7 + int(xi.sum())))
+    ys = oracle.left_fold_scan(x, 7.0)
+    assert same_bits(ys, (7 + np.cumsum(xi)).astype(dtype))
+    assert same_bits(oracle.left_fold(np.zeros(0, dtype), 2.5), dtype(2.5))
+    # up to three elements the left fold is the pairwise tree ((ab)c)
+    y = synth.generate(3, "mixed_magnitude", 4, dtype)
+    for n in (1, 2, 3):
+        assert same_bits(oracle.left_fold(y[:n]), oracle.pw(y[:n]))
+    # from four on they part: (((ab)c)d) against ((ab)(cd))
+    z = synth.generate(4096, "mixed_magnitude", 5, dtype)
+    diff = sum(not same_bits(oracle.left_fold_scan(z)[i], oracle.scan(z, "pairwise")[i])
+               for i in range(3, 200))
+    assert diff > 50
 
 
 def test_published_golden_values_decode():
