@@ -46,7 +46,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["device.hpp", "launch.hpp", "reduce.hpp", "reduce.hip", "scan.hpp",
                   "scan_tile.hpp", "scan_kernels.hpp", "scan.hip", "scan_with_init.hip",
                   "scan_wide.hip", "scan_wide_init.hip",
-                  "scan_rows.hip", "scan_ip.hpp", "scan_ip.hip"]
+                  "scan_rows.hip", "scan_ip.hpp", "scan_ip_fast.hpp", "scan_ip.hip",
+                  "scan_ip1.hip"]
 
 
 def kernel_sources_sha256() -> str:

@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libcanon")
 
 SOURCES = [
     "api.cpp", "reduce.hip", "scan.hip", "scan_with_init.hip", "scan_wide.hip",
-    "scan_wide_init.hip", "scan_rows.hip", "scan_ip.hip",
+    "scan_wide_init.hip", "scan_rows.hip", "scan_ip.hip", "scan_ip1.hip",
 ]
 
 # -ffp-contract=off: no FMA contraction; no fast-math; packed FP32 disabled.

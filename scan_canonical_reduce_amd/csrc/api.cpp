@@ -129,16 +129,32 @@ T* ip_nodes(void* ws)
 // iterated_pairwise with L = 1 is the pairwise expression: CR_1 = PW.
 bool is_ip(int policy, uint32_t param) { return policy == CANON_ITERATED_PAIRWISE && param > 1; }
 
+// The register geometry of the iterated_pairwise scan runs in one pass (its
+// items must fit one launch); any other geometry in three kernels.
+bool ip_single(const IpLayout& ip) { return ip.fast_logrv >= 0; }
+bool ip_fits(const IpLayout& ip) { return ip.nseg * ip.tps < (1ull << 31); }
+
+// Workspace of an iterated_pairwise scan: the largest of its possible plans
+// (16-byte aligned or not).
+size_t ip_ws(uint64_t nseg, uint64_t cols, uint32_t L, size_t es)
+{
+    size_t need = 0;
+    for (int al = 0; al < 2; ++al) {
+        const IpLayout ip = make_ip_layout(nseg, cols, L, es, al != 0);
+        size_t b = kWsAlign + round_up(ip.total * es, kWsAlign);
+        if (ip_single(ip)) {
+            const size_t b1 = round_up(make_ip_single_layout(ip).total_words * 8, kWsAlign);
+            if (b1 > b) b = b1;
+        }
+        if (b > need) need = b;
+    }
+    return need;
+}
+
 size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
-    if (is_ip(policy, param))
-    {
-        // the larger of the two layouts (register path or LDS path)
-        const uint64_t a = make_ip_layout(1, n, param, es, true).total;
-        const uint64_t b = make_ip_layout(1, n, param, es, false).total;
-        return kWsAlign + round_up((a > b ? a : b) * es, kWsAlign);
-    }
+    if (is_ip(policy, param)) return ip_ws(1, n, param, es);
     const ScanLayout lay = es == 8 ? scan_layout<double>(n, policy, param)
                                    : scan_layout<float>(n, policy, param);
     return round_up(lay.total_words * 8, kWsAlign);
@@ -148,9 +164,7 @@ size_t scan_rows_ws(uint64_t rows, uint64_t cols, int policy, uint32_t param, si
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8)) return 0;
     if (rows == 0 || cols == 0 || !is_ip(policy, param)) return 0;
-    const uint64_t a = make_ip_layout(rows, cols, param, es, true).total;
-    const uint64_t b = make_ip_layout(rows, cols, param, es, false).total;
-    return kWsAlign + round_up((a > b ? a : b) * es, kWsAlign);
+    return ip_ws(rows, cols, param, es);
 }
 
 // out == null: the plain inclusive scan; else the scan with an initial value.
@@ -172,6 +186,11 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
         const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), aligned16(x) && aligned16(y));
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
             return s;
+        if (ip_single(ip)) {
+            if (!ip_fits(ip)) return CANON_EUNSUPPORTED;
+            return hip_status(launch_scan_ip_single<T>(x, n, y, n, n, static_cast<uint64_t*>(ws),
+                                                       make_ip_single_layout(ip), out, st));
+        }
         return hip_status(launch_scan_ip<T>(x, n, y, n, 1, n, static_cast<uint32_t*>(ws),
                                             ip_nodes<T>(ws), ip, out, st));
     }
@@ -211,6 +230,12 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
         if (canon_status_t s =
                 check_ws(ws, ws_bytes, scan_rows_ws(rows, cols, policy, param, sizeof(T))))
             return s;
+        if (ip_single(ip)) {
+            if (!ip_fits(ip)) return CANON_EUNSUPPORTED;
+            return hip_status(launch_scan_ip_single<T>(x, ldx, y, ldy, cols,
+                                                       static_cast<uint64_t*>(ws),
+                                                       make_ip_single_layout(ip), out, st));
+        }
         return hip_status(launch_scan_ip<T>(x, ldx, y, ldy, rows, cols,
                                             static_cast<uint32_t*>(ws), ip_nodes<T>(ws), ip, out,
                                             st));

@@ -70,6 +70,40 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
     return lay;
 }
 
+// Workspace of the single-pass iterated_pairwise scan (fast geometry, any
+// segment count), in 64-bit words from the workspace start:
+//   word 0: error word (low 32 bits); word 1: ticket counter (low 32 bits);
+//   [woff[k], +nseg * cnt[k] * L): node level k, one published word per lane
+//     (node (k, u) of segment s at woff[k] + (s * cnt[k] + u) * L);
+//   [cbase, ...): 32-bit arrival counters, level k >= 1 at coff[k] (in
+//     32-bit units from cbase): one per node, counting its finished children.
+struct IpSingleLayout {
+    IpLayout g;
+    uint64_t woff[kIpMaxLevels];
+    uint64_t coff[kIpMaxLevels];
+    uint64_t cbase;
+    uint64_t counters;
+    uint64_t total_words;
+};
+
+inline IpSingleLayout make_ip_single_layout(const IpLayout& g)
+{
+    IpSingleLayout s{};
+    s.g = g;
+    uint64_t off = 32;  // 256 bytes of header
+    uint64_t c = 0;
+    for (int k = 0; k < kIpMaxLevels; ++k) {
+        s.woff[k] = off;
+        off += g.nseg * g.cnt[k] * g.L;
+        s.coff[k] = c;
+        if (k >= 1) c += g.nseg * g.cnt[k];
+    }
+    s.cbase = off;
+    s.counters = c;
+    s.total_words = off + (c + 1) / 2;
+    return s;
+}
+
 inline size_t ip_lds_bytes(const IpLayout& lay, size_t elem_size)
 {
     return (size_t)((1ull << lay.r_log) + 1) * 2 * (1ull << lay.lp_log) * elem_size;
@@ -79,6 +113,11 @@ inline size_t ip_lds_bytes(const IpLayout& lay, size_t elem_size)
 // value that *out describes (ScanOut, scan.hpp).
 template <typename T>
 struct ScanOut;
+
+template <typename T>
+hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                                 uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>* out,
+                                 hipStream_t s);
 
 template <typename T>
 hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,

@@ -1,0 +1,182 @@
+// Register geometry and lane trees of the iterated_pairwise scan's fast path
+// (shared by the three-kernel and the single-pass scans).
+#pragma once
+
+#include "device.hpp"
+#include "scan_ip.hpp"
+
+namespace canon {
+
+// ============================================================================
+// Fast path: L = 64 * E * RV with RV = 2^LOGRV in {1, ..., 8} (a row is RV
+// wave-wide 16-byte loads), 16-byte aligned rows.  A tile is 64 / RV rows;
+// each thread holds 16 vectors: wave w owns rows w*RW .. w*RW + RW-1
+// (RW = 16 / RV), vector u = row-in-wave u / RV, row-vector q = u % RV, lanes
+// (q * 64 + lane) * E + e.  The lane tree of a row has three kinds of levels:
+// inside a vector (static), across the 64 lanes (xor butterfly), across the
+// RV vectors of the row (in the thread).
+// ============================================================================
+template <typename T, int LOGRV>
+struct IpFast {
+    static constexpr int E = Elem<T>::E;
+    static constexpr int LOGE = Elem<T>::LOGE;
+    static constexpr int RV = 1 << LOGRV;
+    static constexpr int NV = 16;
+    static constexpr int RW = NV / RV;
+    static constexpr int LOGRW = 4 - LOGRV;
+    static constexpr int R = 4 * RW;  // rows per tile
+    static constexpr int L = 64 * E * RV;
+};
+
+// butterfly partner value of `v` held by lane ^ 2^K
+template <int K, typename T>
+__device__ __forceinline__ T xor_lane(T v)
+{
+    return shfl_xor<(1 << K)>(v);
+}
+
+template <typename T, int LOGRV, bool GUARD>
+__device__ __forceinline__ void ipf_load(const T* __restrict__ xs, uint64_t cols, uint64_t row0,
+                                         int w, int lane, T (&a)[16][Elem<T>::E])
+{
+    using F = IpFast<T, LOGRV>;
+#pragma unroll
+    for (int u = 0; u < F::NV; ++u) {
+        const uint64_t row = row0 + (uint64_t)w * F::RW + u / F::RV;
+        const uint64_t gi = row * F::L + (uint64_t)((u % F::RV) * 64 + lane) * F::E;
+        if (!GUARD || gi + F::E <= cols) {
+            load_vec(xs + gi, a[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < F::E; ++e) a[u][e] = gi + e < cols ? xs[gi + e] : neg_zero<T>();
+        }
+    }
+}
+
+// In-wave pairwise prefix down each lane over the wave's RW rows (Sklansky
+// over rows; the upper half receives the end of the lower half).
+template <typename T, int LOGRV>
+__device__ __forceinline__ void ipf_columns_in_wave(T (&a)[16][Elem<T>::E])
+{
+    using F = IpFast<T, LOGRV>;
+#pragma unroll
+    for (int h = 1; h < F::RW; h *= 2)
+#pragma unroll
+        for (int r = 0; r < F::RW; ++r)
+            if (r & h)
+#pragma unroll
+                for (int q = 0; q < F::RV; ++q)
+#pragma unroll
+                    for (int e = 0; e < F::E; ++e)
+                        a[r * F::RV + q][e] = a[((r & ~(2 * h - 1)) + h - 1) * F::RV + q][e] +
+                                              a[r * F::RV + q][e];
+}
+
+// The sibling values one row contributes to the walks of the lanes of a
+// row (its own, as the A side, or the next one, as the B side), per 16-byte
+// vector q of the row held by this thread:
+//   sv[l][q][s]: the complete subtree of 2^l slots starting at slot s 2^l
+//                (inside the vector, l < log2 E);
+//   o[K][q]:     the partner lane's subtree at lane level K (lane ^ 2^K);
+//   pv[l][q]:    this thread's subtree of vector q at vector level l.
+template <typename T, int LOGRV>
+struct IpRowTree {
+    static constexpr int E = Elem<T>::E, LOGE = Elem<T>::LOGE, RV = 1 << LOGRV;
+    T sv[LOGE][RV][E];
+    T o[6][RV];
+    T pv[LOGRV > 0 ? LOGRV : 1][RV];
+    T root;  // the complete tree over the whole row (the same in every lane)
+
+    // row = vectors rows[v0 .. v0 + RV)
+    template <int NV>
+    __device__ __forceinline__ void build(const T (&rows)[NV][E], int v0, int lane)
+    {
+        T p[RV];
+#pragma unroll
+        for (int q = 0; q < RV; ++q) {
+            T cur[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) cur[e] = rows[v0 + q][e];
+#pragma unroll
+            for (int l = 0; l < LOGE; ++l) {
+#pragma unroll
+                for (int s2 = 0; s2 < (E >> l); ++s2) sv[l][q][s2] = cur[s2];
+#pragma unroll
+                for (int s2 = 0; s2 < (E >> (l + 1)); ++s2) cur[s2] = cur[2 * s2] + cur[2 * s2 + 1];
+            }
+            p[q] = cur[0];
+        }
+#define CANON_IP_TREE_LANE(K)                                                           \
+    {                                                                                   \
+        const bool right = (lane >> (K)) & 1;                                           \
+        _Pragma("unroll") for (int q = 0; q < RV; ++q)                                  \
+        {                                                                               \
+            o[K][q] = xor_lane<K>(p[q]);                                                \
+            p[q] = right ? (o[K][q] + p[q]) : (p[q] + o[K][q]);                         \
+        }                                                                               \
+    }
+        CANON_IP_TREE_LANE(0)
+        CANON_IP_TREE_LANE(1)
+        CANON_IP_TREE_LANE(2)
+        CANON_IP_TREE_LANE(3)
+        CANON_IP_TREE_LANE(4)
+        CANON_IP_TREE_LANE(5)
+#undef CANON_IP_TREE_LANE
+#pragma unroll
+        for (int l = 0; l < LOGRV; ++l) {
+            const int h = 1 << l;
+#pragma unroll
+            for (int q = 0; q < RV; ++q) pv[l][q] = p[q];
+#pragma unroll
+            for (int i = 0; i < RV / (2 * h); ++i) p[2 * i * h] = p[2 * i * h] + p[(2 * i + 1) * h];
+        }
+        root = p[0];
+    }
+};
+
+// val[q][e]: the walk of every lane of row vectors rows[v0 .. v0 + RV) from
+// its leaf to the root: at each level the sibling subtree lies wholly left
+// (A row, added on the left) or wholly right (B row, added on the right).
+template <typename T, int LOGRV, int NV>
+__device__ __forceinline__ void ip_walk(const T (&rows)[NV][Elem<T>::E], int v0,
+                                        const IpRowTree<T, LOGRV>& A,
+                                        const IpRowTree<T, LOGRV>& B, int lane,
+                                        T (&val)[1 << LOGRV][Elem<T>::E])
+{
+    constexpr int E = Elem<T>::E, LOGE = Elem<T>::LOGE, RV = 1 << LOGRV;
+#pragma unroll
+    for (int q = 0; q < RV; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e) val[q][e] = rows[v0 + q][e];
+#pragma unroll
+    for (int l = 0; l < LOGE; ++l)
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int node = e >> l, sib = node ^ 1;
+                val[q][e] = (node & 1) ? A.sv[l][q][sib] + val[q][e] : val[q][e] + B.sv[l][q][sib];
+            }
+#pragma unroll
+    for (int K = 0; K < 6; ++K) {
+        const bool right = (lane >> K) & 1;
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                val[q][e] = right ? (A.o[K][q] + val[q][e]) : (val[q][e] + B.o[K][q]);
+    }
+#pragma unroll
+    for (int l = 0; l < LOGRV; ++l) {
+        const int h = 1 << l;
+#pragma unroll
+        for (int q = 0; q < RV; ++q) {
+            const int node = q >> l, sib = node ^ 1;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                val[q][e] = (node & 1) ? A.pv[l][sib * h] + val[q][e] : val[q][e] + B.pv[l][sib * h];
+        }
+    }
+}
+
+}  // namespace canon
