@@ -593,7 +593,9 @@ struct WideTile {
     static constexpr int VPB = 1 << VLOG;             // vectors per block
     static constexpr int NBW_LOG = LOGV - VLOG;       // log2 blocks per wave
     static_assert(VLOG >= 0 && VLOG <= LOGV, "blocks of whole vectors inside one wave");
-    static constexpr int kMinWavesPerEu = 1;
+    // f64: two tiles held in at most 168 VGPRs (3 waves per SIMD), a few
+    // values spilled; measured 2% faster at B = 256 (f32: no change)
+    static constexpr int kMinWavesPerEu = sizeof(T) == 8 ? 3 : 1;
     struct State {
         ST st;
         T p;     // lane j < 2^NBW_LOG: pairwise value of the blocks up to block j of this wave
@@ -806,12 +808,16 @@ hipError_t launch_wide_impl(const T* x, T* y, uint64_t n, int b_log, bool aligne
 {
     constexpr int LOGV = scan_log_v<T>();
     const int vlog = b_log - (Elem<T>::LOGE + 6);
-#define CANON_WIDE_CASE(VL)                                                                 \
-    case VL:                                                                                \
-        if (aligned)                                                                        \
-            return launch_k<WideTile<T, true, LOGV, VL, OUTX>>(x, y, n, b_log, ws, lay, 0, out, \
-                                                               s);                          \
-        return launch_k<WideTile<T, false, LOGV, VL, OUTX>>(x, y, n, b_log, ws, lay, 0, out, s);
+#define CANON_WIDE_CASE(VL)                                                                  \
+    case VL:                                                                                 \
+        if constexpr (VL <= LOGV) {                                                          \
+            if (aligned)                                                                     \
+                return launch_k<WideTile<T, true, LOGV, VL, OUTX>>(x, y, n, b_log, ws, lay, 0, \
+                                                                   out, s);                  \
+            return launch_k<WideTile<T, false, LOGV, VL, OUTX>>(x, y, n, b_log, ws, lay, 0,    \
+                                                                out, s);                     \
+        }                                                                                    \
+        return hipErrorInvalidValue;
     switch (vlog) {
         CANON_WIDE_CASE(0)
         CANON_WIDE_CASE(1)
