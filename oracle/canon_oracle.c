@@ -29,20 +29,88 @@
  * part; init on the left; block_dyadic's prefix split into whole blocks and
  * the open block.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
+/* The operators (the expression is defined for any binary operator:        */
+/* P4016R0 "Summary").  min and max are IEEE 754-2019 minimum / maximum: a   */
+/* NaN operand gives NaN, and -0.0 is below +0.0; both are then associative  */
+/* and commutative, so every parenthesisation gives the same value.          */
+static double min_f64(double a, double b)
+{
+    if (isnan(a) || isnan(b)) return a + b;
+    if (a < b) return a;
+    if (b < a) return b;
+    return signbit(a) ? a : b;
+}
+static double max_f64(double a, double b)
+{
+    if (isnan(a) || isnan(b)) return a + b;
+    if (a > b) return a;
+    if (b > a) return b;
+    return signbit(a) ? b : a;
+}
+static float min_f32(float a, float b)
+{
+    if (isnan(a) || isnan(b)) return a + b;
+    if (a < b) return a;
+    if (b < a) return b;
+    return signbit(a) ? a : b;
+}
+static float max_f32(float a, float b)
+{
+    if (isnan(a) || isnan(b)) return a + b;
+    if (a > b) return a;
+    if (b > a) return b;
+    return signbit(a) ? b : a;
+}
+
 #define T double
 #define SFX f64
+#define OP(a, b) ((a) + (b))
 #include "canon_oracle_body.h"
-#undef T
 #undef SFX
+#undef OP
+#define SFX f64_mul
+#define OP(a, b) ((a) * (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+#define SFX f64_min
+#define OP(a, b) min_f64((a), (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+#define SFX f64_max
+#define OP(a, b) max_f64((a), (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+#undef T
 
 #define T float
 #define SFX f32
+#define OP(a, b) ((a) + (b))
 #include "canon_oracle_body.h"
-#undef T
 #undef SFX
+#undef OP
+#define SFX f32_mul
+#define OP(a, b) ((a) * (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+#define SFX f32_min
+#define OP(a, b) min_f32((a), (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+#define SFX f32_max
+#define OP(a, b) max_f32((a), (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+#undef T
 
 int oracle_abi_version(void) { return 1; }

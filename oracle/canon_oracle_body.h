@@ -1,18 +1,25 @@
 /*
- * Body of the CPU oracle, instantiated once per floating-point type by
- * canon_oracle.c (T = double / float, SFX = f64 / f32).
+ * Body of the CPU oracle, instantiated once per floating-point type and
+ * operator by canon_oracle.c (T = double / float; SFX = f64 / f32 for +,
+ * f64_mul, f64_min, ... for the others; OP(a, b) the operator).
  *
  * TEST INFRASTRUCTURE ONLY — see the header of canon_oracle.c.
  *
- * Every "+" below is one IEEE-754 addition in type T, rounded to nearest even;
- * the file is built with -ffp-contract=off and without fast-math, so the
- * compiler may neither fuse nor reassociate.  The left operand of every "+"
- * always covers the lower input indices.
+ * Every OP below is one IEEE-754 operation in type T, rounded to nearest
+ * even; the file is built with -ffp-contract=off and without fast-math, so
+ * the compiler may neither fuse nor reassociate.  The left operand of every
+ * OP always covers the lower input indices.  (The comments write OP as "+".)
  */
 
 #define CAT2(a, b) a##b
 #define CAT(a, b) CAT2(a, b)
 #define FN(name) CAT(name, CAT(_, SFX))
+
+/* The operator itself, one application (for evaluations from scratch).    */
+T FN(oracle_apply)(T a, T b)
+{
+    return OP(a, b);
+}
 
 /* ------------------------------------------------------------------------ */
 /* PW(s): the iterative pairwise tree (canonical-reduce README, P4016R0,    */
@@ -30,7 +37,7 @@ static int FN(pw_strided)(const T* s, size_t n, size_t stride, T* out)
     size_t m = n;
     while (m > 1) {
         size_t k = 0;
-        for (size_t i = 0; i + 1 < m; i += 2) buf[k++] = buf[i] + buf[i + 1];
+        for (size_t i = 0; i + 1 < m; i += 2) buf[k++] = OP(buf[i], buf[i + 1]);
         if (m & 1) buf[k++] = buf[m - 1];
         m = k;
     }
@@ -80,7 +87,7 @@ T FN(oracle_reduce)(const T* x, size_t n, uint32_t L, T init)
 {
     T r;
     if (!FN(oracle_cr)(x, n, L, &r)) return init;
-    return init + r;
+    return OP(init, r);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -119,7 +126,7 @@ int FN(oracle_scan_prefix)(const T* x, size_t i, int policy, uint32_t param, T* 
             free(blocks);
         }
         if (t > 0) hasT = FN(pw_strided)(x + q * B, t, 1, &Tl);
-        if (hasH && hasT) *out = H + Tl;
+        if (hasH && hasT) *out = OP(H, Tl);
         else if (hasH) *out = H;
         else *out = Tl;
         return 1;
@@ -147,7 +154,7 @@ static void FN(st_push)(FN(stack_t)* s, T v)
     s->lvl[s->top] = 0;
     s->top++;
     while (s->top >= 2 && s->lvl[s->top - 1] == s->lvl[s->top - 2]) {
-        s->val[s->top - 2] = s->val[s->top - 2] + s->val[s->top - 1];
+        s->val[s->top - 2] = OP(s->val[s->top - 2], s->val[s->top - 1]);
         s->lvl[s->top - 2] += 1;
         s->top--;
     }
@@ -157,7 +164,7 @@ static int FN(st_collapse)(const FN(stack_t)* s, T* out)
 {
     if (s->top == 0) return 0;
     T acc = s->val[s->top - 1];
-    for (int k = s->top - 2; k >= 0; --k) acc = s->val[k] + acc;
+    for (int k = s->top - 2; k >= 0; --k) acc = OP(s->val[k], acc);
     *out = acc;
     return 1;
 }
@@ -194,7 +201,7 @@ int FN(oracle_scan)(const T* x, T* y, size_t n, int policy, uint32_t param)
             T H = 0, Tl = 0;
             int hasH = FN(st_collapse)(&blocks, &H);
             int hasT = FN(st_collapse)(&tail, &Tl);
-            if (hasH && hasT) y[i] = H + Tl;
+            if (hasH && hasT) y[i] = OP(H, Tl);
             else if (hasH) y[i] = H;
             else y[i] = Tl;
         }
@@ -250,7 +257,7 @@ int FN(oracle_scan_with_init)(const T* x, T* y, size_t n, int policy, uint32_t p
     const size_t nout = kind == 2 ? n + 1 : n;
     for (size_t k = 0; k < nout; ++k) {
         const size_t m = kind == 0 ? k + 1 : k;
-        y[k] = m == 0 ? init : init + s[m - 1];
+        y[k] = m == 0 ? init : OP(init, s[m - 1]);
     }
     free(s);
     return 1;
@@ -264,7 +271,7 @@ int FN(oracle_scan_with_init)(const T* x, T* y, size_t n, int policy, uint32_t p
 T FN(oracle_left_fold)(const T* x, size_t n, T init)
 {
     T acc = init;
-    for (size_t i = 0; i < n; ++i) acc = acc + x[i];
+    for (size_t i = 0; i < n; ++i) acc = OP(acc, x[i]);
     return acc;
 }
 
@@ -272,7 +279,7 @@ void FN(oracle_left_fold_scan)(const T* x, T* y, size_t n, T init)
 {
     T acc = init;
     for (size_t i = 0; i < n; ++i) {
-        acc = acc + x[i];
+        acc = OP(acc, x[i]);
         y[i] = acc;
     }
 }

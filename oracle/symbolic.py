@@ -17,8 +17,9 @@ the other:
   Points", written out on trees.
 
 ``to_str`` prints a tree with letters a, b, c, ... for indices 0, 1, 2, ...;
-``evaluate`` computes its value with one IEEE addition per node in the dtype
-of the given values.
+``evaluate`` computes its value with one IEEE operation per node (addition by
+default; multiplication, minimum or maximum on request) in the dtype of the
+given values.
 """
 from __future__ import annotations
 
@@ -109,16 +110,43 @@ def to_str(tree) -> str:
     return "(" + to_str(tree[0]) + to_str(tree[1]) + ")"
 
 
-def evaluate(tree, values, init=None):
-    """Value of a tree: one addition in values' dtype per internal node."""
+def _minimum(a, b):
+    """IEEE 754-2019 minimum: NaN if either is NaN, -0.0 below +0.0."""
+    if np.isnan(a) or np.isnan(b):
+        return a + b
+    if a < b or (a == b and np.signbit(a)):
+        return a
+    return b
+
+
+def _maximum(a, b):
+    """IEEE 754-2019 maximum: NaN if either is NaN, +0.0 above -0.0."""
+    if np.isnan(a) or np.isnan(b):
+        return a + b
+    if a > b or (a == b and not np.signbit(a)):
+        return a
+    return b
+
+
+def evaluate(tree, values, init=None, op="add"):
+    """Value of a tree: one application of op ("add", "mul", "min", "max")
+    in values' dtype per internal node."""
     t = values.dtype.type
     if isinstance(tree, str):
         return t(init)
     if isinstance(tree, int):
         return t(values[tree])
-    a = evaluate(tree[0], values, init)
-    b = evaluate(tree[1], values, init)
-    return t(a + b)
+    a = evaluate(tree[0], values, init, op)
+    b = evaluate(tree[1], values, init, op)
+    if op == "add":
+        return t(a + b)
+    if op == "mul":
+        return t(a * b)
+    if op == "min":
+        return t(_minimum(a, b))
+    if op == "max":
+        return t(_maximum(a, b))
+    raise ValueError(op)
 
 
 def leaves(tree):
