@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CANON_ABI_VERSION 2 /* 2: scans with an initial value */
+#define CANON_ABI_VERSION 3 /* 2: scans with an initial value; 3: operators */
 
 /* Largest lane count L for reduce and iterated_pairwise, and largest block
  * size B for block_dyadic.  Larger values return CANON_EUNSUPPORTED. */
@@ -84,6 +84,18 @@ typedef enum {
     CANON_ITERATED_PAIRWISE = 1, /* param = L, 1 <= L <= CANON_MAX_IP_L */
     CANON_BLOCK_DYADIC = 2       /* param = B, power of two, 1 <= B <= CANON_MAX_B */
 } canon_policy_t;
+
+/* The binary operator the expression is evaluated with (P4016R0 "Summary":
+ * the canonical expression is defined for any operator).  Absent values
+ * (lanes without an element, padding) take the operator's exact identity:
+ * -0.0, 1.0, +inf, -inf.  MIN and MAX are IEEE 754-2019 minimum and maximum:
+ * NaN if either operand is NaN, -0.0 below +0.0. */
+typedef enum {
+    CANON_OP_ADD = 0,
+    CANON_OP_MUL = 1,
+    CANON_OP_MIN = 2,
+    CANON_OP_MAX = 3
+} canon_op_t;
 
 /* Which prefix each output of a scan with an initial value observes. */
 typedef enum {
@@ -188,6 +200,43 @@ canon_status_t canon_scan_rows_with_init_f32(const float* x, size_t ldx, float* 
                                             size_t rows, size_t cols, int policy, uint32_t param,
                                             int kind, float init, void* ws, size_t ws_bytes,
                                             void* stream);
+
+/* ------------------------------------------------------------- operators */
+/* The same expressions with `op` (a canon_op_t; anything else returns
+ * CANON_EINVAL) in place of every addition, op(init, R) in place of
+ * init + R, and the operator's identity as the absent value.  Arguments,
+ * layouts, workspaces (the *_workspace_bytes functions above, which do not
+ * depend on the operator) and errors are those of the functions above;
+ * canon_scan_op_* and canon_scan_rows_op_* take kind and init as the scans
+ * with an initial value do (kind CANON_SCAN_INCLUSIVE with init = the
+ * identity is the plain scan).  CANON_OP_ADD gives exactly the results of
+ * the functions above.  The other operators run the general streaming
+ * reduce kernel for every L and alignment, and the scan kernels with an
+ * output stage. */
+canon_status_t canon_reduce_op_f64(const double* x, size_t n, uint32_t L, int op, double init,
+                                   double* out, void* ws, size_t ws_bytes, void* stream);
+canon_status_t canon_reduce_op_f32(const float* x, size_t n, uint32_t L, int op, float init,
+                                   float* out, void* ws, size_t ws_bytes, void* stream);
+canon_status_t canon_reduce_rows_op_f64(const double* x, size_t rows, size_t cols, size_t ldx,
+                                        uint32_t L, int op, double init, double* out, void* ws,
+                                        size_t ws_bytes, void* stream);
+canon_status_t canon_reduce_rows_op_f32(const float* x, size_t rows, size_t cols, size_t ldx,
+                                        uint32_t L, int op, float init, float* out, void* ws,
+                                        size_t ws_bytes, void* stream);
+canon_status_t canon_scan_op_f64(const double* x, double* y, size_t n, int policy, uint32_t param,
+                                 int op, int kind, double init, void* ws, size_t ws_bytes,
+                                 void* stream);
+canon_status_t canon_scan_op_f32(const float* x, float* y, size_t n, int policy, uint32_t param,
+                                 int op, int kind, float init, void* ws, size_t ws_bytes,
+                                 void* stream);
+canon_status_t canon_scan_rows_op_f64(const double* x, size_t ldx, double* y, size_t ldy,
+                                      size_t rows, size_t cols, int policy, uint32_t param,
+                                      int op, int kind, double init, void* ws, size_t ws_bytes,
+                                      void* stream);
+canon_status_t canon_scan_rows_op_f32(const float* x, size_t ldx, float* y, size_t ldy,
+                                      size_t rows, size_t cols, int policy, uint32_t param,
+                                      int op, int kind, float init, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /* -------------------------------------------------------------- checking */
 /* Every scan workspace begins with a 32-bit error word.  The single-pass

@@ -18,6 +18,10 @@ same names without the ``canon_`` prefix:
                                           "exclusive" or "include_initial"
                                           (len(x) + 1 outputs)
     scan_rows_with_init(X, policy, param, kind, init)
+    reduce_op(x, L, op, init), reduce_rows_op(X, L, op, init),
+    scan_op(x, policy, param, op, kind, init), scan_rows_op(...)
+                                       -> the same with op in "add", "mul",
+                                          "min", "max" (IEEE minimum/maximum)
 
 ``policy`` is "pairwise", "iterated_pairwise" (param = L) or "block_dyadic"
 (param = B, a power of two).
@@ -34,6 +38,9 @@ LIB_PATH = os.path.join(_HERE, "libcanon.so")
 
 POLICIES = {"pairwise": 0, "iterated_pairwise": 1, "block_dyadic": 2}
 SCAN_KINDS = {"inclusive": 0, "exclusive": 1, "include_initial": 2}
+OPS = {"add": 0, "mul": 1, "min": 2, "max": 3}
+# the absent value of each operator (its identity)
+IDENTITY = {"add": -0.0, "mul": 1.0, "min": float("inf"), "max": float("-inf")}
 STATUS = {0: "CANON_OK", 1: "CANON_EINVAL", 2: "CANON_EUNSUPPORTED", 3: "CANON_EWORKSPACE",
           4: "CANON_EHIP"}
 
@@ -45,6 +52,9 @@ EXPORTS = [
     "canon_scan_rows_workspace_bytes", "canon_scan_rows_f64", "canon_scan_rows_f32",
     "canon_scan_with_init_f64", "canon_scan_with_init_f32",
     "canon_scan_rows_with_init_f64", "canon_scan_rows_with_init_f32",
+    "canon_reduce_op_f64", "canon_reduce_op_f32", "canon_reduce_rows_op_f64",
+    "canon_reduce_rows_op_f32", "canon_scan_op_f64", "canon_scan_op_f32",
+    "canon_scan_rows_op_f64", "canon_scan_rows_op_f32",
     "canon_workspace_error",
 ]
 
@@ -90,12 +100,20 @@ def lib() -> ctypes.CDLL:
     L.canon_scan_with_init_f32.argtypes = [P, P, S, I, U, I, F, P, S, P]
     L.canon_scan_rows_with_init_f64.argtypes = [P, S, P, S, S, S, I, U, I, D, P, S, P]
     L.canon_scan_rows_with_init_f32.argtypes = [P, S, P, S, S, S, I, U, I, F, P, S, P]
+    L.canon_reduce_op_f64.argtypes = [P, S, U, I, D, P, P, S, P]
+    L.canon_reduce_op_f32.argtypes = [P, S, U, I, F, P, P, S, P]
+    L.canon_reduce_rows_op_f64.argtypes = [P, S, S, S, U, I, D, P, P, S, P]
+    L.canon_reduce_rows_op_f32.argtypes = [P, S, S, S, U, I, F, P, P, S, P]
+    L.canon_scan_op_f64.argtypes = [P, P, S, I, U, I, I, D, P, S, P]
+    L.canon_scan_op_f32.argtypes = [P, P, S, I, U, I, I, F, P, S, P]
+    L.canon_scan_rows_op_f64.argtypes = [P, S, P, S, S, S, I, U, I, I, D, P, S, P]
+    L.canon_scan_rows_op_f32.argtypes = [P, S, P, S, S, S, I, U, I, I, F, P, S, P]
     L.canon_workspace_error.argtypes = [P, ctypes.POINTER(U), P]
     for name in EXPORTS:
         if name not in ("canon_abi_version", "canon_status_str", "canon_last_hip_error") and \
                 not name.endswith("workspace_bytes"):
             getattr(L, name).restype = I
-    if L.canon_abi_version() != 2:
+    if L.canon_abi_version() != 3:
         raise CanonError("libcanon ABI version mismatch")
     _lib = L
     return L
@@ -294,6 +312,101 @@ def scan_rows_with_init(X: torch.Tensor, policy="pairwise", param: int = 0, kind
         _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, k, float(init), _ptr(w),
         nb if w is None else w.numel(), _stream())
     _check(st, "scan_rows_with_init")
+    return out
+
+
+def _op(op) -> int:
+    if isinstance(op, str):
+        return OPS[op]
+    return int(op)
+
+
+def _op_init(op, init):
+    name = op if isinstance(op, str) else {v: k for k, v in OPS.items()}[int(op)]
+    return IDENTITY[name] if init is None else init
+
+
+def reduce_op(x: torch.Tensor, L: int, op="add", init=None, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None) -> torch.Tensor:
+    """op(init, expression of x) with the operator op; init defaults to the
+    operator's identity."""
+    _need_gpu(x)
+    if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
+        raise ValueError("reduce_op takes a contiguous 1-d tensor")
+    sfx = _sfx(x)
+    if out is None:
+        out = torch.empty((), dtype=x.dtype, device=x.device)
+    nb = lib().canon_reduce_workspace_bytes(x.numel(), L, x.element_size())
+    w = _ws(nb, x.device, ws)
+    st = getattr(lib(), f"canon_reduce_op_{sfx}")(
+        _ptr(x), x.numel(), L, _op(op), float(_op_init(op, init)), out.data_ptr(), _ptr(w),
+        nb if w is None else w.numel(), _stream())
+    _check(st, "reduce_op")
+    return out
+
+
+def reduce_rows_op(X: torch.Tensor, L: int, op="add", init=None,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """reduce_op of every row of a 2-d tensor."""
+    _need_gpu(X)
+    sfx = _sfx(X)
+    rows, cols, ld = _rows_view(X)
+    if out is None:
+        out = torch.empty(rows, dtype=X.dtype, device=X.device)
+    st = getattr(lib(), f"canon_reduce_rows_op_{sfx}")(
+        _ptr(X), rows, cols, ld, L, _op(op), float(_op_init(op, init)), out.data_ptr(), None, 0,
+        _stream())
+    _check(st, "reduce_rows_op")
+    return out
+
+
+def scan_op(x: torch.Tensor, policy="pairwise", param: int = 0, op="add", kind="inclusive",
+            init=None, out: torch.Tensor | None = None,
+            ws: torch.Tensor | None = None) -> torch.Tensor:
+    """scan_with_init with the operator op; init defaults to the operator's
+    identity (with kind "inclusive": the plain scan)."""
+    _need_gpu(x)
+    if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
+        raise ValueError("scan_op takes a contiguous 1-d tensor")
+    sfx = _sfx(x)
+    k = _kind(kind)
+    m = x.numel() + (1 if k == 2 else 0)
+    if out is None:
+        out = torch.empty(m, dtype=x.dtype, device=x.device)
+    if out.dim() != 1 or out.numel() < m or (m > 0 and out.stride(0) != 1) or out.dtype != x.dtype:
+        raise ValueError(f"scan_op: out must be a contiguous {x.dtype} tensor of {m}")
+    p = _policy(policy)
+    nb = lib().canon_scan_workspace_bytes(x.numel(), p, param, x.element_size())
+    w = _ws(nb, x.device, ws)
+    st = getattr(lib(), f"canon_scan_op_{sfx}")(
+        _ptr(x), out.data_ptr(), x.numel(), p, param, _op(op), k, float(_op_init(op, init)),
+        _ptr(w), nb if w is None else w.numel(), _stream())
+    _check(st, "scan_op")
+    return out
+
+
+def scan_rows_op(X: torch.Tensor, policy="pairwise", param: int = 0, op="add", kind="inclusive",
+                 init=None, out: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None) -> torch.Tensor:
+    """scan_op of every row of a 2-d tensor (one more column for
+    include_initial)."""
+    _need_gpu(X)
+    sfx = _sfx(X)
+    rows, cols, ldx = _rows_view(X)
+    k = _kind(kind)
+    ycols = cols + (1 if k == 2 else 0)
+    if out is None:
+        out = torch.empty((rows, ycols), dtype=X.dtype, device=X.device)
+    if out.dim() != 2 or out.shape[0] != rows or out.shape[1] < ycols or out.dtype != X.dtype:
+        raise ValueError(f"scan_rows_op: out must be {X.dtype} of shape ({rows}, >= {ycols})")
+    _, _, ldy = _rows_view(out)
+    p = _policy(policy)
+    nb = lib().canon_scan_rows_workspace_bytes(rows, cols, p, param, X.element_size())
+    w = _ws(nb, X.device, ws)
+    st = getattr(lib(), f"canon_scan_rows_op_{sfx}")(
+        _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, _op(op), k,
+        float(_op_init(op, init)), _ptr(w), nb if w is None else w.numel(), _stream())
+    _check(st, "scan_rows_op")
     return out
 
 

@@ -8,7 +8,10 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/canon.h"
+#include "device.hpp"
 #include "reduce.hpp"
 #include "scan.hpp"
 #include "scan_ip.hpp"
@@ -16,6 +19,20 @@
 using namespace canon;
 
 namespace {
+
+// V is the kernels' value type: double / float for +, or OpVal<B, Op> for
+// another operator (whose calls reach only the general reduce kernel and the
+// scan kernels with an output stage).
+template <typename V>
+constexpr bool is_op_v = !std::is_same<V, typename Elem<V>::base_t>::value;
+
+// Minimum and maximum are associative and commutative with the semantics of
+// device.hpp (NaN payloads aside), so every policy's expression has the same
+// value: their scans run the pairwise kernels whatever the policy.
+template <typename V>
+constexpr bool is_order_free_v =
+    std::is_same<V, OpVal<typename Elem<V>::base_t, OpMin>>::value ||
+    std::is_same<V, OpVal<typename Elem<V>::base_t, OpMax>>::value;
 
 thread_local int g_last_hip_error = 0;
 
@@ -69,12 +86,13 @@ canon_status_t reduce_impl(const T* x, size_t n, uint32_t L, T init, T* out, voi
 {
     if (out == nullptr || L == 0 || (n > 0 && x == nullptr)) return CANON_EINVAL;
     if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
-    const ReducePlan pl = plan_reduce(n, L, sizeof(T), aligned16(x), kReduceTargetWG);
+    const ReducePlan pl =
+        plan_reduce(n, L, sizeof(T), !is_op_v<T> && aligned16(x), kReduceTargetWG);
     // the documented size (covers either plan), so that a caller who sizes by
     // canon_reduce_workspace_bytes is never rejected and never overrun
     if (canon_status_t s = check_ws(ws, ws_bytes, reduce_ws(n, L, sizeof(T)))) return s;
-    return hip_status(launch_reduce<T>(x, n, L, init, out, static_cast<T*>(ws), pl,
-                                       static_cast<hipStream_t>(stream)));
+    return hip_status(launch_reduce<T, !is_op_v<T>>(x, n, L, init, out, static_cast<T*>(ws), pl,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 template <typename T>
@@ -154,7 +172,15 @@ size_t ip_ws(uint64_t nseg, uint64_t cols, uint32_t L, size_t es)
 size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
-    if (is_ip(policy, param)) return ip_ws(1, n, param, es);
+    if (is_ip(policy, param)) {
+        // also enough for the pairwise layout (the order-free operators run
+        // the pairwise scan whatever the policy)
+        const size_t a = ip_ws(1, n, param, es);
+        const ScanLayout p = es == 8 ? scan_layout<double>(n, CANON_PAIRWISE, 0)
+                                     : scan_layout<float>(n, CANON_PAIRWISE, 0);
+        const size_t b = round_up(p.total_words * 8, kWsAlign);
+        return a > b ? a : b;
+    }
     const ScanLayout lay = es == 8 ? scan_layout<double>(n, policy, param)
                                    : scan_layout<float>(n, policy, param);
     return round_up(lay.total_words * 8, kWsAlign);
@@ -182,17 +208,25 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
         if (y == nullptr) return CANON_EINVAL;
         return hip_status(launch_put_column<T>(y, 1, 1, out->init, st));
     }
-    if (is_ip(policy, param)) {
+    if constexpr (is_order_free_v<T>) {
+        const ScanLayout lay = scan_layout<T>(n, CANON_PAIRWISE, 0);
+        if (lay.ntiles > 0xFFFFFFFFull) return CANON_EUNSUPPORTED;
+        if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
+            return s;
+        return hip_status(launch_scan_pw_with_init<T>(x, y, n, aligned16(x) && aligned16(y),
+                                                      static_cast<uint64_t*>(ws), lay, *out, st));
+    } else if (is_ip(policy, param)) {
         const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), aligned16(x) && aligned16(y));
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
             return s;
         if (ip_single(ip)) {
             if (!ip_fits(ip)) return CANON_EUNSUPPORTED;
-            return hip_status(launch_scan_ip_single<T>(x, n, y, n, n, static_cast<uint64_t*>(ws),
-                                                       make_ip_single_layout(ip), out, st));
+            return hip_status(launch_scan_ip_single<T, !is_op_v<T>>(
+                x, n, y, n, n, static_cast<uint64_t*>(ws), make_ip_single_layout(ip), out, st));
         }
-        return hip_status(launch_scan_ip<T>(x, n, y, n, 1, n, static_cast<uint32_t*>(ws),
-                                            ip_nodes<T>(ws), ip, out, st));
+        return hip_status(launch_scan_ip<T, !is_op_v<T>>(x, n, y, n, 1, n,
+                                                         static_cast<uint32_t*>(ws),
+                                                         ip_nodes<T>(ws), ip, out, st));
     }
     const ScanLayout lay = scan_layout<T>(n, policy, param);
     if (lay.ntiles > 0xFFFFFFFFull) return CANON_EUNSUPPORTED;
@@ -204,8 +238,10 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
     if (out)
         return hip_status(launch_scan_with_init<T>(x, y, n, pairwise, b_log, al,
                                                    static_cast<uint64_t*>(ws), lay, *out, st));
-    return hip_status(
-        launch_scan<T>(x, y, n, pairwise, b_log, al, static_cast<uint64_t*>(ws), lay, st));
+    if constexpr (!is_op_v<T>)
+        return hip_status(
+            launch_scan<T>(x, y, n, pairwise, b_log, al, static_cast<uint64_t*>(ws), lay, st));
+    return CANON_EINVAL;
 }
 
 template <typename T>
@@ -223,7 +259,12 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
     if (rows == 0 || ycols == 0) return CANON_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (cols == 0) return hip_status(launch_put_column<T>(y, ldy, rows, out->init, st));
-    if (is_ip(policy, param)) {
+    if constexpr (is_order_free_v<T>) {
+        const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
+                        (ldy * sizeof(T)) % 16 == 0;
+        return hip_status(launch_scan_rows<T, false, true>(x, ldx, y, ldy, rows, cols, true, 0, al,
+                                                           out, st));
+    } else if (is_ip(policy, param)) {
         const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                         (ldy * sizeof(T)) % 16 == 0;
         const IpLayout ip = make_ip_layout(rows, cols, param, sizeof(T), al);
@@ -232,11 +273,11 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
             return s;
         if (ip_single(ip)) {
             if (!ip_fits(ip)) return CANON_EUNSUPPORTED;
-            return hip_status(launch_scan_ip_single<T>(x, ldx, y, ldy, cols,
-                                                       static_cast<uint64_t*>(ws),
-                                                       make_ip_single_layout(ip), out, st));
+            return hip_status(launch_scan_ip_single<T, !is_op_v<T>>(
+                x, ldx, y, ldy, cols, static_cast<uint64_t*>(ws), make_ip_single_layout(ip), out,
+                st));
         }
-        return hip_status(launch_scan_ip<T>(x, ldx, y, ldy, rows, cols,
+        return hip_status(launch_scan_ip<T, !is_op_v<T>>(x, ldx, y, ldy, rows, cols,
                                             static_cast<uint32_t*>(ws), ip_nodes<T>(ws), ip, out,
                                             st));
     }
@@ -244,8 +285,75 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
     const int b_log = pairwise ? 0 : log2_exact(param);
     const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                     (ldy * sizeof(T)) % 16 == 0;
-    return hip_status(
-        launch_scan_rows<T>(x, ldx, y, ldy, rows, cols, pairwise, b_log, al, out, st));
+    return hip_status(launch_scan_rows<T, !is_op_v<T>>(x, ldx, y, ldy, rows, cols, pairwise, b_log,
+                                                       al, out, st));
+}
+
+// Calls f with a value of type Tag<V>, V the kernels' value type for the
+// operator `op` over base type B (CANON_EINVAL for an unknown operator).
+template <typename V>
+struct Tag {
+    using type = V;
+};
+
+template <typename B, class F>
+canon_status_t with_op(int op, F&& f)
+{
+    switch (op) {
+        case CANON_OP_ADD: return f(Tag<B>{});
+        case CANON_OP_MUL: return f(Tag<OpVal<B, OpMul>>{});
+        case CANON_OP_MIN: return f(Tag<OpVal<B, OpMin>>{});
+        case CANON_OP_MAX: return f(Tag<OpVal<B, OpMax>>{});
+        default: return CANON_EINVAL;
+    }
+}
+
+template <typename B>
+canon_status_t reduce_op(const B* x, size_t n, uint32_t L, int op, B init, B* out, void* ws,
+                         size_t ws_bytes, void* stream)
+{
+    return with_op<B>(op, [&](auto tag) {
+        using V = typename decltype(tag)::type;
+        return reduce_impl<V>(reinterpret_cast<const V*>(x), n, L, __builtin_bit_cast(V, init),
+                              reinterpret_cast<V*>(out), ws, ws_bytes, stream);
+    });
+}
+
+template <typename B>
+canon_status_t reduce_rows_op(const B* x, size_t rows, size_t cols, size_t ldx, uint32_t L,
+                              int op, B init, B* out, void* ws, size_t ws_bytes, void* stream)
+{
+    return with_op<B>(op, [&](auto tag) {
+        using V = typename decltype(tag)::type;
+        return reduce_rows_impl<V>(reinterpret_cast<const V*>(x), rows, cols, ldx, L,
+                                   __builtin_bit_cast(V, init), reinterpret_cast<V*>(out), ws,
+                                   ws_bytes, stream);
+    });
+}
+
+template <typename B>
+canon_status_t scan_op(const B* x, B* y, size_t n, int policy, uint32_t param, int op, int kind,
+                       B init, void* ws, size_t ws_bytes, void* stream)
+{
+    return with_op<B>(op, [&](auto tag) {
+        using V = typename decltype(tag)::type;
+        const ScanOut<V> out{__builtin_bit_cast(V, init), kind};
+        return scan_impl<V>(reinterpret_cast<const V*>(x), reinterpret_cast<V*>(y), n, policy,
+                            param, &out, ws, ws_bytes, stream);
+    });
+}
+
+template <typename B>
+canon_status_t scan_rows_op(const B* x, size_t ldx, B* y, size_t ldy, size_t rows, size_t cols,
+                            int policy, uint32_t param, int op, int kind, B init, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    return with_op<B>(op, [&](auto tag) {
+        using V = typename decltype(tag)::type;
+        const ScanOut<V> out{__builtin_bit_cast(V, init), kind};
+        return scan_rows_impl<V>(reinterpret_cast<const V*>(x), ldx, reinterpret_cast<V*>(y), ldy,
+                                 rows, cols, policy, param, &out, ws, ws_bytes, stream);
+    });
 }
 
 }  // namespace
@@ -381,6 +489,64 @@ canon_status_t canon_scan_rows_with_init_f32(const float* x, size_t ldx, float* 
     const ScanOut<float> out{init, kind};
     return scan_rows_impl<float>(x, ldx, y, ldy, rows, cols, policy, param, &out, ws, ws_bytes,
                                  stream);
+}
+
+canon_status_t canon_reduce_op_f64(const double* x, size_t n, uint32_t L, int op, double init,
+                                   double* out, void* ws, size_t ws_bytes, void* stream)
+{
+    return reduce_op<double>(x, n, L, op, init, out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_reduce_op_f32(const float* x, size_t n, uint32_t L, int op, float init,
+                                   float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    return reduce_op<float>(x, n, L, op, init, out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_reduce_rows_op_f64(const double* x, size_t rows, size_t cols, size_t ldx,
+                                        uint32_t L, int op, double init, double* out, void* ws,
+                                        size_t ws_bytes, void* stream)
+{
+    return reduce_rows_op<double>(x, rows, cols, ldx, L, op, init, out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_reduce_rows_op_f32(const float* x, size_t rows, size_t cols, size_t ldx,
+                                        uint32_t L, int op, float init, float* out, void* ws,
+                                        size_t ws_bytes, void* stream)
+{
+    return reduce_rows_op<float>(x, rows, cols, ldx, L, op, init, out, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_op_f64(const double* x, double* y, size_t n, int policy, uint32_t param,
+                                 int op, int kind, double init, void* ws, size_t ws_bytes,
+                                 void* stream)
+{
+    return scan_op<double>(x, y, n, policy, param, op, kind, init, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_op_f32(const float* x, float* y, size_t n, int policy, uint32_t param,
+                                 int op, int kind, float init, void* ws, size_t ws_bytes,
+                                 void* stream)
+{
+    return scan_op<float>(x, y, n, policy, param, op, kind, init, ws, ws_bytes, stream);
+}
+
+canon_status_t canon_scan_rows_op_f64(const double* x, size_t ldx, double* y, size_t ldy,
+                                      size_t rows, size_t cols, int policy, uint32_t param,
+                                      int op, int kind, double init, void* ws, size_t ws_bytes,
+                                      void* stream)
+{
+    return scan_rows_op<double>(x, ldx, y, ldy, rows, cols, policy, param, op, kind, init, ws,
+                                ws_bytes, stream);
+}
+
+canon_status_t canon_scan_rows_op_f32(const float* x, size_t ldx, float* y, size_t ldy,
+                                      size_t rows, size_t cols, int policy, uint32_t param,
+                                      int op, int kind, float init, void* ws, size_t ws_bytes,
+                                      void* stream)
+{
+    return scan_rows_op<float>(x, ldx, y, ldy, rows, cols, policy, param, op, kind, init, ws,
+                               ws_bytes, stream);
 }
 
 canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream)

@@ -13,34 +13,128 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace canon {
 
 constexpr int kWave = 64;
 
 template <typename T> struct Elem;
 template <> struct Elem<double> {
+    using base_t = double;
     using bits_t = uint64_t;
     static constexpr int E = 2;     // elements per 16-byte vector
     static constexpr int LOGE = 1;
     typedef double vec_t __attribute__((ext_vector_type(2)));
 };
 template <> struct Elem<float> {
+    using base_t = float;
     using bits_t = uint32_t;
     static constexpr int E = 4;
     static constexpr int LOGE = 2;
     typedef float vec_t __attribute__((ext_vector_type(4)));
 };
 
-template <typename T> __device__ __forceinline__ T neg_zero() { return T(-0.0); }
+// ------------------------------------------------------------- operators
+// The expression is the same for any binary operator.  Kernels are written
+// with `a + b` on their value type T; for an operator other than IEEE
+// addition T is OpVal<B, Op>, a B-sized wrapper whose `+` applies Op (left
+// operand on the left), so every kernel evaluates the identical tree.  Op:
+//   OpMul  multiplication, absent value 1.0
+//   OpMin  IEEE 754-2019 minimum (NaN if either operand is NaN, -0.0 below
+//          +0.0), absent value +inf
+//   OpMax  IEEE 754-2019 maximum, absent value -inf
+// The absent value is the operator's exact identity (op(x, absent) == x for
+// every x, NaN payloads aside), as -0.0 is for addition.
+struct OpMul {
+    template <typename B>
+    static __host__ __device__ __forceinline__ B f(B a, B b) { return a * b; }
+    template <typename B>
+    static __host__ __device__ __forceinline__ B identity() { return B(1.0); }
+};
+// minimum / maximum written as selects (no branches inside the unrolled
+// networks): equal operands (also +0.0 and -0.0) give the OR (minimum) or
+// AND (maximum) of their bits, i.e. the operand itself or -0.0 / +0.0.
+template <typename B>
+__host__ __device__ __forceinline__ B bits_or(B a, B b)
+{
+    using U = typename std::conditional<sizeof(B) == 8, uint64_t, uint32_t>::type;
+    return __builtin_bit_cast(B, (U)(__builtin_bit_cast(U, a) | __builtin_bit_cast(U, b)));
+}
+template <typename B>
+__host__ __device__ __forceinline__ B bits_and(B a, B b)
+{
+    using U = typename std::conditional<sizeof(B) == 8, uint64_t, uint32_t>::type;
+    return __builtin_bit_cast(B, (U)(__builtin_bit_cast(U, a) & __builtin_bit_cast(U, b)));
+}
+struct OpMin {
+    template <typename B>
+    static __host__ __device__ __forceinline__ B f(B a, B b)
+    {
+        const B m = a < b ? a : b;
+        const B r = a == b ? bits_or(a, b) : m;
+        return (a != a || b != b) ? a + b : r;
+    }
+    template <typename B>
+    static __host__ __device__ __forceinline__ B identity() { return B(__builtin_inf()); }
+};
+struct OpMax {
+    template <typename B>
+    static __host__ __device__ __forceinline__ B f(B a, B b)
+    {
+        const B m = a > b ? a : b;
+        const B r = a == b ? bits_and(a, b) : m;
+        return (a != a || b != b) ? a + b : r;
+    }
+    template <typename B>
+    static __host__ __device__ __forceinline__ B identity() { return B(-__builtin_inf()); }
+};
+
+template <typename B, class Op>
+struct OpVal {
+    B v;
+};
+template <typename B, class Op>
+__host__ __device__ __forceinline__ OpVal<B, Op> operator+(OpVal<B, Op> a, OpVal<B, Op> b)
+{
+    return OpVal<B, Op>{Op::template f<B>(a.v, b.v)};
+}
+template <typename B, class Op> struct Elem<OpVal<B, Op>> : Elem<B> {};
+
+// The absent value of T's operator.
+template <typename T> struct Absent {
+    static __device__ __forceinline__ T value() { return T(-0.0); }
+};
+template <typename B, class Op> struct Absent<OpVal<B, Op>> {
+    static __device__ __forceinline__ OpVal<B, Op> value()
+    {
+        return OpVal<B, Op>{Op::template identity<B>()};
+    }
+};
+template <typename T> __device__ __forceinline__ T neg_zero() { return Absent<T>::value(); }
+
+// Keeps a value in a VGPR at this point (an empty asm operand): the compiler
+// may not move the operations that produce it past here.
+template <typename T> __device__ __forceinline__ void pin_reg(T& x) { asm volatile("" : "+v"(x)); }
+template <typename B, class Op> __device__ __forceinline__ void pin_reg(OpVal<B, Op>& x)
+{
+    asm volatile("" : "+v"(x.v));
+}
 
 // ---------------------------------------------------------------- 16-byte I/O
+// (T is double / float or an OpVal wrapper of one: same bits either way.)
 template <typename T>
 __device__ __forceinline__ void load_vec(const T* p, T (&v)[Elem<T>::E])
 {
     using V = typename Elem<T>::vec_t;
     V x = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
 #pragma unroll
-    for (int e = 0; e < Elem<T>::E; ++e) v[e] = x[e];
+    for (int e = 0; e < Elem<T>::E; ++e) {
+        // through a scalar: a bit cast of the vector element itself reads
+        // element 0 (seen with this compiler)
+        const typename Elem<T>::base_t b = x[e];
+        v[e] = __builtin_bit_cast(T, b);
+    }
 }
 
 template <typename T>
@@ -49,7 +143,10 @@ __device__ __forceinline__ void store_vec(T* p, const T (&v)[Elem<T>::E])
     using V = typename Elem<T>::vec_t;
     V x;
 #pragma unroll
-    for (int e = 0; e < Elem<T>::E; ++e) x[e] = v[e];
+    for (int e = 0; e < Elem<T>::E; ++e) {
+        const typename Elem<T>::base_t b = __builtin_bit_cast(typename Elem<T>::base_t, v[e]);
+        x[e] = b;
+    }
     __builtin_nontemporal_store(x, reinterpret_cast<V*>(p));
 }
 
@@ -86,6 +183,17 @@ __device__ __forceinline__ float readlane(float v, int lane)
 {
     return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_readlane(
                                          (int)__builtin_bit_cast(uint32_t, v), lane));
+}
+
+template <int PAT, typename B, class Op>
+__device__ __forceinline__ OpVal<B, Op> swz(OpVal<B, Op> v)
+{
+    return OpVal<B, Op>{swz<PAT>(v.v)};
+}
+template <typename B, class Op>
+__device__ __forceinline__ OpVal<B, Op> readlane(OpVal<B, Op> v, int lane)
+{
+    return OpVal<B, Op>{readlane(v.v, lane)};
 }
 
 // Value of `v` held by lane (lane ^ MASK), MASK a power of two below 64.
@@ -166,14 +274,18 @@ __device__ __forceinline__ uint64_t pack_word(float v)
 {
     return (1ull << 32) | (uint64_t)__builtin_bit_cast(uint32_t, v);
 }
-template <typename T> __device__ __forceinline__ T unpack_word(uint64_t w);
-template <> __device__ __forceinline__ double unpack_word<double>(uint64_t w)
+template <typename B, class Op>
+__device__ __forceinline__ uint64_t pack_word(OpVal<B, Op> v)
 {
-    return __builtin_bit_cast(double, w);
+    return pack_word(v.v);
 }
-template <> __device__ __forceinline__ float unpack_word<float>(uint64_t w)
+// The value of a ready word (double / float, or their OpVal wrappers).
+template <typename T> __device__ __forceinline__ T unpack_word(uint64_t w)
 {
-    return __builtin_bit_cast(float, (uint32_t)w);
+    if constexpr (sizeof(T) == 8)
+        return __builtin_bit_cast(T, w);
+    else
+        return __builtin_bit_cast(T, (uint32_t)w);
 }
 
 template <typename T>

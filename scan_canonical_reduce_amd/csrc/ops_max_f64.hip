@@ -1,0 +1,10 @@
+// The kernels reached by the operator entry points, for double with the
+// operator OpMax (device.hpp) in place of addition.
+#include "ops_instantiate.hpp"
+
+namespace canon {
+
+using OpValue = OpVal<double, OpMax>;
+CANON_INSTANTIATE_ORDER_FREE_OP(OpValue)
+
+}  // namespace canon

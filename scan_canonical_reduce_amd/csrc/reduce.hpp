@@ -93,7 +93,9 @@ inline uint64_t reduce_partials_bytes(const ReducePlan& pl, uint32_t L, size_t e
     return pl.P * (uint64_t)L * elem_size;
 }
 
-template <typename T>
+// POW2 = false: only the general streaming kernel is built; the plan must
+// then be one for unaligned input (pl.pow2 false).
+template <typename T, bool POW2 = true>
 hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, T* partial,
                          const ReducePlan& pl, hipStream_t s);
 

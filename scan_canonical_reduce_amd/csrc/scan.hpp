@@ -90,13 +90,19 @@ hipError_t launch_scan_with_init(const T* x, T* y, uint64_t n, bool pairwise, in
                                  bool aligned, uint64_t* ws, const ScanLayout& lay,
                                  const ScanOut<T>& out, hipStream_t s);
 
+template <typename T>
+hipError_t launch_scan_pw_with_init(const T* x, T* y, uint64_t n, bool aligned, uint64_t* ws,
+                                    const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s);
+
 // y[r * ldy] = v for r < rows, on stream s.
 template <typename T>
 hipError_t launch_put_column(T* y, uint64_t ldy, uint64_t rows, T v, hipStream_t s);
 
 // out == null: the plain inclusive scan of every row; else the scan with an
 // initial value that *out describes.
-template <typename T>
+// PLAIN = false: only the kernels with an output stage are built (out must
+// not be null).  PW_ONLY: only the pairwise kernels are built.
+template <typename T, bool PLAIN = true, bool PW_ONLY = false>
 hipError_t launch_scan_rows(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t rows,
                             uint64_t cols, bool pairwise, int b_log, bool aligned,
                             const ScanOut<T>* out, hipStream_t s);

@@ -114,12 +114,14 @@ inline size_t ip_lds_bytes(const IpLayout& lay, size_t elem_size)
 template <typename T>
 struct ScanOut;
 
-template <typename T>
+// PLAIN = false (both launchers): only the kernels with an output stage are
+// built (out must not be null).
+template <typename T, bool PLAIN = true>
 hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
                                  uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>* out,
                                  hipStream_t s);
 
-template <typename T>
+template <typename T, bool PLAIN = true>
 hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,
                           uint64_t cols, uint32_t* err, T* nodes, const IpLayout& lay,
                           const ScanOut<T>* out, hipStream_t s);

@@ -1,0 +1,453 @@
+// Canonical scan, policy iterated_pairwise<L>, in one pass over the input
+// (gfx950, fast geometry: L = 64 * E * RV, 16-byte aligned rows).
+//
+// Expression and evaluation inside a tile: as in scan_ip.hip (canonical-
+// reduce README, P4229R0 "Summary"; P4016R0 "Key Design Points").  Tile t
+// needs, for every lane, the pairwise value of that lane over all rows
+// before the tile: the right-nested combination of node (k, (t >> k) - 1)
+// for the set bits k of t, lowest level first, where node (k, u) is the
+// complete per-lane pairwise tree over tiles [u 2^k, (u+1) 2^k).
+//
+// Across tiles, without a second read of the input and without any
+// workgroup waiting before it has published what others need:
+//   * each tile publishes its own per-lane totals (node (0, t)) as soon as
+//     its in-tile column scan is done (the tile's "front");
+//   * node (k+1, v) is formed by whichever of its two children finishes
+//     second: after publishing a child, the finishing tile counts it in the
+//     parent's arrival counter, and the tile that counts second reads the
+//     other child, adds (left child on the left) and publishes the parent,
+//     then tries the next level; a tile counting first stops there;
+//   * the tile's "back" then reads the nodes of its set bits, applies them,
+//     walks its rows' lane trees and stores.
+// Every node a tile waits for covers only tiles with smaller tickets, and
+// the work that publishes it waits only for words already being written, so
+// every wait ends.  Every value is fixed by position, never by arrival order.
+// Published words are self-describing (device.hpp): polled without fences.
+//
+// PIPE kernels are persistent and software-pipelined like the single-pass
+// scalar scan: a workgroup holds two tiles and runs the next tile's front
+// before the current tile's back, so a back's reads of nodes published by
+// the tiles just before it have had a whole front to arrive.
+#pragma once
+#include "device.hpp"
+#include "launch.hpp"
+#include "scan.hpp"
+#include "scan_ip.hpp"
+#include "scan_ip_fast.hpp"
+
+namespace canon {
+
+// LDS values staged per batch of look-back nodes (a multiple of kIpThreads;
+// at least one node of L values).
+constexpr int kIp1Stage = 1024;
+// Persistent, two tiles per workgroup (else one workgroup per tile): the
+// geometries whose two tiles fit the registers without spilling.
+template <int LOGRV>
+constexpr bool ip1_pipelined()
+{
+    return LOGRV == 0;
+}
+
+__device__ __forceinline__ uint64_t* ip1_word(uint64_t* ws, const IpSingleLayout& lay, int k,
+                                              uint64_t seg, uint64_t u, uint64_t col)
+{
+    return ws + lay.woff[k] + (seg * lay.g.cnt[k] + u) * (uint64_t)lay.g.L + col;
+}
+
+__device__ __forceinline__ uint32_t* ip1_counter(uint64_t* ws, const IpSingleLayout& lay, int k,
+                                                 uint64_t seg, uint64_t v)
+{
+    return reinterpret_cast<uint32_t*>(ws + lay.cbase) + lay.coff[k] + seg * lay.g.cnt[k] + v;
+}
+
+// Header (error word, ticket), every node word not ready, counters zero.
+template <typename T>
+__global__ __launch_bounds__(256) void k_ip1_init(uint64_t* __restrict__ ws, IpSingleLayout lay)
+{
+    const uint64_t nr = not_ready_word<T>();
+    const uint64_t cw = (lay.counters + 1) / 2;
+    const uint64_t total = lay.cbase + cw;
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * 256)
+        ws[i] = i < 32 ? 0ull : (i < lay.cbase ? nr : 0ull);
+}
+
+template <typename T, int LOGRV>
+struct Ip1Shared {
+    static constexpr int L = IpFast<T, LOGRV>::L;
+    static constexpr int STAGE = L > kIp1Stage ? L : kIp1Stage;
+    T row[4][L];  // per-wave rows exchanged between the waves
+    T h[STAGE];   // node values of the earlier tiles, a batch at a time
+    uint32_t ticket;
+};
+
+template <typename T, int LOGRV>
+struct Ip1Ctx {
+    const T* x;
+    uint64_t ldx;
+    T* y;
+    uint64_t ldy;
+    uint64_t cols;
+    uint64_t* ws;
+    const IpSingleLayout* lay;
+    uint32_t* err;
+    Ip1Shared<T, LOGRV>* sh;
+    int lane, w;
+    T init;
+    int kind;
+};
+
+// One tile in registers: vector u of thread (w, lane) holds row
+// w * RW + u / RV of the tile, columns ((u % RV) * 64 + lane) * E + e.
+template <typename T, int LOGRV>
+struct Ip1Tile {
+    T a[IpFast<T, LOGRV>::NV][Elem<T>::E];
+    uint64_t item;
+};
+
+template <typename T, int LOGRV>
+__device__ __forceinline__ uint64_t ip1_ticket(const Ip1Ctx<T, LOGRV>& c)
+{
+    if (threadIdx.x == 0)
+        c.sh->ticket = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(c.ws + 1), 1u,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint64_t it = c.sh->ticket;
+    __syncthreads();  // the slot is rewritten by the next ticket
+    return it;
+}
+
+template <typename T, int LOGRV>
+__device__ __forceinline__ void ip1_load(Ip1Tile<T, LOGRV>& s, uint64_t item,
+                                         const Ip1Ctx<T, LOGRV>& c)
+{
+    using F = IpFast<T, LOGRV>;
+    s.item = item;
+    const uint64_t seg = item / c.lay->g.tps, t = item % c.lay->g.tps;
+    const uint64_t row0 = t * F::R;
+    const T* xs = c.x + seg * c.ldx;
+    if ((row0 + F::R) * F::L <= c.cols)
+        ipf_load<T, LOGRV, false>(xs, c.cols, row0, c.w, c.lane, s.a);
+    else
+        ipf_load<T, LOGRV, true>(xs, c.cols, row0, c.w, c.lane, s.a);
+}
+
+// Front: the lane prefixes inside the tile, the tile's totals published,
+// and the parents it completes.
+template <typename T, int LOGRV>
+__device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, LOGRV>& c)
+{
+    using F = IpFast<T, LOGRV>;
+    constexpr int E = F::E, RV = F::RV, RW = F::RW;
+    const IpSingleLayout& lay = *c.lay;
+    const uint64_t seg = s.item / lay.g.tps, t = s.item % lay.g.tps;
+    const int lane = c.lane, w = c.w;
+    auto& a = s.a;
+
+    ipf_columns_in_wave<T, LOGRV>(a);
+#pragma unroll
+    for (int q = 0; q < RV; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            c.sh->row[w][(q * 64 + lane) * E + e] = a[(RW - 1) * RV + q][e];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < RV; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = (q * 64 + lane) * E + e;
+            const T t0 = c.sh->row[0][j], t1 = c.sh->row[1][j], t2 = c.sh->row[2][j];
+            if (w & 1) {
+                const T v = (w & 2) ? t2 : t0;
+#pragma unroll
+                for (int r = 0; r < RW; ++r) a[r * RV + q][e] = v + a[r * RV + q][e];
+            }
+            if (w & 2) {
+                const T v = t0 + t1;
+#pragma unroll
+                for (int r = 0; r < RW; ++r) a[r * RV + q][e] = v + a[r * RV + q][e];
+            }
+        }
+    __syncthreads();  // every wave has read row[]
+
+    if (w == 3) {
+        T cur[RV][E];
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                cur[q][e] = a[(RW - 1) * RV + q][e];
+                publish(ip1_word(c.ws, lay, 0, seg, t, (uint64_t)(q * 64 + lane) * E + e),
+                        cur[q][e]);
+            }
+        uint64_t u = t;
+        for (int k = 0; k + 1 < lay.g.levels; ++k) {
+            const uint64_t v = u >> 1;
+            if (v >= lay.g.cnt[k + 1]) break;  // the parent covers tiles past the end
+            uint32_t before = 0;
+            if (lane == 0)
+                before = __hip_atomic_fetch_add(ip1_counter(c.ws, lay, k + 1, seg, v), 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            before = __builtin_amdgcn_readfirstlane(before);
+            if (before == 0) break;  // the sibling completes the parent
+            // the sibling's words: all reads issued, then each waited for
+            uint64_t sw[RV][E];
+#pragma unroll
+            for (int q = 0; q < RV; ++q)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    sw[q][e] = __hip_atomic_load(
+                        ip1_word(c.ws, lay, k, seg, u ^ 1, (uint64_t)(q * 64 + lane) * E + e),
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int q = 0; q < RV; ++q)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint64_t col = (uint64_t)(q * 64 + lane) * E + e;
+                    const T sib = ready_or_wait<T>(
+                        sw[q][e], ip1_word(c.ws, lay, k, seg, u ^ 1, col), c.err);
+                    cur[q][e] = (u & 1) ? sib + cur[q][e] : cur[q][e] + sib;
+                    publish(ip1_word(c.ws, lay, k + 1, seg, v, col), cur[q][e]);
+                }
+            u = v;
+        }
+    }
+}
+
+// Back: the nodes of the earlier tiles applied (right-nested, lowest level
+// first), each row's lane tree walked, the outputs stored.
+template <typename T, int LOGRV, bool OUTX>
+__device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, LOGRV>& c)
+{
+    using F = IpFast<T, LOGRV>;
+    using SH = Ip1Shared<T, LOGRV>;
+    constexpr int E = F::E, RV = F::RV, RW = F::RW;
+    constexpr int NB = SH::STAGE / F::L;         // nodes per batch
+    constexpr int PER = SH::STAGE / kIpThreads;  // words per thread per batch
+    const IpSingleLayout& lay = *c.lay;
+    const uint64_t seg = s.item / lay.g.tps, t = s.item % lay.g.tps;
+    const int lane = c.lane, w = c.w;
+    auto& a = s.a;
+    T* ys = c.y + seg * c.ldy;
+    const uint64_t row0 = t * F::R;
+    const bool full = (row0 + F::R) * F::L <= c.cols;
+
+    // The node words of up to NB set bits at a time, spread over the threads
+    // (word idx of a batch: node idx / L, lane idx % L), every read issued
+    // before any is waited for, then staged in LDS.
+    T b[RV][E];
+#pragma unroll
+    for (int q = 0; q < RV; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e) b[q][e] = neg_zero<T>();
+    int k = 0;
+    while (k < lay.g.levels && (t >> k) != 0) {
+        int lv[NB];
+        int nb = 0;
+        for (; k < lay.g.levels && (t >> k) != 0 && nb < NB; ++k)
+            if ((t >> k) & 1) lv[nb++] = k;
+        if (nb == 0) break;
+        uint64_t wv[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = i * kIpThreads + (int)threadIdx.x;
+            const int m = idx / F::L, col = idx % F::L;
+            wv[i] = not_ready_word<T>();
+            if (m < nb)
+                wv[i] = __hip_atomic_load(ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = i * kIpThreads + (int)threadIdx.x;
+            const int m = idx / F::L, col = idx % F::L;
+            if (m < nb)
+                c.sh->h[idx] = ready_or_wait<T>(
+                    wv[i], ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col), c.err);
+        }
+        __syncthreads();
+        for (int m = 0; m < nb; ++m) {
+#pragma unroll
+            for (int q = 0; q < RV; ++q)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const T hv = c.sh->h[m * F::L + (q * 64 + lane) * E + e];
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) a[r * RV + q][e] = hv + a[r * RV + q][e];
+                    b[q][e] = hv + b[q][e];
+                }
+        }
+        __syncthreads();  // h is refilled by the next batch
+    }
+    // the B row of each wave's first row: the A row just above it
+#pragma unroll
+    for (int q = 0; q < RV; ++q)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            c.sh->row[w][(q * 64 + lane) * E + e] = a[(RW - 1) * RV + q][e];
+    __syncthreads();
+    if (w > 0) {
+#pragma unroll
+        for (int q = 0; q < RV; ++q)
+#pragma unroll
+            for (int e = 0; e < E; ++e) b[q][e] = c.sh->row[w - 1][(q * 64 + lane) * E + e];
+    }
+    __syncthreads();  // row[] is rewritten by the next front
+
+    // walk every lane up its row's tree (each row's sibling values built once)
+    IpRowTree<T, LOGRV> tb;
+    tb.template build<RV>(b, 0, lane);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        IpRowTree<T, LOGRV> ta;
+        ta.template build<F::NV>(a, r * RV, lane);
+        T val[RV][E];
+        ip_walk<T, LOGRV>(a, r * RV, ta, tb, lane, val);
+        const uint64_t row = row0 + (uint64_t)w * RW + r;
+        if constexpr (OUTX) {
+            if (c.kind != kScanInclusive) {
+                // one position up, the value before a row's first lane being
+                // the end of the previous row (the root of its B tree);
+                // include_initial: the holder of element cols - 1 also
+                // writes y[cols]
+                if (c.kind == kScanIncludeInitial) {
+#pragma unroll
+                    for (int q = 0; q < RV; ++q)
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (row * F::L + (uint64_t)(q * 64 + lane) * E + e + 1 == c.cols)
+                                ys[c.cols] = c.init + val[q][e];
+                }
+                T prev = tb.root;
+#pragma unroll
+                for (int q = 0; q < RV; ++q) {
+                    const T up = shfl_up1(val[q][E - 1]);
+                    const T before = lane == 0 ? prev : up;
+                    prev = readlane(val[q][E - 1], 63);
+#pragma unroll
+                    for (int e = E - 1; e > 0; --e) val[q][e] = val[q][e - 1];
+                    val[q][0] = before;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < RV; ++q)
+#pragma unroll
+                for (int e = 0; e < E; ++e) val[q][e] = c.init + val[q][e];
+        }
+#pragma unroll
+        for (int q = 0; q < RV; ++q) {
+            const uint64_t gi = row * F::L + (uint64_t)(q * 64 + lane) * E;
+            if (full || gi + E <= c.cols) {
+                store_vec(ys + gi, val[q]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (gi + e < c.cols) ys[gi + e] = val[q][e];
+            }
+        }
+        tb = ta;
+    }
+}
+
+// PIPE: persistent workgroups, two tiles each (the next front before the
+// current back); else one workgroup per tile.
+template <typename T, int LOGRV, bool OUTX, bool PIPE>
+__global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ x, uint64_t ldx,
+                                                          T* __restrict__ y, uint64_t ldy,
+                                                          uint64_t cols, uint64_t* __restrict__ ws,
+                                                          IpSingleLayout lay, T init, int kind)
+{
+    __shared__ Ip1Shared<T, LOGRV> sh;
+    const Ip1Ctx<T, LOGRV> c{x,
+                             ldx,
+                             y,
+                             ldy,
+                             cols,
+                             ws,
+                             &lay,
+                             reinterpret_cast<uint32_t*>(ws),
+                             &sh,
+                             (int)(threadIdx.x & 63),
+                             (int)(threadIdx.x >> 6),
+                             init,
+                             kind};
+    const uint64_t items = lay.g.nseg * lay.g.tps;
+    uint64_t it = ip1_ticket(c);
+    if (it >= items) return;
+    Ip1Tile<T, LOGRV> A, B;
+    ip1_load(A, it, c);
+    ip1_front(A, c);
+    if constexpr (!PIPE) {
+        ip1_back<T, LOGRV, OUTX>(A, c);
+    } else {
+        for (;;) {
+            it = ip1_ticket(c);
+            if (it < items) {
+                ip1_load(B, it, c);
+                ip1_front(B, c);
+            }
+            ip1_back<T, LOGRV, OUTX>(A, c);
+            if (it >= items) break;
+            it = ip1_ticket(c);
+            if (it < items) {
+                ip1_load(A, it, c);
+                ip1_front(A, c);
+            }
+            ip1_back<T, LOGRV, OUTX>(B, c);
+            if (it >= items) break;
+        }
+    }
+}
+
+template <typename T, int LOGRV, bool OUTX>
+static hipError_t launch_ip1(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                             uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
+                             hipStream_t s)
+{
+    const uint64_t items = lay.g.nseg * lay.g.tps;
+    constexpr bool PIPE = ip1_pipelined<LOGRV>();
+    constexpr auto kern = k_ip_single<T, LOGRV, OUTX, PIPE>;
+    uint64_t grid = items;
+    if (PIPE) {
+        const uint64_t fit = resident_grid<kern>(kIpThreads);
+        if (grid > fit) grid = fit;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kIpThreads), 0, s, x, ldx, y, ldy, cols,
+                       ws, lay, out.init, out.kind);
+    return hipGetLastError();
+}
+
+template <typename T, bool OUTX>
+static hipError_t launch_ip1_o(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                               uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
+                               hipStream_t s)
+{
+    switch (lay.g.fast_logrv) {
+        case 0: return launch_ip1<T, 0, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
+        case 1: return launch_ip1<T, 1, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
+        case 2: return launch_ip1<T, 2, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
+        case 3: return launch_ip1<T, 3, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// One pass; the caller has checked cols > 0, lay.g.fast_logrv >= 0 and that
+// the items fit one launch (nseg * tps < 2^31).
+template <typename T, bool PLAIN>
+hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                                 uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>* out,
+                                 hipStream_t s)
+{
+    const uint64_t words = lay.cbase + (lay.counters + 1) / 2;
+    uint64_t blocks = (words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL((k_ip1_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws, lay);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (out) return launch_ip1_o<T, true>(x, ldx, y, ldy, cols, ws, lay, *out, s);
+    if constexpr (PLAIN)
+        return launch_ip1_o<T, false>(x, ldx, y, ldy, cols, ws, lay, ScanOut<T>{}, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace canon

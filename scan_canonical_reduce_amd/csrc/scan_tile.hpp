@@ -139,10 +139,10 @@ struct ScanTile {
 #pragma unroll
         for (int u = 0; u < V; ++u) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[u][e]));
+            for (int e = 0; e < E; ++e) pin_reg(v[u][e]);
             if constexpr (BD) {
 #pragma unroll
-                for (int k = 0; k < NB; ++k) asm volatile("" : "+v"(c[u][k]));
+                for (int k = 0; k < NB; ++k) pin_reg(c[u][k]);
             }
         }
     }

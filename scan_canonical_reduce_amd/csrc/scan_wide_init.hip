@@ -1,16 +1,9 @@
 // The block_dyadic kernels for blocks of whole vectors inside one wave
 // (WideTile in scan_kernels.hpp), output stage of a scan with an initial
 // value.
-#include "scan_kernels.hpp"
+#include "scan_wide_def.hpp"
 
 namespace canon {
-
-template <typename T, bool OUTX>
-hipError_t launch_wide(const T* x, T* y, uint64_t n, int b_log, bool aligned, uint64_t* ws,
-                       const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s)
-{
-    return launch_wide_impl<T, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
-}
 
 template hipError_t launch_wide<double, true>(const double*, double*, uint64_t, int, bool,
                                               uint64_t*, const ScanLayout&,

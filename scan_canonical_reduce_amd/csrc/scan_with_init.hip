@@ -1,39 +1,8 @@
-// Canonical scan with an initial value, single pass (pairwise,
-// block_dyadic<B>): the kernels of scan_kernels.hpp with the output stage
-// that adds init and, for the exclusive and include_initial kinds, shifts
-// every value one position up.
-#include "scan_kernels.hpp"
+// Scan with an initial value (scan_with_init_impl.hpp), instantiated for
+// double and float with IEEE addition.
+#include "scan_with_init_impl.hpp"
 
 namespace canon {
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_put_column(T* y, uint64_t ldy, uint64_t rows, T v)
-{
-    for (uint64_t r = (uint64_t)blockIdx.x * 256 + threadIdx.x; r < rows;
-         r += (uint64_t)gridDim.x * 256)
-        y[r * ldy] = v;
-}
-
-template <typename T>
-hipError_t launch_put_column(T* y, uint64_t ldy, uint64_t rows, T v, hipStream_t s)
-{
-    if (rows == 0) return hipSuccess;
-    uint64_t grid = (rows + 255) / 256;
-    if (grid > 4096) grid = 4096;
-    hipLaunchKernelGGL((k_put_column<T>), dim3((unsigned)grid), dim3(256), 0, s, y, ldy, rows, v);
-    return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_scan_with_init(const T* x, T* y, uint64_t n, bool pairwise, int b_log,
-                                 bool aligned, uint64_t* ws, const ScanLayout& lay,
-                                 const ScanOut<T>& out, hipStream_t s)
-{
-    if (n == 0)
-        return out.kind == kScanIncludeInitial ? launch_put_column(y, 1, 1, out.init, s)
-                                               : hipSuccess;
-    return launch_scan_impl<T, true>(x, y, n, pairwise, b_log, aligned, ws, lay, out, s);
-}
 
 template hipError_t launch_put_column<double>(double*, uint64_t, uint64_t, double, hipStream_t);
 template hipError_t launch_put_column<float>(float*, uint64_t, uint64_t, float, hipStream_t);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(canon):
 
 def test_version_and_status_strings(canon):
     L = canon.lib()
-    assert L.canon_abi_version() == 2
+    assert L.canon_abi_version() == 3
     for s in range(5):
         assert L.canon_status_str(s).decode().startswith("CANON_")
     assert L.canon_last_hip_error() == 0
@@ -127,6 +127,20 @@ def test_scan_with_init_argument_errors(canon):
     assert g(None, 10, None, 11, 0, 10, 0, 0, 2, 0.0, None, 0, None) == 0   # no rows
     assert g(None, 1, None, 1, 3, 0, 0, 0, 2, 0.0, None, 0, None) == 1      # cols 0: y needed
     assert g(None, 1, None, 1, 3, 0, 0, 0, 1, 0.0, None, 0, None) == 0      # nothing to write
+
+
+def test_operator_argument_errors(canon):
+    L = canon.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.canon_reduce_op_f64(fake, 10, 4, 9, 1.0, fake, None, 0, None) == 1   # bad operator
+    assert L.canon_reduce_op_f64(fake, 10, 0, 1, 1.0, fake, None, 0, None) == 1   # L = 0
+    assert L.canon_scan_op_f64(fake, fake, 10, 0, 0, -1, 0, 1.0, None, 0, None) == 1
+    assert L.canon_scan_op_f64(fake, fake, 10, 0, 0, 1, 7, 1.0, None, 0, None) == 1  # bad kind
+    assert L.canon_scan_op_f32(fake, fake, 1 << 20, 0, 0, 2, 0, 1.0, None, 0, None) == 3
+    assert L.canon_scan_op_f32(fake, fake, 1 << 20, 1, 128, 1, 0, 1.0, None, 0, None) == 3
+    assert L.canon_scan_rows_op_f64(fake, 10, fake, 10, 3, 10, 0, 0, 3, 2, 0.0, None, 0,
+                                    None) == 1                                   # ldy < cols+1
+    assert L.canon_reduce_rows_op_f32(fake, 4, 10, 9, 4, 1, 0.0, fake, None, 0, None) == 1
 
 
 def test_binding_refuses_cpu_tensors(canon):
