@@ -43,21 +43,18 @@ N_MAIN = 1 << 28
 ROWS, COLS = 16384, 4096
 PROFILES = os.path.join(ROOT, "profiles")
 # sources whose kernels the traffic summaries describe
-KERNEL_SOURCES = ["device.hpp", "launch.hpp", "reduce.hpp", "reduce.hip", "scan.hpp",
-                  "scan_tile.hpp", "scan_kernels.hpp", "scan.hip", "scan_with_init.hip",
-                  "scan_wide.hip", "scan_wide_init.hip",
-                  "scan_rows.hip", "scan_ip.hpp", "scan_ip_fast.hpp", "scan_ip.hip",
-                  "scan_ip1.hip"]
-
-
 def kernel_sources_sha256() -> str:
+    """SHA-256 over every source of the library (csrc/*.hip, *.hpp, *.cpp in
+    name order): the profiles' traffic figures are reported only while it
+    still matches the value stored with them."""
+    import glob
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        p = os.path.join(ROOT, "scan_canonical_reduce_amd", "csrc", f)
-        if os.path.exists(p):
-            h.update(f.encode())
-            h.update(open(p, "rb").read())
+    d = os.path.join(ROOT, "scan_canonical_reduce_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.hpp")) +
+                    glob.glob(os.path.join(d, "*.cpp"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
     return h.hexdigest()
 
 
@@ -414,6 +411,55 @@ def run_configs(torch, canon, synth, dev, reps=20):
                    ("iterated_pairwise", 128, "exclusive", 1.0),
                    ("block_dyadic", 16, "inclusive", 1.0)))
     scan_init_cfg("C5 with init", "scan_2e28_f32", (("block_dyadic", 256, "exclusive", 1.0),))
+
+    def op_input(name, op):
+        """The workload's input for min / max; for products, factors near 1
+        drawn with the workload's size and seed (finite products)."""
+        c = synth.CONFIGS[name]
+        if op != "mul":
+            return synth.config_input(name)
+        return (1.0 + synth.generate(c["n"], "uniform_pm1", c["seed"]) * 1e-3).astype(c["dtype"])
+
+    def op_cfg(cfg, name, cases):
+        """Other operators on a workload's shape: reduces checked in full,
+        scans on 34 sampled outputs evaluated from scratch."""
+        for op, what, pol, q in cases:
+            xn = op_input(name, op)
+            x = torch.from_numpy(xn).to(dev)
+            if what == "reduce":
+                ws = torch.empty(max(canon.reduce_workspace_bytes(xn.size, q, xn.itemsize), 1),
+                                 dtype=torch.uint8, device=dev)
+                out = torch.empty((), dtype=x.dtype, device=dev)
+                canon.reduce_op(x, q, op, 1.0, out=out, ws=ws)
+                ok = same(out.cpu().numpy().reshape(1), [oracle.reduce(xn, q, 1.0, op)])
+                us = timed(lambda: canon.reduce_op(x, q, op, 1.0, out=out, ws=ws))
+                add(cfg, f"reduce op={op} L={q} init=1.0", str(xn.dtype), xn.size, xn.nbytes, us,
+                    ok)
+            else:
+                y = torch.empty_like(x)
+                ws = torch.empty(max(canon.scan_workspace_bytes(xn.size, pol, q, xn.itemsize), 1),
+                                 dtype=torch.uint8, device=dev)
+                canon.scan_op(x, pol, q, op, out=y, ws=ws)
+                ok = canon.workspace_error(ws) == 0
+                idx = np.unique(np.concatenate([[0, 1, xn.size - 1],
+                                                rng.integers(0, xn.size, 31)]))
+                got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
+                ident = canon.IDENTITY[op]
+                want = [oracle.scan_with_init_output(xn, int(k), pol, q, ident, "inclusive", op)
+                        for k in idx]
+                ok = ok and same(got, want)
+                us = timed(lambda: canon.scan_op(x, pol, q, op, out=y, ws=ws))
+                label = pol if pol == "pairwise" else f"{pol}<{q}>"
+                add(cfg, f"scan op={op} {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok)
+            del x
+
+    op_cfg("C3 ops", "reduce_2e28_f64", (("mul", "reduce", None, 128), ("min", "reduce", None, 128),
+                                         ("max", "reduce", None, 128)))
+    op_cfg("C5 ops", "scan_2e27_f64", (("mul", "scan", "block_dyadic", 256),
+                                       ("mul", "scan", "pairwise", 0),
+                                       ("mul", "scan", "iterated_pairwise", 128),
+                                       ("min", "scan", "block_dyadic", 256),
+                                       ("max", "scan", "iterated_pairwise", 128)))
 
     print("| config | op | dtype | N | us | GB/s | % of 8 TB/s | elements/s | bit-exact |")
     print("|---|---|---|---|---|---|---|---|---|")

@@ -52,28 +52,14 @@ struct OpMul {
     template <typename B>
     static __host__ __device__ __forceinline__ B identity() { return B(1.0); }
 };
-// minimum / maximum written as selects (no branches inside the unrolled
-// networks): equal operands (also +0.0 and -0.0) give the OR (minimum) or
-// AND (maximum) of their bits, i.e. the operand itself or -0.0 / +0.0.
-template <typename B>
-__host__ __device__ __forceinline__ B bits_or(B a, B b)
-{
-    using U = typename std::conditional<sizeof(B) == 8, uint64_t, uint32_t>::type;
-    return __builtin_bit_cast(B, (U)(__builtin_bit_cast(U, a) | __builtin_bit_cast(U, b)));
-}
-template <typename B>
-__host__ __device__ __forceinline__ B bits_and(B a, B b)
-{
-    using U = typename std::conditional<sizeof(B) == 8, uint64_t, uint32_t>::type;
-    return __builtin_bit_cast(B, (U)(__builtin_bit_cast(U, a) & __builtin_bit_cast(U, b)));
-}
+// minimum / maximum: the compiler's IEEE 754-2019 minimum / maximum (one
+// v_minimum3_f32 / v_maximum3_f32 on gfx950; v_min_f64 / v_max_f64 with the
+// NaN case selected in double).
 struct OpMin {
     template <typename B>
     static __host__ __device__ __forceinline__ B f(B a, B b)
     {
-        const B m = a < b ? a : b;
-        const B r = a == b ? bits_or(a, b) : m;
-        return (a != a || b != b) ? a + b : r;
+        return __builtin_elementwise_minimum(a, b);
     }
     template <typename B>
     static __host__ __device__ __forceinline__ B identity() { return B(__builtin_inf()); }
@@ -82,9 +68,7 @@ struct OpMax {
     template <typename B>
     static __host__ __device__ __forceinline__ B f(B a, B b)
     {
-        const B m = a > b ? a : b;
-        const B r = a == b ? bits_and(a, b) : m;
-        return (a != a || b != b) ? a + b : r;
+        return __builtin_elementwise_maximum(a, b);
     }
     template <typename B>
     static __host__ __device__ __forceinline__ B identity() { return B(-__builtin_inf()); }
@@ -100,6 +84,10 @@ __host__ __device__ __forceinline__ OpVal<B, Op> operator+(OpVal<B, Op> a, OpVal
     return OpVal<B, Op>{Op::template f<B>(a.v, b.v)};
 }
 template <typename B, class Op> struct Elem<OpVal<B, Op>> : Elem<B> {};
+
+// T is an OpVal wrapper (an operator other than addition).
+template <typename T>
+constexpr bool kIsOpVal = !std::is_same<T, typename Elem<T>::base_t>::value;
 
 // The absent value of T's operator.
 template <typename T> struct Absent {

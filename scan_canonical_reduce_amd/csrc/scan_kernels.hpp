@@ -288,7 +288,8 @@ struct FullTile {
     // aligned f64 pairwise: hold the two tiles in at most 168 VGPRs (3 waves
     // per SIMD), which they fit without spilling (measured 2-10% faster;
     // float pairwise is there without the bound, and slower with it)
-    static constexpr int kMinWavesPerEu = (MODE == 0 && ALIGNED && sizeof(T) == 8) ? 3 : 1;
+    static constexpr int kMinWavesPerEu =
+        (MODE == 0 && ALIGNED && sizeof(T) == 8 && !kIsOpVal<T>) ? 3 : 1;
 
     static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
     {
@@ -595,7 +596,7 @@ struct WideTile {
     static_assert(VLOG >= 0 && VLOG <= LOGV, "blocks of whole vectors inside one wave");
     // f64: two tiles held in at most 168 VGPRs (3 waves per SIMD), a few
     // values spilled; measured 2% faster at B = 256 (f32: no change)
-    static constexpr int kMinWavesPerEu = sizeof(T) == 8 ? 3 : 1;
+    static constexpr int kMinWavesPerEu = (sizeof(T) == 8 && !kIsOpVal<T>) ? 3 : 1;
     struct State {
         ST st;
         T p;     // lane j < 2^NBW_LOG: pairwise value of the blocks up to block j of this wave

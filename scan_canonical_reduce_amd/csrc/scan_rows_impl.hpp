@@ -120,12 +120,17 @@ hipError_t launch_scan_rows(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64
     }
     if (pairwise || b_log == 0)
         return launch_scan_rows_m<T, 0, PLAIN>(x, ldx, y, ldy, rows, cols, 0, aligned, out, s);
-    if constexpr (PW_ONLY) return hipErrorInvalidValue;
-    if constexpr (Elem<T>::LOGE >= 2) {
-        if (b_log < Elem<T>::LOGE)
-            return launch_scan_rows_m<T, 2, PLAIN>(x, ldx, y, ldy, rows, cols, b_log, aligned, out, s);
+    if constexpr (PW_ONLY) {
+        return hipErrorInvalidValue;
+    } else {
+        if constexpr (Elem<T>::LOGE >= 2) {
+            if (b_log < Elem<T>::LOGE)
+                return launch_scan_rows_m<T, 2, PLAIN>(x, ldx, y, ldy, rows, cols, b_log, aligned,
+                                                       out, s);
+        }
+        return launch_scan_rows_m<T, 1, PLAIN>(x, ldx, y, ldy, rows, cols, b_log, aligned, out,
+                                               s);
     }
-    return launch_scan_rows_m<T, 1, PLAIN>(x, ldx, y, ldy, rows, cols, b_log, aligned, out, s);
 }
 
 }  // namespace canon
