@@ -138,6 +138,33 @@ __device__ __forceinline__ void store_vec(T* p, const T (&v)[Elem<T>::E])
     __builtin_nontemporal_store(x, reinterpret_cast<V*>(p));
 }
 
+// 16 bytes from / to LDS in one access (element e of lane l at l * E + e:
+// one element at a time would hit the same banks from neighbouring lanes).
+template <typename T>
+__device__ __forceinline__ void lds_load_vec(const T* p, T (&v)[Elem<T>::E])
+{
+    using V = typename Elem<T>::vec_t;
+    const V x = *reinterpret_cast<const V*>(p);
+#pragma unroll
+    for (int e = 0; e < Elem<T>::E; ++e) {
+        const typename Elem<T>::base_t b = x[e];
+        v[e] = __builtin_bit_cast(T, b);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_store_vec(T* p, const T (&v)[Elem<T>::E])
+{
+    using V = typename Elem<T>::vec_t;
+    V x;
+#pragma unroll
+    for (int e = 0; e < Elem<T>::E; ++e) {
+        const typename Elem<T>::base_t b = __builtin_bit_cast(typename Elem<T>::base_t, v[e]);
+        x[e] = b;
+    }
+    *reinterpret_cast<V*>(p) = x;
+}
+
 // ------------------------------------------------------- wave64 lane moves
 // ds_swizzle in bit mode: source lane = ((lane & AND) | OR) ^ XOR within each
 // group of 32 lanes.  PAT = AND | OR << 5 | XOR << 10.

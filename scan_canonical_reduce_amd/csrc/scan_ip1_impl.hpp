@@ -76,8 +76,8 @@ template <typename T, int LOGRV>
 struct Ip1Shared {
     static constexpr int L = IpFast<T, LOGRV>::L;
     static constexpr int STAGE = L > kIp1Stage ? L : kIp1Stage;
-    T row[4][L];  // per-wave rows exchanged between the waves
-    T h[STAGE];   // node values of the earlier tiles, a batch at a time
+    alignas(16) T row[4][L];  // per-wave rows exchanged between the waves
+    alignas(16) T h[STAGE];   // node values of the earlier tiles, a batch at a time
     uint32_t ticket;
 };
 
@@ -146,17 +146,17 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
 
     ipf_columns_in_wave<T, LOGRV>(a);
 #pragma unroll
-    for (int q = 0; q < RV; ++q)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            c.sh->row[w][(q * 64 + lane) * E + e] = a[(RW - 1) * RV + q][e];
+    for (int q = 0; q < RV; ++q) lds_store_vec(&c.sh->row[w][(q * 64 + lane) * E], a[(RW - 1) * RV + q]);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < RV; ++q)
+    for (int q = 0; q < RV; ++q) {
+        T r0[E], r1[E], r2[E];
+        lds_load_vec(&c.sh->row[0][(q * 64 + lane) * E], r0);
+        lds_load_vec(&c.sh->row[1][(q * 64 + lane) * E], r1);
+        lds_load_vec(&c.sh->row[2][(q * 64 + lane) * E], r2);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const int j = (q * 64 + lane) * E + e;
-            const T t0 = c.sh->row[0][j], t1 = c.sh->row[1][j], t2 = c.sh->row[2][j];
+            const T t0 = r0[e], t1 = r1[e], t2 = r2[e];
             if (w & 1) {
                 const T v = (w & 2) ? t2 : t0;
 #pragma unroll
@@ -168,6 +168,7 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
                 for (int r = 0; r < RW; ++r) a[r * RV + q][e] = v + a[r * RV + q][e];
             }
         }
+    }
     __syncthreads();  // every wave has read row[]
 
     if (w == 3) {
@@ -268,29 +269,26 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         __syncthreads();
         for (int m = 0; m < nb; ++m) {
 #pragma unroll
-            for (int q = 0; q < RV; ++q)
+            for (int q = 0; q < RV; ++q) {
+                T hv[E];
+                lds_load_vec(&c.sh->h[m * F::L + (q * 64 + lane) * E], hv);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const T hv = c.sh->h[m * F::L + (q * 64 + lane) * E + e];
 #pragma unroll
-                    for (int r = 0; r < RW; ++r) a[r * RV + q][e] = hv + a[r * RV + q][e];
-                    b[q][e] = hv + b[q][e];
+                    for (int r = 0; r < RW; ++r) a[r * RV + q][e] = hv[e] + a[r * RV + q][e];
+                    b[q][e] = hv[e] + b[q][e];
                 }
+            }
         }
         __syncthreads();  // h is refilled by the next batch
     }
     // the B row of each wave's first row: the A row just above it
 #pragma unroll
-    for (int q = 0; q < RV; ++q)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            c.sh->row[w][(q * 64 + lane) * E + e] = a[(RW - 1) * RV + q][e];
+    for (int q = 0; q < RV; ++q) lds_store_vec(&c.sh->row[w][(q * 64 + lane) * E], a[(RW - 1) * RV + q]);
     __syncthreads();
     if (w > 0) {
 #pragma unroll
-        for (int q = 0; q < RV; ++q)
-#pragma unroll
-            for (int e = 0; e < E; ++e) b[q][e] = c.sh->row[w - 1][(q * 64 + lane) * E + e];
+        for (int q = 0; q < RV; ++q) lds_load_vec(&c.sh->row[w - 1][(q * 64 + lane) * E], b[q]);
     }
     __syncthreads();  // row[] is rewritten by the next front
 
