@@ -87,12 +87,12 @@ canon_status_t reduce_impl(const T* x, size_t n, uint32_t L, T init, T* out, voi
     if (out == nullptr || L == 0 || (n > 0 && x == nullptr)) return CANON_EINVAL;
     if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
     const ReducePlan pl =
-        plan_reduce(n, L, sizeof(T), !is_op_v<T> && aligned16(x), kReduceTargetWG);
+        plan_reduce(n, L, sizeof(T), aligned16(x), kReduceTargetWG);
     // the documented size (covers either plan), so that a caller who sizes by
     // canon_reduce_workspace_bytes is never rejected and never overrun
     if (canon_status_t s = check_ws(ws, ws_bytes, reduce_ws(n, L, sizeof(T)))) return s;
-    return hip_status(launch_reduce<T, !is_op_v<T>>(x, n, L, init, out, static_cast<T*>(ws), pl,
-                                                    static_cast<hipStream_t>(stream)));
+    return hip_status(launch_reduce<T>(x, n, L, init, out, static_cast<T*>(ws), pl,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 template <typename T>

@@ -1,8 +1,8 @@
 // Explicit instantiations of the launchers for one value type V (an
 // OpVal<B, Op>: the kernels with the operator Op in place of addition).
 // Only the kernels that the operator entry points reach are built: the
-// general reduce streaming kernel, and the scans with an output stage (for
-// an order-free operator, minimum or maximum, the pairwise scans only).
+// reduce kernels, and the scans with an output stage (for an order-free
+// operator, minimum or maximum, the pairwise scans only).
 #pragma once
 
 #include "reduce_impl.hpp"
@@ -13,8 +13,8 @@
 #include "scan_with_init_impl.hpp"
 
 #define CANON_INSTANTIATE_OP(V)                                                                  \
-    template hipError_t launch_reduce<V, false>(const V*, uint64_t, uint32_t, V, V*, V*,          \
-                                                const ReducePlan&, hipStream_t);                   \
+    template hipError_t launch_reduce<V, true>(const V*, uint64_t, uint32_t, V, V*, V*,           \
+                                               const ReducePlan&, hipStream_t);                    \
     template hipError_t launch_reduce_rows<V>(const V*, uint64_t, uint64_t, uint64_t, uint32_t, V, \
                                               V*, hipStream_t);                                    \
     template hipError_t launch_put_column<V>(V*, uint64_t, uint64_t, V, hipStream_t);             \
@@ -37,8 +37,8 @@
 // Minimum and maximum: every parenthesisation gives the same value, so one
 // scan kernel (pairwise) serves every policy.
 #define CANON_INSTANTIATE_ORDER_FREE_OP(V)                                                       \
-    template hipError_t launch_reduce<V, false>(const V*, uint64_t, uint32_t, V, V*, V*,          \
-                                                const ReducePlan&, hipStream_t);                   \
+    template hipError_t launch_reduce<V, true>(const V*, uint64_t, uint32_t, V, V*, V*,           \
+                                               const ReducePlan&, hipStream_t);                    \
     template hipError_t launch_reduce_rows<V>(const V*, uint64_t, uint64_t, uint64_t, uint32_t, V, \
                                               V*, hipStream_t);                                    \
     template hipError_t launch_put_column<V>(V*, uint64_t, uint64_t, V, hipStream_t);             \
