@@ -211,6 +211,66 @@ __device__ __forceinline__ OpVal<B, Op> readlane(OpVal<B, Op> v, int lane)
     return OpVal<B, Op>{readlane(v.v, lane)};
 }
 
+// One 32-bit lane move through DPP (the source operand of a VALU move read
+// from another lane of the same row of 16): lanes outside the row and bank
+// masks keep `old`.
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, BANKS, false);
+}
+
+// Apply a 32-bit lane move to each half of a 64-bit value, or to a 32-bit one.
+template <typename T, typename F>
+__device__ __forceinline__ T per_dword(T v, T old, F f)
+{
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, v), o = __builtin_bit_cast(uint64_t, old);
+        const uint32_t lo = f((uint32_t)o, (uint32_t)b);
+        const uint32_t hi = f((uint32_t)(o >> 32), (uint32_t)(b >> 32));
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    } else {
+        return __builtin_bit_cast(T, f(__builtin_bit_cast(uint32_t, old), __builtin_bit_cast(uint32_t, v)));
+    }
+}
+
+// The 32-bit value held by lane (lane ^ MASK), MASK a power of two below 64,
+// without an LDS round trip: DPP quad permutations for 1 and 2, two
+// bank-masked row shifts for 4 and 8, the gfx950 lane-swap instructions
+// (v_permlane16_swap / v_permlane32_swap) for 16 and 32.
+template <int MASK>
+__device__ __forceinline__ uint32_t xor32(uint32_t v)
+{
+    if constexpr (MASK == 1) {
+        return dpp32<0xB1>(0u, v);  // quad_perm [1,0,3,2]
+    } else if constexpr (MASK == 2) {
+        return dpp32<0x4E>(0u, v);  // quad_perm [2,3,0,1]
+    } else if constexpr (MASK == 4) {
+        // lanes with bit 2 clear read lane + 4 (row_shl:4), the others lane - 4
+        return dpp32<0x114, 0xF, 0xA>(dpp32<0x104, 0xF, 0x5>(0u, v), v);
+    } else if constexpr (MASK == 8) {
+        return dpp32<0x118, 0xF, 0xC>(dpp32<0x108, 0xF, 0x3>(0u, v), v);
+    } else if constexpr (MASK == 16) {
+        // swap of rows 1, 3 of the first operand with rows 0, 2 of the second
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (__lane_id() & 16) ? r[0] : r[1];
+    } else {
+        // swap of the upper half of the first operand with the lower half of the second
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (__lane_id() & 32) ? r[0] : r[1];
+    }
+}
+
+// Value of `v` held by lane (lane ^ MASK) through xor32 (VALU lane moves;
+// shfl_xor below goes through the LDS crossbar and keeps fewer registers
+// live, which the kernels held to a fixed occupancy rely on).
+template <int MASK, typename T>
+__device__ __forceinline__ T shfl_xor_valu(T v)
+{
+    static_assert(MASK > 0 && MASK < 64 && (MASK & (MASK - 1)) == 0, "xor mask");
+    return per_dword(v, v, [](uint32_t, uint32_t x) { return xor32<MASK>(x); });
+}
+
 // Value of `v` held by lane (lane ^ MASK), MASK a power of two below 64.
 template <int MASK, typename T>
 __device__ __forceinline__ T shfl_xor(T v)

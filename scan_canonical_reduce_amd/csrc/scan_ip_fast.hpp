@@ -28,11 +28,12 @@ struct IpFast {
     static constexpr int L = 64 * E * RV;
 };
 
-// butterfly partner value of `v` held by lane ^ 2^K
+// butterfly partner value of `v` held by lane ^ 2^K (VALU lane moves: the
+// row trees are a chain of six dependent exchanges per row)
 template <int K, typename T>
 __device__ __forceinline__ T xor_lane(T v)
 {
-    return shfl_xor<(1 << K)>(v);
+    return shfl_xor_valu<(1 << K)>(v);
 }
 
 template <typename T, int LOGRV, bool GUARD>
