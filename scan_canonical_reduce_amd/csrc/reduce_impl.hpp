@@ -403,6 +403,94 @@ __global__ __launch_bounds__(kRowsThreads) void k_reduce_rows(const T* __restric
 }
 
 // ============================================================================
+// Row-batched reduce, register path: L = 2^LOGL with a row of L at most one
+// wave-wide load (L <= 64 E), 16-byte aligned rows, at most
+// 2^kRowsStackDepth batches per row.  One wave per row: the wave walks the
+// row's batches in order (pow2_batch, as the streaming kernel) with a
+// binary-counter stack, which leaves the row's L lane values in lanes
+// 0 .. CW-1 (VE each); the complete tree over the lanes is taken in the
+// thread and then across those lanes, and init is added on the left.
+// ============================================================================
+constexpr int kRowsStackDepth = 6;
+
+template <typename T, int LOGL>
+__global__ __launch_bounds__(kRowsThreads) void k_reduce_rows_pow2(const T* __restrict__ x,
+                                                                   uint64_t rows, uint64_t cols,
+                                                                   uint64_t ldx, T init,
+                                                                   T* __restrict__ out)
+{
+    using GM = Pow2Geom<T, LOGL>;
+    static_assert(GM::LOGC <= 6, "a row of L fits one wave-wide load");
+    constexpr int VE = GM::VE;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & (GM::CW - 1), g = lane >> GM::LOG_CW;
+    const uint64_t waves = (uint64_t)gridDim.x * (kRowsThreads / 64);
+    const uint64_t msr = (cols + (1ull << GM::LOG_SR) - 1) >> GM::LOG_SR;
+    const uint64_t nb = (msr + GM::GU - 1) / GM::GU;
+    const uint64_t nfull = ((cols >> GM::LOG_SR) / GM::GU) < nb ? (cols >> GM::LOG_SR) / GM::GU : nb;
+    for (uint64_t row = (uint64_t)blockIdx.x * (kRowsThreads / 64) + (threadIdx.x >> 6); row < rows;
+         row += waves) {
+        const T* xr = x + row * ldx;
+        TreeStack<T, VE, kRowsStackDepth> st;
+        T v[VE];
+        for (uint64_t k = 0; k < nfull; ++k) {
+            pow2_batch<T, LOGL, false>(xr, cols, k * GM::GU, 0, c, g, v);
+            st.push(k, v);
+        }
+        for (uint64_t k = nfull; k < nb; ++k) {
+            pow2_batch<T, LOGL, true>(xr, cols, k * GM::GU, 0, c, g, v);
+            st.push(k, v);
+        }
+        st.collapse(nb, v);
+        // lanes c * VE + i: the tree over the thread's VE lanes, then across
+        // the CW threads holding the row's lanes (lower lanes on the left)
+#pragma unroll
+        for (int h = 1; h < VE; h *= 2)
+#pragma unroll
+            for (int i = 0; i < VE; i += 2 * h) v[i] = v[i] + v[i + h];
+        T r = v[0];
+#pragma unroll
+        for (int k = 0; k < GM::LOG_CW; ++k) {
+            T o;
+            switch (k) {
+                case 0: o = shfl_xor<1>(r); break;
+                case 1: o = shfl_xor<2>(r); break;
+                case 2: o = shfl_xor<4>(r); break;
+                case 3: o = shfl_xor<8>(r); break;
+                case 4: o = shfl_xor<16>(r); break;
+                default: o = shfl_xor<32>(r); break;
+            }
+            r = ((lane >> k) & 1) ? (o + r) : (r + o);
+        }
+        if (lane == 0) out[row] = (cols == 0) ? init : init + r;
+    }
+}
+
+template <typename T, int LOGL>
+static hipError_t launch_rows_pow2(const T* x, uint64_t rows, uint64_t cols, uint64_t ldx, T init,
+                                   T* out, hipStream_t s)
+{
+    constexpr int RPB = kRowsThreads / 64;  // rows per workgroup
+    uint64_t grid = (rows + RPB - 1) / RPB;
+    if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
+    hipLaunchKernelGGL((k_reduce_rows_pow2<T, LOGL>), dim3((unsigned)grid), dim3(kRowsThreads), 0,
+                       s, x, rows, cols, ldx, init, out);
+    return hipGetLastError();
+}
+
+template <typename T, int LOGL>
+static hipError_t launch_rows_pow2_dispatch(int logl, const T* x, uint64_t rows, uint64_t cols,
+                                            uint64_t ldx, T init, T* out, hipStream_t s)
+{
+    if constexpr (LOGL > Elem<T>::LOGE + 6) {
+        return hipErrorInvalidValue;
+    } else {
+        if (logl == LOGL) return launch_rows_pow2<T, LOGL>(x, rows, cols, ldx, init, out, s);
+        return launch_rows_pow2_dispatch<T, LOGL + 1>(logl, x, rows, cols, ldx, init, out, s);
+    }
+}
+
+// ============================================================================
 // Host-side launchers (called from api.cpp).
 // ============================================================================
 template <typename T, int LOGL>
@@ -455,6 +543,13 @@ hipError_t launch_reduce_rows(const T* x, uint64_t rows, uint64_t cols, uint64_t
 {
     int lp_log = 0;
     while ((1ull << lp_log) < L) ++lp_log;
+    // register path: power-of-two L of at most one wave-wide load per row of
+    // L, 16-byte aligned rows, and rows short enough for its stack
+    const uint64_t batch_elems = 64ull * kReduceBatch * Elem<T>::E;
+    const bool aligned = ((uintptr_t)x % 16 == 0) && ((ldx * sizeof(T)) % 16 == 0);
+    if ((1ull << lp_log) == L && lp_log <= Elem<T>::LOGE + 6 && aligned &&
+        cols <= (batch_elems << kRowsStackDepth))
+        return launch_rows_pow2_dispatch<T, 0>(lp_log, x, rows, cols, ldx, init, out, s);
     int lw_log = lp_log < 8 ? lp_log : 8;
     constexpr auto kern = k_reduce_rows<T>;
     // one workgroup per row (the kernel strides over rows past the grid limit)

@@ -112,6 +112,37 @@ def test_reduce_rows(canon, dtype, L):
         assert_bit_exact(got, want, f"cols={cols}")
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [1, 2, 4, 16, 64, 128, 256])
+def test_reduce_rows_aligned(canon, dtype, L):
+    """16-byte aligned rows and a power-of-two L: the one-wave-per-row
+    register kernel (for L up to one wave-wide load per row of L), ragged
+    row ends, a row count that is not a multiple of the rows per workgroup."""
+    rows, ld = 37, 5008
+    X = synth.generate(rows * ld, "mixed_magnitude", 40 + L, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for cols in (0, 1, L - 1, L, L + 1, 1023, 1024, 1025, 2049, 4096, 5000, 5008):
+        if cols < 0:
+            continue
+        got = to_host(canon.reduce_rows(Xd[:, :cols], L, 0.1))
+        want = oracle.reduce_rows(X, L, 0.1, cols=cols)
+        assert_bit_exact(got, want, f"cols={cols}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_reduce_rows_long_rows(canon, dtype):
+    """Rows around the register kernel's length limit (64 batches of one
+    wave each) and past it (the general row kernel)."""
+    e = 2 if dtype == np.float64 else 4
+    limit = 64 * 8 * e * 64
+    rows, ld = 5, limit + 16
+    X = synth.generate(rows * ld, "mixed_magnitude", 47, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for cols in (limit - 1, limit, limit + 1, ld):
+        got = to_host(canon.reduce_rows(Xd[:, :cols], 16, -2.5))
+        assert_bit_exact(got, oracle.reduce_rows(X, 16, -2.5, cols=cols), f"cols={cols}")
+
+
 def test_reduce_rows_shape_of_workload(canon):
     rows, cols = 2048, 4096
     X = synth.generate(rows * cols, "uniform_pm1", 1004).reshape(rows, cols)
