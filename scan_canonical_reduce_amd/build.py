@@ -1,4 +1,5 @@
-"""Build libcanon.so (HIP for gfx950) in-tree with hipcc.
+"""Build libcanon.so (HIP for gfx950) in-tree with hipcc, and the test
+library of a caller-defined operator (tests/user_op).
 
 Usage: python -m scan_canonical_reduce_amd.build
 """
@@ -45,11 +46,33 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Libraries built from canon_user_op.hpp with a caller-defined operator:
+# (source, output), relative to the repository root.  The skew operator is
+# the one the GPU tests of caller-defined operators load.
+ROOT = os.path.dirname(HERE)
+USER_OP_LIBS = [("tests/user_op/skew_op.hip", "tests/user_op/libcanon_skew.so")]
+
+
+def _build_user_op(pair) -> str:
+    src, out = (os.path.join(ROOT, p) for p in pair)
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), *HIPFLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC, src,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        user = [ex.submit(_build_user_op, p) for p in USER_OP_LIBS]  # longest first
         objs = list(ex.map(_compile, srcs))
+        for f in user:
+            f.result()
     tmp = OUT + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -152,3 +152,21 @@ def test_binding_refuses_cpu_tensors(canon):
         canon.scan(x, "pairwise")
     with pytest.raises(TypeError):
         canon._sfx(torch.zeros(2, dtype=torch.int32))
+
+
+USER_OP_LIB = os.path.join(ROOT, "tests", "user_op", "libcanon_skew.so")
+
+
+@pytest.mark.skipif(not os.path.exists(USER_OP_LIB),
+                    reason="the caller-defined-operator library is built by build()")
+def test_user_op_library_exports():
+    """CANON_USER_OP defines the entry points its header documents."""
+    text = open(os.path.join(ROOT, "include", "canon_user_op.hpp")).read()
+    documented = set(re.findall(r"\bprefix_([A-Za-z_0-9]+)\(", text))
+    assert {"reduce_T", "reduce_rows_T", "scan_T", "scan_rows_T", "last_hip_error"} <= documented
+    out = os.popen(f"nm -D --defined-only {USER_OP_LIB}").read()
+    names = ["canon_skew_last_hip_error"] + [
+        f"canon_skew_{f}_{t}" for f in ("reduce", "reduce_rows", "scan", "scan_rows")
+        for t in ("f64", "f32")]
+    for name in names:
+        assert re.search(rf"\bT {name}\b", out), name
