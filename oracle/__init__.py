@@ -34,8 +34,10 @@ _SRC = [os.path.join(_HERE, "canon_oracle.c"), os.path.join(_HERE, "canon_oracle
 POLICIES = {"pairwise": 0, "iterated_pairwise": 1, "block_dyadic": 2}
 
 # The operators the expression is evaluated with ("add" is +; min and max are
-# IEEE 754-2019 minimum / maximum).
-OPS = ("add", "mul", "min", "max")
+# IEEE 754-2019 minimum / maximum; "skew" is a (+) b = (a + b) + ((a * 0.25)
+# * b) * b, neither commutative nor associative, with -0.0 as its identity:
+# the operator of the caller-defined-operator tests).
+OPS = ("add", "mul", "min", "max", "skew")
 
 # Which prefix each output of a scan with an initial value observes.
 SCAN_KINDS = {"inclusive": 0, "exclusive": 1, "include_initial": 2}

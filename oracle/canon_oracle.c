@@ -67,6 +67,22 @@ static float max_f32(float a, float b)
     return signbit(a) ? b : a;
 }
 
+/* A skewed operator for tests of operand order and parenthesisation:
+ * a (+) b = (a + b) + ((a * 0.25) * b) * b, neither commutative nor
+ * associative; -0.0 is a two-sided identity for finite operands. */
+static double skew_f64(double a, double b)
+{
+    const double s = a + b;
+    const double q = (a * 0.25) * b;
+    return s + q * b;
+}
+static float skew_f32(float a, float b)
+{
+    const float s = a + b;
+    const float q = (a * 0.25f) * b;
+    return s + q * b;
+}
+
 #define T double
 #define SFX f64
 #define OP(a, b) ((a) + (b))
@@ -85,6 +101,12 @@ static float max_f32(float a, float b)
 #undef OP
 #define SFX f64_max
 #define OP(a, b) max_f64((a), (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+
+#define SFX f64_skew
+#define OP(a, b) skew_f64((a), (b))
 #include "canon_oracle_body.h"
 #undef SFX
 #undef OP
@@ -108,6 +130,12 @@ static float max_f32(float a, float b)
 #undef OP
 #define SFX f32_max
 #define OP(a, b) max_f32((a), (b))
+#include "canon_oracle_body.h"
+#undef SFX
+#undef OP
+
+#define SFX f32_skew
+#define OP(a, b) skew_f32((a), (b))
 #include "canon_oracle_body.h"
 #undef SFX
 #undef OP

@@ -128,9 +128,18 @@ def _maximum(a, b):
     return b
 
 
+def _skew(a, b):
+    """a (+) b = (a + b) + ((a * 0.25) * b) * b, each step rounded in the
+    operands' dtype."""
+    t = type(a)
+    s = t(a + b)
+    q = t(t(a * t(0.25)) * b)
+    return t(s + t(q * b))
+
+
 def evaluate(tree, values, init=None, op="add"):
-    """Value of a tree: one application of op ("add", "mul", "min", "max")
-    in values' dtype per internal node."""
+    """Value of a tree: one application of op ("add", "mul", "min", "max",
+    "skew") in values' dtype per internal node."""
     t = values.dtype.type
     if isinstance(tree, str):
         return t(init)
@@ -146,6 +155,8 @@ def evaluate(tree, values, init=None, op="add"):
         return t(_minimum(a, b))
     if op == "max":
         return t(_maximum(a, b))
+    if op == "skew":
+        return _skew(t(a), t(b))
     raise ValueError(op)
 
 

@@ -1,7 +1,9 @@
 """Pins for the oracle with other operators: multiplication, minimum and
 maximum (the canonical expression is defined for any binary operator:
 canonical-reduce README, P4016R0 "Summary"; min and max are read as IEEE
-754-2019 minimum / maximum).
+754-2019 minimum / maximum), and "skew", a (+) b = (a + b) + ((a/4) b) b,
+neither commutative nor associative (the caller-defined-operator tests use
+it: any change of operand order or of parenthesisation changes its values).
 
 Checked against things other than the oracle itself:
   * the independently written symbolic trees evaluated with the operator;
@@ -23,8 +25,8 @@ import synth
 from oracle import symbolic as S
 
 DTYPES = [np.float64, np.float32]
-OPS = ["mul", "min", "max"]
-IDENT = {"add": -0.0, "mul": 1.0, "min": np.inf, "max": -np.inf}
+OPS = ["mul", "min", "max", "skew"]
+IDENT = {"add": -0.0, "mul": 1.0, "min": np.inf, "max": -np.inf, "skew": -0.0}
 POLICIES = [("pairwise", 0), ("block_dyadic", 4), ("iterated_pairwise", 3)]
 
 
@@ -45,9 +47,17 @@ def near_one(n, seed, dtype):
     return (1.0 + u * 1e-3).astype(dtype)
 
 
+def small(n, seed, dtype):
+    """Values in (-1e-3, 1e-3): sums and skew terms stay far from overflow."""
+    return (synth.generate(n, "uniform_pm1", seed) * 1e-3).astype(dtype)
+
+
 def data(op, n, seed, dtype):
-    return near_one(n, seed, dtype) if op == "mul" else synth.generate(
-        n, "mixed_magnitude", seed, dtype)
+    if op == "mul":
+        return near_one(n, seed, dtype)
+    if op == "skew":
+        return small(n, seed, dtype)
+    return synth.generate(n, "mixed_magnitude", seed, dtype)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -158,3 +168,41 @@ def test_mul_init_placement():
         folded = oracle.cr(np.concatenate([[1.0 + 1e-3], x]), 4, "mul")
         diff += not same_bits(got, folded)
     assert diff > 20
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_skew_operator_definition_and_identity(dtype):
+    """One application against the definition written with numpy scalars;
+    -0.0 is a two-sided identity, signed zeros included; the operator is not
+    commutative and not associative on ordinary values."""
+    t = dtype
+    rng = np.random.Generator(np.random.PCG64(75))
+    for a, b in rng.uniform(-3, 3, (200, 2)):
+        a, b = t(a), t(b)
+        want = t(t(a + b) + t(t(t(a * t(0.25)) * b) * b))
+        assert same_bits(oracle.apply(a, b, "skew"), want)
+    vals = [t(0.0), t(-0.0), t(1.5), t(-2.25), t(1e-30), t(3e4)]
+    for v in vals:
+        assert same_bits(oracle.apply(v, t(-0.0), "skew"), v)
+        assert same_bits(oracle.apply(t(-0.0), v, "skew"), v)
+    a, b, c = t(0.5), t(0.25), t(-0.75)
+    assert not same_bits(oracle.apply(a, b, "skew"), oracle.apply(b, a, "skew"))
+    ab_c = oracle.apply(oracle.apply(a, b, "skew"), c, "skew")
+    a_bc = oracle.apply(a, oracle.apply(b, c, "skew"), "skew")
+    assert not same_bits(ab_c, a_bc)
+
+
+def _swapped(tree):
+    return tree if isinstance(tree, (int, str)) else (_swapped(tree[1]), _swapped(tree[0]))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("policy,param", POLICIES)
+def test_skew_sees_operand_order(dtype, policy, param):
+    """Evaluating the mirrored trees gives other bits for most prefixes, so a
+    kernel that swaps operands anywhere cannot match the oracle with skew."""
+    x = small(64, 76, dtype)
+    y = oracle.scan(x, policy, param, "skew")
+    differ = sum(not same_bits(y[i], S.evaluate(_swapped(S.scan_tree(i, policy, param)), x,
+                                                op="skew")) for i in range(1, 64))
+    assert differ > 40
