@@ -674,10 +674,15 @@ struct WideTile {
             const T cj = j == 0 ? cw : readlane(p, j - 1);
 #pragma unroll
             for (int e = 0; e < E - 1; ++e) o[e] = cj + s.st.v[u][e];
-            if ((u + 1) % VPB == 0)
-                o[E - 1] = c.lane == 63 ? readlane(p, j) : cj + s.st.v[u][E - 1];
-            else
+            if ((u + 1) % VPB == 0) {
+                // read in every lane, outside the lane-63 select (compiled
+                // inside the branch that lane 63 alone takes, the read gave
+                // wrong values for a caller-defined operator)
+                const T pj = readlane(p, j);
+                o[E - 1] = c.lane == 63 ? pj : cj + s.st.v[u][E - 1];
+            } else {
                 o[E - 1] = cj + s.st.v[u][E - 1];
+            }
         };
         if constexpr (OUTX) {
             // the element before the wave's first one ends the previous
