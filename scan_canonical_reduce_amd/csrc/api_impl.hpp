@@ -28,7 +28,8 @@ inline constexpr bool is_op_v = !std::is_same<V, typename Elem<V>::base_t>::valu
 
 // Minimum and maximum are associative and commutative with the semantics of
 // device.hpp (NaN payloads aside), so every policy's expression has the same
-// value: their scans run the pairwise kernels whatever the policy.
+// value: their scans run one kernel (launch_scan_order_free) whatever the
+// policy.
 template <typename V>
 inline constexpr bool is_order_free_v =
     std::is_same<V, OpVal<typename Elem<V>::base_t, OpMin>>::value ||
@@ -173,8 +174,8 @@ inline size_t scan_ws(uint64_t n, int policy, uint32_t param, size_t es)
 {
     if (check_policy(policy, param) != CANON_OK || (es != 4 && es != 8) || n == 0) return 0;
     if (is_ip(policy, param)) {
-        // also enough for the pairwise layout (the order-free operators run
-        // the pairwise scan whatever the policy)
+        // also enough for the tile layout (the order-free operators run one
+        // single-pass scan whatever the policy)
         const size_t a = ip_ws(1, n, param, es);
         const ScanLayout p = es == 8 ? scan_layout<double>(n, CANON_PAIRWISE, 0)
                                      : scan_layout<float>(n, CANON_PAIRWISE, 0);
@@ -213,8 +214,8 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
         if (lay.ntiles > 0xFFFFFFFFull) return CANON_EUNSUPPORTED;
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
             return s;
-        return hip_status(launch_scan_pw_with_init<T>(x, y, n, aligned16(x) && aligned16(y),
-                                                      static_cast<uint64_t*>(ws), lay, *out, st));
+        return hip_status(launch_scan_order_free<T>(x, y, n, aligned16(x) && aligned16(y),
+                                                    static_cast<uint64_t*>(ws), lay, *out, st));
     } else if (is_ip(policy, param)) {
         const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), aligned16(x) && aligned16(y));
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))

@@ -91,8 +91,8 @@ hipError_t launch_scan_with_init(const T* x, T* y, uint64_t n, bool pairwise, in
                                  const ScanOut<T>& out, hipStream_t s);
 
 template <typename T>
-hipError_t launch_scan_pw_with_init(const T* x, T* y, uint64_t n, bool aligned, uint64_t* ws,
-                                    const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s);
+hipError_t launch_scan_order_free(const T* x, T* y, uint64_t n, bool aligned, uint64_t* ws,
+                                  const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s);
 
 // y[r * ldy] = v for r < rows, on stream s.
 template <typename T>

@@ -36,11 +36,13 @@ hipError_t launch_scan_with_init(const T* x, T* y, uint64_t n, bool pairwise, in
     return launch_scan_impl<T, true>(x, y, n, pairwise, b_log, aligned, ws, lay, out, s);
 }
 
-// The pairwise policy only (for operators whose every parenthesisation gives
-// the same value, which any policy's scan therefore equals).
+// For operators whose every parenthesisation gives the same value (minimum,
+// maximum), so that every policy's scan equals every other's: the
+// block_dyadic tiles with blocks of one wave-wide vector, which apply the
+// operator fewer times per element than the pairwise tiles.
 template <typename T>
-hipError_t launch_scan_pw_with_init(const T* x, T* y, uint64_t n, bool aligned, uint64_t* ws,
-                                    const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s)
+hipError_t launch_scan_order_free(const T* x, T* y, uint64_t n, bool aligned, uint64_t* ws,
+                                  const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s)
 {
     if (n == 0)
         return out.kind == kScanIncludeInitial ? launch_put_column(y, 1, 1, out.init, s)
@@ -51,7 +53,11 @@ hipError_t launch_scan_pw_with_init(const T* x, T* y, uint64_t n, bool aligned, 
                        lay.total_words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_full<T, 0, true>(x, y, n, 0, aligned, ws, lay, out, s);
+    constexpr int LOGV = scan_log_v<T>();
+    constexpr int b_log = Elem<T>::LOGE + 6;
+    if (aligned)
+        return launch_k<WideTile<T, true, LOGV, 0, true>>(x, y, n, b_log, ws, lay, 0, out, s);
+    return launch_k<WideTile<T, false, LOGV, 0, true>>(x, y, n, b_log, ws, lay, 0, out, s);
 }
 
 }  // namespace canon
