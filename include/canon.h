@@ -89,7 +89,9 @@ typedef enum {
  * the canonical expression is defined for any operator).  Absent values
  * (lanes without an element, padding) take the operator's exact identity:
  * -0.0, 1.0, +inf, -inf.  MIN and MAX are IEEE 754-2019 minimum and maximum:
- * NaN if either operand is NaN, -0.0 below +0.0. */
+ * NaN if either operand is NaN, -0.0 below +0.0.  Other operators
+ * (non-commutative ones included) are compiled into the caller's own library
+ * through canon_user_op.hpp. */
 typedef enum {
     CANON_OP_ADD = 0,
     CANON_OP_MUL = 1,
