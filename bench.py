@@ -108,7 +108,7 @@ def log(*a):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU (no collectives); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
