@@ -74,3 +74,22 @@ def test_reduce_and_scans_past_2_32_elements(canon, dtype):
     del ws
     canon.scan_with_init(x, "block_dyadic", 256, "exclusive", 0.5, out=y)
     check(y, 0.5, 1, "exclusive init 0.5")
+
+
+def test_rows_past_2_32_elements(canon):
+    """Row reduce and row scan over more than 2^32 elements in all (rows of
+    7 * 586 doubles, so every row holds the same exact pattern)."""
+    cols = 7 * 586
+    rows = (1 << 32) // cols + 2
+    X = torch.empty(rows, cols, dtype=torch.float64, device="cuda")
+    row = (torch.arange(cols, dtype=torch.int64, device="cuda") % 7 - 3).to(torch.float64)
+    X[:] = row
+    assert X.numel() > (1 << 32)
+    total = float(prefix(torch.tensor(cols - 1)).item())
+    r = canon.reduce_rows(X, 16, 0.5)
+    assert bool((r == total + 0.5).all()), "row reduce"
+    Y = canon.scan_rows(X, "block_dyadic", 16)
+    want = prefix(torch.arange(cols, dtype=torch.int64, device="cuda")).to(torch.float64)
+    for r0 in range(0, rows, 1 << 16):
+        assert torch.equal(Y[r0:r0 + (1 << 16)].view(torch.int64),
+                           want.expand(min(1 << 16, rows - r0), cols).view(torch.int64)), r0
