@@ -217,14 +217,17 @@ canon_status_t scan_impl(const T* x, T* y, size_t n, int policy, uint32_t param,
         return hip_status(launch_scan_order_free<T>(x, y, n, aligned16(x) && aligned16(y),
                                                     static_cast<uint64_t*>(ws), lay, *out, st));
     } else if (is_ip(policy, param)) {
-        const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), aligned16(x) && aligned16(y));
+        const bool al = aligned16(x) && aligned16(y);
         if (canon_status_t s = check_ws(ws, ws_bytes, scan_ws(n, policy, param, sizeof(T))))
             return s;
-        if (ip_single(ip)) {
-            if (!ip_fits(ip)) return CANON_EUNSUPPORTED;
+        // the register geometry runs in one pass at any alignment
+        const IpLayout reg = make_ip_layout(1, n, param, sizeof(T), true);
+        if (ip_single(reg) && ip_fits(reg))
             return hip_status(launch_scan_ip_single<T, !is_op_v<T>>(
-                x, n, y, n, n, static_cast<uint64_t*>(ws), make_ip_single_layout(ip), out, st));
-        }
+                x, n, y, n, n, static_cast<uint64_t*>(ws), make_ip_single_layout(reg), out, al,
+                st));
+        const IpLayout ip = make_ip_layout(1, n, param, sizeof(T), al);
+        if (ip_single(ip)) return CANON_EUNSUPPORTED;  // too many tiles for one launch
         return hip_status(launch_scan_ip<T, !is_op_v<T>>(x, n, y, n, 1, n,
                                                          static_cast<uint32_t*>(ws),
                                                          ip_nodes<T>(ws), ip, out, st));
@@ -268,16 +271,17 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
     } else if (is_ip(policy, param)) {
         const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                         (ldy * sizeof(T)) % 16 == 0;
-        const IpLayout ip = make_ip_layout(rows, cols, param, sizeof(T), al);
         if (canon_status_t s =
                 check_ws(ws, ws_bytes, scan_rows_ws(rows, cols, policy, param, sizeof(T))))
             return s;
-        if (ip_single(ip)) {
-            if (!ip_fits(ip)) return CANON_EUNSUPPORTED;
+        // the register geometry runs in one pass at any alignment
+        const IpLayout reg = make_ip_layout(rows, cols, param, sizeof(T), true);
+        if (ip_single(reg) && ip_fits(reg))
             return hip_status(launch_scan_ip_single<T, !is_op_v<T>>(
-                x, ldx, y, ldy, cols, static_cast<uint64_t*>(ws), make_ip_single_layout(ip), out,
-                st));
-        }
+                x, ldx, y, ldy, cols, static_cast<uint64_t*>(ws), make_ip_single_layout(reg), out,
+                al, st));
+        const IpLayout ip = make_ip_layout(rows, cols, param, sizeof(T), al);
+        if (ip_single(ip)) return CANON_EUNSUPPORTED;  // too many tiles for one launch
         return hip_status(launch_scan_ip<T, !is_op_v<T>>(x, ldx, y, ldy, rows, cols,
                                             static_cast<uint32_t*>(ws), ip_nodes<T>(ws), ip, out,
                                             st));

@@ -32,7 +32,7 @@
     template hipError_t launch_scan_ip_single<V, false>(const V*, uint64_t, V*, uint64_t,         \
                                                         uint64_t, uint64_t*,                       \
                                                         const IpSingleLayout&,                     \
-                                                        const ScanOut<V>*, hipStream_t);
+                                                        const ScanOut<V>*, bool, hipStream_t);
 
 // Minimum and maximum: every parenthesisation gives the same value, so one
 // scan kernel (block_dyadic with one-vector blocks) serves every policy.

@@ -115,11 +115,14 @@ template <typename T>
 struct ScanOut;
 
 // PLAIN = false (both launchers): only the kernels with an output stage are
-// built (out must not be null).
+// built (out must not be null).  The single-pass launcher takes the layout
+// of the register geometry whatever the alignment; `aligned` (rows on
+// 16-byte boundaries: x, y and both pitches) selects 16-byte loads and
+// stores, else element loads and stores.
 template <typename T, bool PLAIN = true>
 hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
                                  uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>* out,
-                                 hipStream_t s);
+                                 bool aligned, hipStream_t s);
 
 template <typename T, bool PLAIN = true>
 hipError_t launch_scan_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t nseg,

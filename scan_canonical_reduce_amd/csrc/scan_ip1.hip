@@ -5,10 +5,10 @@
 namespace canon {
 
 template hipError_t launch_scan_ip_single<double, true>(const double*, uint64_t, double*, uint64_t,
-                                                  uint64_t, uint64_t*, const IpSingleLayout&,
-                                                  const ScanOut<double>*, hipStream_t);
+                                                        uint64_t, uint64_t*, const IpSingleLayout&,
+                                                        const ScanOut<double>*, bool, hipStream_t);
 template hipError_t launch_scan_ip_single<float, true>(const float*, uint64_t, float*, uint64_t,
-                                                 uint64_t, uint64_t*, const IpSingleLayout&,
-                                                 const ScanOut<float>*, hipStream_t);
+                                                       uint64_t, uint64_t*, const IpSingleLayout&,
+                                                       const ScanOut<float>*, bool, hipStream_t);
 
 }  // namespace canon

@@ -95,6 +95,7 @@ struct Ip1Ctx {
     int lane, w;
     T init;
     int kind;
+    bool aligned;  // 16-byte loads and stores (else element ones)
 };
 
 // One tile in registers: vector u of thread (w, lane) holds row
@@ -126,7 +127,7 @@ __device__ __forceinline__ void ip1_load(Ip1Tile<T, LOGRV>& s, uint64_t item,
     const uint64_t seg = item / c.lay->g.tps, t = item % c.lay->g.tps;
     const uint64_t row0 = t * F::R;
     const T* xs = c.x + seg * c.ldx;
-    if ((row0 + F::R) * F::L <= c.cols)
+    if (c.aligned && (row0 + F::R) * F::L <= c.cols)
         ipf_load<T, LOGRV, false>(xs, c.cols, row0, c.w, c.lane, s.a);
     else
         ipf_load<T, LOGRV, true>(xs, c.cols, row0, c.w, c.lane, s.a);
@@ -335,7 +336,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
 #pragma unroll
         for (int q = 0; q < RV; ++q) {
             const uint64_t gi = row * F::L + (uint64_t)(q * 64 + lane) * E;
-            if (full || gi + E <= c.cols) {
+            if (c.aligned && (full || gi + E <= c.cols)) {
                 store_vec(ys + gi, val[q]);
             } else {
 #pragma unroll
@@ -353,7 +354,8 @@ template <typename T, int LOGRV, bool OUTX, bool PIPE>
 __global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ x, uint64_t ldx,
                                                           T* __restrict__ y, uint64_t ldy,
                                                           uint64_t cols, uint64_t* __restrict__ ws,
-                                                          IpSingleLayout lay, T init, int kind)
+                                                          IpSingleLayout lay, T init, int kind,
+                                                          bool aligned)
 {
     __shared__ Ip1Shared<T, LOGRV> sh;
     const Ip1Ctx<T, LOGRV> c{x,
@@ -368,7 +370,8 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ 
                              (int)(threadIdx.x & 63),
                              (int)(threadIdx.x >> 6),
                              init,
-                             kind};
+                             kind,
+                             aligned};
     const uint64_t items = lay.g.nseg * lay.g.tps;
     uint64_t it = ip1_ticket(c);
     if (it >= items) return;
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ 
 template <typename T, int LOGRV, bool OUTX>
 static hipError_t launch_ip1(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
                              uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
-                             hipStream_t s)
+                             bool aligned, hipStream_t s)
 {
     const uint64_t items = lay.g.nseg * lay.g.tps;
     constexpr bool PIPE = ip1_pipelined<LOGRV>();
@@ -411,20 +414,20 @@ static hipError_t launch_ip1(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint6
         if (grid > fit) grid = fit;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kIpThreads), 0, s, x, ldx, y, ldy, cols,
-                       ws, lay, out.init, out.kind);
+                       ws, lay, out.init, out.kind, aligned);
     return hipGetLastError();
 }
 
 template <typename T, bool OUTX>
 static hipError_t launch_ip1_o(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
                                uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
-                               hipStream_t s)
+                               bool al, hipStream_t s)
 {
     switch (lay.g.fast_logrv) {
-        case 0: return launch_ip1<T, 0, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
-        case 1: return launch_ip1<T, 1, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
-        case 2: return launch_ip1<T, 2, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
-        case 3: return launch_ip1<T, 3, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, s);
+        case 0: return launch_ip1<T, 0, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case 1: return launch_ip1<T, 1, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case 2: return launch_ip1<T, 2, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case 3: return launch_ip1<T, 3, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -434,7 +437,7 @@ static hipError_t launch_ip1_o(const T* x, uint64_t ldx, T* y, uint64_t ldy, uin
 template <typename T, bool PLAIN>
 hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
                                  uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>* out,
-                                 hipStream_t s)
+                                 bool aligned, hipStream_t s)
 {
     const uint64_t words = lay.cbase + (lay.counters + 1) / 2;
     uint64_t blocks = (words + 255) / 256;
@@ -442,9 +445,9 @@ hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, u
     hipLaunchKernelGGL((k_ip1_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws, lay);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (out) return launch_ip1_o<T, true>(x, ldx, y, ldy, cols, ws, lay, *out, s);
+    if (out) return launch_ip1_o<T, true>(x, ldx, y, ldy, cols, ws, lay, *out, aligned, s);
     if constexpr (PLAIN)
-        return launch_ip1_o<T, false>(x, ldx, y, ldy, cols, ws, lay, ScanOut<T>{}, s);
+        return launch_ip1_o<T, false>(x, ldx, y, ldy, cols, ws, lay, ScanOut<T>{}, aligned, s);
     return hipErrorInvalidValue;
 }
 

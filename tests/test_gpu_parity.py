@@ -308,6 +308,25 @@ def test_scan_iterated_pairwise_in_place_unaligned(canon):
     assert_bit_exact(to_host(y), oracle.scan(x[1:], "iterated_pairwise", 7), "unaligned")
 
 
+@pytest.mark.parametrize("dtype,L", [(np.float64, 128), (np.float64, 256), (np.float64, 1024),
+                                     (np.float32, 256), (np.float32, 1024)])
+def test_scan_iterated_pairwise_unaligned_register_geometry(canon, dtype, L):
+    """L = 64 E 2^k with a start off the 16-byte grid: the one-pass kernel with
+    element loads and stores; several tiles, a ragged tail, in place, and an
+    exclusive scan with an initial value."""
+    n = 200_003
+    x = synth.generate(n + 1, "mixed_magnitude", 404 + L, dtype)
+    base = to_dev(x)
+    y = canon.scan(base[1:], "iterated_pairwise", L)
+    assert_bit_exact(to_host(y), oracle.scan(x[1:], "iterated_pairwise", L), "unaligned")
+    canon.scan(base[1:], "iterated_pairwise", L, out=base[1:])
+    assert_bit_exact(to_host(base[1:]), oracle.scan(x[1:], "iterated_pairwise", L), "in place")
+    base = to_dev(x)
+    y = canon.scan_with_init(base[1:], "iterated_pairwise", L, "exclusive", 0.5)
+    assert_bit_exact(to_host(y), oracle.scan_with_init(x[1:], "iterated_pairwise", L, 0.5,
+                                                       "exclusive"), "exclusive")
+
+
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("L", [3, 16, 128])
 def test_scan_rows_iterated_pairwise(canon, dtype, L):
