@@ -95,7 +95,6 @@ struct Ip1Ctx {
     int lane, w;
     T init;
     int kind;
-    bool aligned;  // 16-byte loads and stores (else element ones)
 };
 
 // One tile in registers: vector u of thread (w, lane) holds row
@@ -118,7 +117,8 @@ __device__ __forceinline__ uint64_t ip1_ticket(const Ip1Ctx<T, LOGRV>& c)
     return it;
 }
 
-template <typename T, int LOGRV>
+// AL: rows on 16-byte boundaries (16-byte loads; else element loads).
+template <bool AL, typename T, int LOGRV>
 __device__ __forceinline__ void ip1_load(Ip1Tile<T, LOGRV>& s, uint64_t item,
                                          const Ip1Ctx<T, LOGRV>& c)
 {
@@ -127,7 +127,7 @@ __device__ __forceinline__ void ip1_load(Ip1Tile<T, LOGRV>& s, uint64_t item,
     const uint64_t seg = item / c.lay->g.tps, t = item % c.lay->g.tps;
     const uint64_t row0 = t * F::R;
     const T* xs = c.x + seg * c.ldx;
-    if (c.aligned && (row0 + F::R) * F::L <= c.cols)
+    if (AL && (row0 + F::R) * F::L <= c.cols)
         ipf_load<T, LOGRV, false>(xs, c.cols, row0, c.w, c.lane, s.a);
     else
         ipf_load<T, LOGRV, true>(xs, c.cols, row0, c.w, c.lane, s.a);
@@ -218,7 +218,7 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
 
 // Back: the nodes of the earlier tiles applied (right-nested, lowest level
 // first), each row's lane tree walked, the outputs stored.
-template <typename T, int LOGRV, bool OUTX>
+template <typename T, int LOGRV, bool OUTX, bool AL>
 __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, LOGRV>& c)
 {
     using F = IpFast<T, LOGRV>;
@@ -336,7 +336,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
 #pragma unroll
         for (int q = 0; q < RV; ++q) {
             const uint64_t gi = row * F::L + (uint64_t)(q * 64 + lane) * E;
-            if (c.aligned && (full || gi + E <= c.cols)) {
+            if (AL && (full || gi + E <= c.cols)) {
                 store_vec(ys + gi, val[q]);
             } else {
 #pragma unroll
@@ -350,12 +350,11 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
 
 // PIPE: persistent workgroups, two tiles each (the next front before the
 // current back); else one workgroup per tile.
-template <typename T, int LOGRV, bool OUTX, bool PIPE>
+template <typename T, int LOGRV, bool OUTX, bool PIPE, bool AL>
 __global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ x, uint64_t ldx,
                                                           T* __restrict__ y, uint64_t ldy,
                                                           uint64_t cols, uint64_t* __restrict__ ws,
-                                                          IpSingleLayout lay, T init, int kind,
-                                                          bool aligned)
+                                                          IpSingleLayout lay, T init, int kind)
 {
     __shared__ Ip1Shared<T, LOGRV> sh;
     const Ip1Ctx<T, LOGRV> c{x,
@@ -370,34 +369,51 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ 
                              (int)(threadIdx.x & 63),
                              (int)(threadIdx.x >> 6),
                              init,
-                             kind,
-                             aligned};
+                             kind};
     const uint64_t items = lay.g.nseg * lay.g.tps;
     uint64_t it = ip1_ticket(c);
     if (it >= items) return;
     Ip1Tile<T, LOGRV> A, B;
-    ip1_load(A, it, c);
+    ip1_load<AL>(A, it, c);
     ip1_front(A, c);
     if constexpr (!PIPE) {
-        ip1_back<T, LOGRV, OUTX>(A, c);
+        ip1_back<T, LOGRV, OUTX, AL>(A, c);
     } else {
         for (;;) {
             it = ip1_ticket(c);
             if (it < items) {
-                ip1_load(B, it, c);
+                ip1_load<AL>(B, it, c);
                 ip1_front(B, c);
             }
-            ip1_back<T, LOGRV, OUTX>(A, c);
+            ip1_back<T, LOGRV, OUTX, AL>(A, c);
             if (it >= items) break;
             it = ip1_ticket(c);
             if (it < items) {
-                ip1_load(A, it, c);
+                ip1_load<AL>(A, it, c);
                 ip1_front(A, c);
             }
-            ip1_back<T, LOGRV, OUTX>(B, c);
+            ip1_back<T, LOGRV, OUTX, AL>(B, c);
             if (it >= items) break;
         }
     }
+}
+
+template <typename T, int LOGRV, bool OUTX, bool AL>
+static hipError_t launch_ip1_al(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                                uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
+                                hipStream_t s)
+{
+    const uint64_t items = lay.g.nseg * lay.g.tps;
+    constexpr bool PIPE = ip1_pipelined<LOGRV>();
+    constexpr auto kern = k_ip_single<T, LOGRV, OUTX, PIPE, AL>;
+    uint64_t grid = items;
+    if (PIPE) {
+        const uint64_t fit = resident_grid<kern>(kIpThreads);
+        if (grid > fit) grid = fit;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kIpThreads), 0, s, x, ldx, y, ldy, cols,
+                       ws, lay, out.init, out.kind);
+    return hipGetLastError();
 }
 
 template <typename T, int LOGRV, bool OUTX>
@@ -405,17 +421,8 @@ static hipError_t launch_ip1(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint6
                              uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
                              bool aligned, hipStream_t s)
 {
-    const uint64_t items = lay.g.nseg * lay.g.tps;
-    constexpr bool PIPE = ip1_pipelined<LOGRV>();
-    constexpr auto kern = k_ip_single<T, LOGRV, OUTX, PIPE>;
-    uint64_t grid = items;
-    if (PIPE) {
-        const uint64_t fit = resident_grid<kern>(kIpThreads);
-        if (grid > fit) grid = fit;
-    }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kIpThreads), 0, s, x, ldx, y, ldy, cols,
-                       ws, lay, out.init, out.kind, aligned);
-    return hipGetLastError();
+    if (aligned) return launch_ip1_al<T, LOGRV, OUTX, true>(x, ldx, y, ldy, cols, ws, lay, out, s);
+    return launch_ip1_al<T, LOGRV, OUTX, false>(x, ldx, y, ldy, cols, ws, lay, out, s);
 }
 
 template <typename T, bool OUTX>
