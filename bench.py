@@ -293,30 +293,56 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def run_configs(torch, canon, synth, dev, reps=20):
+SCRUB_BYTES = 512 << 20  # twice the 256 MB Infinity Cache (MALL)
+
+
+def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
     """Every workload config: each op checked against the oracle (full result
     for reduces and for the 2^20 scans, 32 sampled prefixes evaluated from
-    scratch for the large scans, 64 sampled rows for the row ops), then the
-    mean of `reps` calls timed with HIP events on the current stream.  Prints
-    one markdown table."""
+    scratch for the large scans, 64 sampled rows for the row ops), then
+    `warmup` untimed calls and `reps` calls each bracketed by HIP events on
+    the current stream (median, 10th and 90th percentile; GB/s from the
+    median), and the mean of `reps` calls issued back to back between two
+    events (no event between calls).  The 2^20 inputs
+    are also timed with a 512 MiB buffer rewritten before every call, so that
+    neither L2 nor the MALL holds them ("MALL scrubbed" rows).  Prints one
+    markdown table."""
     import oracle
     rng = np.random.default_rng(7)
     stream = torch.cuda.current_stream()
     rows = []
+    scrub_buf = []
 
-    def timed(fn):
-        for _ in range(3):
+    def scrub():
+        if not scrub_buf:
+            scrub_buf.append(torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev))
+        scrub_buf[0].fill_(1.0)
+
+    def timed(fn, scrubbed=False):
+        for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
         torch.cuda._sleep(HOST_AHEAD_SPIN)
-        a.record(stream)
-        for _ in range(reps):
+        for r in range(reps):
+            if scrubbed:
+                scrub()
+            ev[2 * r].record(stream)
             fn()
-        b.record(stream)
+            ev[2 * r + 1].record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3  # us
+        t = sorted(ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e3 for r in range(reps))  # us
+        chain = None
+        if not scrubbed:
+            torch.cuda._sleep(HOST_AHEAD_SPIN)
+            ev[0].record(stream)
+            for _ in range(reps):
+                fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            chain = ev[0].elapsed_time(ev[1]) / reps * 1e3
+        return {"median": t[reps // 2], "p10": t[reps // 10], "p90": t[(9 * reps) // 10],
+                "chain": chain}
 
     def same(got, want):
         got = np.asarray(got)
@@ -324,12 +350,14 @@ def run_configs(torch, canon, synth, dev, reps=20):
         u = np.uint64 if got.dtype == np.float64 else np.uint32
         return bool(np.array_equal(got.view(u), want.view(u)))
 
-    def add(cfg, op, dt, n, nbytes, us, ok):
+    def add(cfg, op, dt, n, nbytes, t, ok):
+        us = t["median"]
         gbs = nbytes / (us * 1e-6) / 1e9
-        rows.append((cfg, op, dt, n, us, gbs, 100.0 * gbs / HBM_PEAK_GBS, n / (us * 1e-6), ok))
-        log(f"[configs] {cfg} {op}: {us:.1f} us {gbs:.0f} GB/s parity {'PASS' if ok else 'FAIL'}")
+        rows.append((cfg, op, dt, n, t, gbs, 100.0 * gbs / HBM_PEAK_GBS, n / (us * 1e-6), ok))
+        log(f"[configs] {cfg} {op}: median {us:.1f} us (p10 {t['p10']:.1f}, p90 {t['p90']:.1f}) "
+            f"{gbs:.0f} GB/s parity {'PASS' if ok else 'FAIL'}")
 
-    def reduce_cfg(cfg, name, Ls, init):
+    def reduce_cfg(cfg, name, Ls, init, scrubbed=False):
         xn = synth.config_input(name)
         x = torch.from_numpy(xn).to(dev)
         out = torch.empty((), dtype=x.dtype, device=dev)
@@ -340,8 +368,12 @@ def run_configs(torch, canon, synth, dev, reps=20):
             ok = same(out.cpu().numpy().reshape(1), [oracle.reduce(xn, L, init)])
             us = timed(lambda: canon.reduce(x, L, init, out=out, ws=ws))
             add(cfg, f"reduce L={L} init={init}", str(xn.dtype), xn.size, xn.nbytes, us, ok)
+            if scrubbed:
+                us = timed(lambda: canon.reduce(x, L, init, out=out, ws=ws), scrubbed=True)
+                add(cfg + " MALL scrubbed", f"reduce L={L} init={init}", str(xn.dtype), xn.size,
+                    xn.nbytes, us, ok)
 
-    def scan_cfg(cfg, name, pols, full):
+    def scan_cfg(cfg, name, pols, full, scrubbed=False):
         xn = synth.config_input(name)
         x = torch.from_numpy(xn).to(dev)
         y = torch.empty_like(x)
@@ -365,9 +397,14 @@ def run_configs(torch, canon, synth, dev, reps=20):
             us = timed(lambda: canon.scan(x, pol, q, out=y, ws=ws))
             label = pol if pol == "pairwise" else f"{pol}<{q}>"
             add(cfg, f"scan {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok)
+            if scrubbed:
+                us = timed(lambda: canon.scan(x, pol, q, out=y, ws=ws), scrubbed=True)
+                add(cfg + " MALL scrubbed", f"scan {label}", str(xn.dtype), xn.size,
+                    2 * xn.nbytes, us, ok)
 
-    reduce_cfg("C1", "reduce_1m", (16, 128), 0.0)
-    scan_cfg("C2", "scan_1m", (("block_dyadic", 256), ("pairwise", 0)), True)
+    reduce_cfg("C1", "reduce_1m", (16, 128), 0.0, scrubbed=True)
+    scan_cfg("C2", "scan_1m", (("block_dyadic", 256), ("pairwise", 0)), True, scrubbed=True)
+    scrub_buf.clear()
     reduce_cfg("C3", "reduce_2e28_f64", (128,), 1.0)
     reduce_cfg("C3", "reduce_2e29_f32", (128,), 1.0)
     Xn = synth.config_input("rows_16384x4096")
@@ -467,10 +504,13 @@ def run_configs(torch, canon, synth, dev, reps=20):
                                        ("min", "scan", "block_dyadic", 256),
                                        ("max", "scan", "iterated_pairwise", 128)))
 
-    print("| config | op | dtype | N | us | GB/s | % of 8 TB/s | elements/s | bit-exact |")
-    print("|---|---|---|---|---|---|---|---|---|")
-    for cfg, op, dt, n, us, gbs, pct, eps, ok in rows:
-        print(f"| {cfg} | {op} | {dt} | {n} | {us:.1f} | {gbs:.0f} | {pct:.1f} | {eps:.3g} | "
+    print("| config | op | dtype | N | median us | p10 us | p90 us | back-to-back mean us | "
+          "GB/s | % of 8 TB/s | elements/s | bit-exact |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for cfg, op, dt, n, t, gbs, pct, eps, ok in rows:
+        chain = "n/a" if t["chain"] is None else f"{t['chain']:.1f}"
+        print(f"| {cfg} | {op} | {dt} | {n} | {t['median']:.1f} | {t['p10']:.1f} | "
+              f"{t['p90']:.1f} | {chain} | {gbs:.0f} | {pct:.1f} | {eps:.3g} | "
               f"{'yes' if ok else 'NO'} |")
 
 
@@ -528,9 +568,26 @@ def cpu_baseline(x_np, X_np, have_ip):
     combines 128 lane values per prefix, about 10x slower per element), the
     row ops over all 16384 rows.  value = algorithmic bytes / seconds."""
     import oracle
+    # one core, as a single-threaded baseline; the previous affinity comes back afterwards
+    allowed = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    core = min(allowed) if allowed else None
+    if core is not None:
+        os.sched_setaffinity(0, {core})
+    try:
+        t0 = time.perf_counter()
+        nbytes, sample = _cpu_baseline_work(oracle, x_np, X_np, have_ip)
+        dt = time.perf_counter() - t0
+    finally:
+        if core is not None:
+            os.sched_setaffinity(0, allowed)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2), "cpu": host_cpu_model(),
+            "pinned_core": core, "host_threads": os.cpu_count()}
+
+
+def _cpu_baseline_work(oracle, x_np, X_np, have_ip):
     n = x_np.size
     nbytes = 0
-    t0 = time.perf_counter()
     oracle.reduce(x_np, 128, 1.0)
     nbytes += n * 8
     for p, q in (("block_dyadic", 256), ("block_dyadic", 16), ("pairwise", 0)):
@@ -548,9 +605,19 @@ def cpu_baseline(x_np, X_np, have_ip):
         oracle.scan_rows(X_np, "block_dyadic", 16)
         nbytes += 2 * X_np.size * 8
         sample += "; row reduce and row scan over all 16384 rows"
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+    return nbytes, sample
+
+
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
