@@ -224,8 +224,11 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
     using F = IpFast<T, LOGRV>;
     using SH = Ip1Shared<T, LOGRV>;
     constexpr int E = F::E, RV = F::RV, RW = F::RW;
-    constexpr int NB = SH::STAGE / F::L;         // nodes per batch
-    constexpr int PER = SH::STAGE / kIpThreads;  // words per thread per batch
+    // The node words are read by waves 0-2 alone: wave 3 comes to the back
+    // from the front's climb, and its reads would hold up the batch.
+    constexpr int RT = kIpThreads - 64;                  // reading threads
+    constexpr int NB = SH::STAGE / F::L;                 // nodes per batch
+    constexpr int PER = (SH::STAGE + RT - 1) / RT;       // words per reading thread
     const IpSingleLayout& lay = *c.lay;
     const uint64_t seg = s.item / lay.g.tps, t = s.item % lay.g.tps;
     const int lane = c.lane, w = c.w;
@@ -234,9 +237,9 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
     const uint64_t row0 = t * F::R;
     const bool full = (row0 + F::R) * F::L <= c.cols;
 
-    // The node words of up to NB set bits at a time, spread over the threads
-    // (word idx of a batch: node idx / L, lane idx % L), every read issued
-    // before any is waited for, then staged in LDS.
+    // The node words of up to NB set bits at a time, spread over the reading
+    // threads (word idx of a batch: node idx / L, lane idx % L), every read
+    // issued before any is waited for, then staged in LDS.
     T b[RV][E];
 #pragma unroll
     for (int q = 0; q < RV; ++q)
@@ -249,23 +252,26 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         for (; k < lay.g.levels && (t >> k) != 0 && nb < NB; ++k)
             if ((t >> k) & 1) lv[nb++] = k;
         if (nb == 0) break;
-        uint64_t wv[PER];
+        if (w < 3) {
+            uint64_t wv[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int idx = i * kIpThreads + (int)threadIdx.x;
-            const int m = idx / F::L, col = idx % F::L;
-            wv[i] = not_ready_word<T>();
-            if (m < nb)
-                wv[i] = __hip_atomic_load(ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col),
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+            for (int i = 0; i < PER; ++i) {
+                const int idx = i * RT + (int)threadIdx.x;
+                const int m = idx / F::L, col = idx % F::L;
+                wv[i] = not_ready_word<T>();
+                if (idx < SH::STAGE && m < nb)
+                    wv[i] = __hip_atomic_load(
+                        ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col), __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+            }
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int idx = i * kIpThreads + (int)threadIdx.x;
-            const int m = idx / F::L, col = idx % F::L;
-            if (m < nb)
-                c.sh->h[idx] = ready_or_wait<T>(
-                    wv[i], ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col), c.err);
+            for (int i = 0; i < PER; ++i) {
+                const int idx = i * RT + (int)threadIdx.x;
+                const int m = idx / F::L, col = idx % F::L;
+                if (idx < SH::STAGE && m < nb)
+                    c.sh->h[idx] = ready_or_wait<T>(
+                        wv[i], ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col), c.err);
+            }
         }
         __syncthreads();
         for (int m = 0; m < nb; ++m) {

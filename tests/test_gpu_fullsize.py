@@ -88,3 +88,35 @@ def test_scan_iterated_pairwise_full_size(canon, L):
     assert_bit_exact(got, want, "probes")
     back = to_host(canon.reduce(xd, L, -0.0)).reshape(1)
     assert_bit_exact(to_host(y[-1:]), back, "scan back == reduce (GPU)")
+
+
+def test_bench_step_scans_full_size(canon):
+    """The scans of the benchmark step on its own input (f64, N = 2^28, mixed
+    magnitudes, output and workspace passed in as the benchmark does):
+    pairwise and block_dyadic compared on every element, iterated_pairwise<128>
+    on the first 2^22 elements and on sampled prefixes evaluated from scratch,
+    and every back element against the GPU reduce of the same expression."""
+    x = synth.config_input("reduce_2e28_f64")
+    xd = to_dev(x)
+    y = torch.empty_like(xd)
+    for policy, param in (("block_dyadic", 256), ("block_dyadic", 16), ("pairwise", 0),
+                          ("iterated_pairwise", 128)):
+        print(f"[fullsize] reduce_2e28_f64 scan {policy}<{param}>", flush=True)
+        ws = torch.empty(canon.scan_workspace_bytes(x.size, policy, param, 8),
+                         dtype=torch.uint8, device="cuda")
+        canon.scan(xd, policy, param, out=y, ws=ws)
+        assert canon.workspace_error(ws) == 0
+        if policy == "iterated_pairwise":
+            head = 1 << 22
+            assert_bit_exact(to_host(y[:head]), oracle.scan(x[:head], policy, param), "head")
+            idx = _probes(x.size, seed=78)
+            got = to_host(y[torch.from_numpy(idx).to("cuda")])
+            want = np.array([oracle.scan_prefix(x, int(i), policy, param) for i in idx])
+            assert_bit_exact(got, want, "probes")
+        else:
+            assert_bit_exact(to_host(y), oracle.scan(x, policy, param), f"{policy}<{param}>")
+        # scan back == reduce of the same expression (block sizes divide 2^28)
+        L = param if policy == "iterated_pairwise" else 1
+        back = to_host(canon.reduce(xd, L, -0.0)).reshape(1)
+        assert_bit_exact(to_host(y[-1:]), back, f"{policy} back == reduce")
+        del ws
