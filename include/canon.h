@@ -61,7 +61,8 @@
 extern "C" {
 #endif
 
-#define CANON_ABI_VERSION 3 /* 2: scans with an initial value; 3: operators */
+#define CANON_ABI_VERSION 4 /* 2: scans with an initial value; 3: operators;
+                               4: tile geometry queries, schedule override */
 
 /* Largest lane count L for reduce and iterated_pairwise, and largest block
  * size B for block_dyadic.  Larger values return CANON_EUNSUPPORTED. */
@@ -212,9 +213,11 @@ canon_status_t canon_scan_rows_with_init_f32(const float* x, size_t ldx, float* 
  * canon_scan_op_* and canon_scan_rows_op_* take kind and init as the scans
  * with an initial value do (kind CANON_SCAN_INCLUSIVE with init = the
  * identity is the plain scan).  CANON_OP_ADD gives exactly the results of
- * the functions above.  The other operators run the general streaming
- * reduce kernel for every L and alignment, and the scan kernels with an
- * output stage. */
+ * the functions above.  The other operators run the reduce kernels of
+ * addition (the register streaming kernel for a power-of-two L and 16-byte
+ * aligned input, the general streaming kernel otherwise) and the scan
+ * kernels with an output stage; CANON_OP_MIN and CANON_OP_MAX, associative
+ * and commutative, run one scan kernel whatever the policy. */
 canon_status_t canon_reduce_op_f64(const double* x, size_t n, uint32_t L, int op, double init,
                                    double* out, void* ws, size_t ws_bytes, void* stream);
 canon_status_t canon_reduce_op_f32(const float* x, size_t n, uint32_t L, int op, float init,
@@ -241,13 +244,45 @@ canon_status_t canon_scan_rows_op_f32(const float* x, size_t ldx, float* y, size
                                       void* stream);
 
 /* -------------------------------------------------------------- checking */
-/* Every scan workspace begins with a 32-bit error word.  The single-pass
- * scans (pairwise, block_dyadic) wait on values published by earlier
- * workgroups with a bounded spin; if a bound is ever exceeded the kernel
- * stops waiting, records a nonzero error word and finishes (the output is
- * then invalid).  This call copies the word to *err_out and synchronises
- * `stream`.  0 means no error. */
+/* Every scan workspace begins with a 32-bit error word, which every scan
+ * call given a workspace of nonzero size sets.  The single-pass scans wait
+ * on values published by earlier workgroups with a bounded spin; if a bound
+ * is ever exceeded the kernel stops waiting, records a nonzero error word
+ * and finishes (the output is then invalid).  This call copies the word to
+ * *err_out and synchronises `stream`.  0 means no error. */
 canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream);
+
+/* -------------------------------------------------------------- geometry */
+/* Elements per tile, the unit one workgroup step of a scan covers: for the
+ * 1-D scans (canon_scan_*) and for the row scans (canon_scan_rows_*, tiles
+ * within a row), given the policy, its param and elem_size (4 or 8), for
+ * 16-byte aligned data.  Results never depend on it; it tells a caller (a
+ * test) where sizes cross tile and tile-group edges.  0 for an invalid
+ * policy, param or element size. */
+size_t canon_scan_tile_elems(int policy, uint32_t param, size_t elem_size);
+size_t canon_scan_rows_tile_elems(int policy, uint32_t param, size_t elem_size);
+
+/* ------------------------------------------------------ schedule override */
+/* Process-wide override of how work is spread over workgroups, for tests
+ * that show the results do not depend on the schedule (P4016R0 "Summary":
+ * an implementation may schedule freely as long as the value is the
+ * canonical one).  value 0 restores the default.
+ *   CANON_SCHED_GRID             at most `value` workgroups for every
+ *                                persistent (ticket-driven) or grid-stride
+ *                                kernel: single-pass scans, the pipelined
+ *                                iterated_pairwise pass, the three-kernel
+ *                                iterated_pairwise path, row reduces and row
+ *                                scans (kernels with one workgroup per tile
+ *                                keep their grid)
+ *   CANON_SCHED_REDUCE_PARTIALS  workgroups (row ranges, hence partials) the
+ *                                streaming reduce aims for; the reduce
+ *                                workspace size follows it
+ * Returns CANON_EINVAL for an unknown knob.  Not synchronised with calls in
+ * flight on other host threads: set it between calls. */
+#define CANON_SCHED_GRID 0
+#define CANON_SCHED_REDUCE_PARTIALS 1
+canon_status_t canon_set_schedule(int knob, uint64_t value);
+uint64_t canon_get_schedule(int knob);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,19 @@ same names without the ``canon_`` prefix:
 
 ``policy`` is "pairwise", "iterated_pairwise" (param = L) or "block_dyadic"
 (param = B, a power of two).
+
+The scans wait on values published by other workgroups with a bounded spin;
+if a bound were ever exceeded the kernel records an error word in its
+workspace.  The scan functions read that word (``check``): by default when
+they allocated the workspace themselves (the call then synchronises), and
+always when ``check=True``; a caller passing ``ws`` without ``check`` reads it
+with ``workspace_error(ws)`` when convenient.  A nonzero word raises
+CanonError.
+
+    scan_tile_elems(policy, param, elem_size), scan_rows_tile_elems(...)
+                                       -> elements per scan tile
+    set_schedule(knob, value), schedule(grid=..., reduce_partials=...)
+                                       -> the schedule override (tests)
 """
 from __future__ import annotations
 
@@ -55,8 +68,12 @@ EXPORTS = [
     "canon_reduce_op_f64", "canon_reduce_op_f32", "canon_reduce_rows_op_f64",
     "canon_reduce_rows_op_f32", "canon_scan_op_f64", "canon_scan_op_f32",
     "canon_scan_rows_op_f64", "canon_scan_rows_op_f32",
-    "canon_workspace_error",
+    "canon_workspace_error", "canon_scan_tile_elems", "canon_scan_rows_tile_elems",
+    "canon_set_schedule", "canon_get_schedule",
 ]
+
+ABI_VERSION = 4
+SCHED = {"grid": 0, "reduce_partials": 1}
 
 _lib = None
 
@@ -109,11 +126,19 @@ def lib() -> ctypes.CDLL:
     L.canon_scan_rows_op_f64.argtypes = [P, S, P, S, S, S, I, U, I, I, D, P, S, P]
     L.canon_scan_rows_op_f32.argtypes = [P, S, P, S, S, S, I, U, I, I, F, P, S, P]
     L.canon_workspace_error.argtypes = [P, ctypes.POINTER(U), P]
+    L.canon_scan_tile_elems.argtypes = [I, U, S]
+    L.canon_scan_tile_elems.restype = S
+    L.canon_scan_rows_tile_elems.argtypes = [I, U, S]
+    L.canon_scan_rows_tile_elems.restype = S
+    L.canon_set_schedule.argtypes = [I, ctypes.c_uint64]
+    L.canon_get_schedule.argtypes = [I]
+    L.canon_get_schedule.restype = ctypes.c_uint64
     for name in EXPORTS:
-        if name not in ("canon_abi_version", "canon_status_str", "canon_last_hip_error") and \
-                not name.endswith("workspace_bytes"):
+        if name not in ("canon_abi_version", "canon_status_str", "canon_last_hip_error",
+                        "canon_scan_tile_elems", "canon_scan_rows_tile_elems",
+                        "canon_get_schedule") and not name.endswith("workspace_bytes"):
             getattr(L, name).restype = I
-    if L.canon_abi_version() != 3:
+    if L.canon_abi_version() != ABI_VERSION:
         raise CanonError("libcanon ABI version mismatch")
     _lib = L
     return L
@@ -168,6 +193,17 @@ def _ws(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor | None:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _check_ws(w: torch.Tensor | None, ws: torch.Tensor | None, check, what: str) -> None:
+    """Reads a scan's error word: when check is True, or when check is None
+    and the workspace is the binding's own (w is not the caller's ws)."""
+    if w is None or check is False or (check is None and w is ws):
+        return
+    err = workspace_error(w)
+    if err != 0:
+        raise CanonError(f"{what}: a bounded wait gave up (error word {err:#x}); "
+                         "the output is invalid")
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -203,7 +239,7 @@ def reduce(x: torch.Tensor, L: int, init: float = 0.0, out: torch.Tensor | None 
 
 
 def scan(x: torch.Tensor, policy="pairwise", param: int = 0, out: torch.Tensor | None = None,
-         ws: torch.Tensor | None = None) -> torch.Tensor:
+         ws: torch.Tensor | None = None, check: bool | None = None) -> torch.Tensor:
     """Prefix values of the policy's expression; out may be x (in place)."""
     _need_gpu(x)
     if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
@@ -218,6 +254,7 @@ def scan(x: torch.Tensor, policy="pairwise", param: int = 0, out: torch.Tensor |
         _ptr(x), out.data_ptr(), x.numel(), p, param, _ptr(w), nb if w is None else w.numel(),
         _stream())
     _check(st, "scan")
+    _check_ws(w, ws, check, "scan")
     return out
 
 
@@ -244,7 +281,8 @@ def reduce_rows(X: torch.Tensor, L: int, init: float = 0.0,
 
 
 def scan_rows(X: torch.Tensor, policy="pairwise", param: int = 0,
-              out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+              out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+              check: bool | None = None) -> torch.Tensor:
     """One canonical scan per row of a 2-d tensor."""
     _need_gpu(X)
     sfx = _sfx(X)
@@ -259,12 +297,13 @@ def scan_rows(X: torch.Tensor, policy="pairwise", param: int = 0,
         _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, _ptr(w),
         nb if w is None else w.numel(), _stream())
     _check(st, "scan_rows")
+    _check_ws(w, ws, check, "scan_rows")
     return out
 
 
 def scan_with_init(x: torch.Tensor, policy="pairwise", param: int = 0, kind="inclusive",
                    init: float = -0.0, out: torch.Tensor | None = None,
-                   ws: torch.Tensor | None = None) -> torch.Tensor:
+                   ws: torch.Tensor | None = None, check: bool | None = None) -> torch.Tensor:
     """Scan with an initial value: each output is init + the policy's value on
     the prefix it observes (x[0..i] for "inclusive", x[0..i-1] for
     "exclusive" and "include_initial", init alone for the empty prefix);
@@ -287,12 +326,14 @@ def scan_with_init(x: torch.Tensor, policy="pairwise", param: int = 0, kind="inc
         _ptr(x), out.data_ptr(), x.numel(), p, param, k, float(init), _ptr(w),
         nb if w is None else w.numel(), _stream())
     _check(st, "scan_with_init")
+    _check_ws(w, ws, check, "scan_with_init")
     return out
 
 
 def scan_rows_with_init(X: torch.Tensor, policy="pairwise", param: int = 0, kind="inclusive",
                         init: float = -0.0, out: torch.Tensor | None = None,
-                        ws: torch.Tensor | None = None) -> torch.Tensor:
+                        ws: torch.Tensor | None = None,
+                        check: bool | None = None) -> torch.Tensor:
     """scan_with_init of every row of a 2-d tensor; the result has one more
     column for include_initial."""
     _need_gpu(X)
@@ -312,6 +353,7 @@ def scan_rows_with_init(X: torch.Tensor, policy="pairwise", param: int = 0, kind
         _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, k, float(init), _ptr(w),
         nb if w is None else w.numel(), _stream())
     _check(st, "scan_rows_with_init")
+    _check_ws(w, ws, check, "scan_rows_with_init")
     return out
 
 
@@ -362,7 +404,7 @@ def reduce_rows_op(X: torch.Tensor, L: int, op="add", init=None,
 
 def scan_op(x: torch.Tensor, policy="pairwise", param: int = 0, op="add", kind="inclusive",
             init=None, out: torch.Tensor | None = None,
-            ws: torch.Tensor | None = None) -> torch.Tensor:
+            ws: torch.Tensor | None = None, check: bool | None = None) -> torch.Tensor:
     """scan_with_init with the operator op; init defaults to the operator's
     identity (with kind "inclusive": the plain scan)."""
     _need_gpu(x)
@@ -382,12 +424,13 @@ def scan_op(x: torch.Tensor, policy="pairwise", param: int = 0, op="add", kind="
         _ptr(x), out.data_ptr(), x.numel(), p, param, _op(op), k, float(_op_init(op, init)),
         _ptr(w), nb if w is None else w.numel(), _stream())
     _check(st, "scan_op")
+    _check_ws(w, ws, check, "scan_op")
     return out
 
 
 def scan_rows_op(X: torch.Tensor, policy="pairwise", param: int = 0, op="add", kind="inclusive",
                  init=None, out: torch.Tensor | None = None,
-                 ws: torch.Tensor | None = None) -> torch.Tensor:
+                 ws: torch.Tensor | None = None, check: bool | None = None) -> torch.Tensor:
     """scan_op of every row of a 2-d tensor (one more column for
     include_initial)."""
     _need_gpu(X)
@@ -407,6 +450,7 @@ def scan_rows_op(X: torch.Tensor, policy="pairwise", param: int = 0, op="add", k
         _ptr(X), ldx, out.data_ptr(), ldy, rows, cols, p, param, _op(op), k,
         float(_op_init(op, init)), _ptr(w), nb if w is None else w.numel(), _stream())
     _check(st, "scan_rows_op")
+    _check_ws(w, ws, check, "scan_rows_op")
     return out
 
 
@@ -416,3 +460,44 @@ def workspace_error(ws: torch.Tensor) -> int:
     _check(lib().canon_workspace_error(ws.data_ptr(), ctypes.byref(v), _stream()),
            "workspace_error")
     return v.value
+
+
+def scan_tile_elems(policy, param: int, elem_size: int) -> int:
+    """Elements per tile of the 1-d scans (16-byte aligned data)."""
+    return lib().canon_scan_tile_elems(_policy(policy), param, elem_size)
+
+
+def scan_rows_tile_elems(policy, param: int, elem_size: int) -> int:
+    """Elements per tile within a row of the row scans."""
+    return lib().canon_scan_rows_tile_elems(_policy(policy), param, elem_size)
+
+
+def set_schedule(knob, value: int) -> None:
+    """The schedule override ("grid" or "reduce_partials"; 0 = default)."""
+    k = SCHED[knob] if isinstance(knob, str) else int(knob)
+    _check(lib().canon_set_schedule(k, int(value)), "set_schedule")
+
+
+def get_schedule(knob) -> int:
+    k = SCHED[knob] if isinstance(knob, str) else int(knob)
+    return int(lib().canon_get_schedule(k))
+
+
+class schedule:
+    """Context manager: the schedule override for the calls inside it, e.g.
+    ``with schedule(grid=3): ...``; the previous values are restored."""
+
+    def __init__(self, **knobs):
+        self.knobs = knobs
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.knobs.items():
+            self.saved[k] = get_schedule(k)
+            set_schedule(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_schedule(k, v)
+        return False

@@ -22,11 +22,12 @@ SOURCES = [
     "ops_max_f64.hip", "ops_max_f32.hip",
 ]
 
-# -ffp-contract=off: no FMA contraction; no fast-math; packed FP32 disabled.
+# -ffp-contract=off: no FMA contraction; no fast-math; subnormals kept (no
+# flush to zero in device code, float included); packed FP32 disabled.
 HIPFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
-    "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature",
+    "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function",
 ]
 
 

@@ -273,4 +273,44 @@ canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* st
     return hip_status(e);
 }
 
+size_t canon_scan_tile_elems(int policy, uint32_t param, size_t elem_size)
+{
+    if (check_policy(policy, param) != CANON_OK || (elem_size != 4 && elem_size != 8)) return 0;
+    if (is_ip(policy, param)) {
+        const IpLayout ip = make_ip_layout(1, 1, param, elem_size, true);
+        return (size_t)(1ull << ip.r_log) * param;
+    }
+    return (size_t)1 << (elem_size == 8 ? scan_tile_log<double>() : scan_tile_log<float>());
+}
+
+size_t canon_scan_rows_tile_elems(int policy, uint32_t param, size_t elem_size)
+{
+    if (check_policy(policy, param) != CANON_OK || (elem_size != 4 && elem_size != 8)) return 0;
+    if (is_ip(policy, param)) return canon_scan_tile_elems(policy, param, elem_size);
+    // E elements per vector, 64 lanes, 2^scan_rows_log_v vectors, 4 waves
+    return elem_size == 8 ? (size_t)2 << (6 + scan_rows_log_v<double>() + 2)
+                          : (size_t)4 << (6 + scan_rows_log_v<float>() + 2);
+}
+
+canon_status_t canon_set_schedule(int knob, uint64_t value)
+{
+    switch (knob) {
+        case CANON_SCHED_GRID: g_sched_grid_cap.store(value, std::memory_order_relaxed); break;
+        case CANON_SCHED_REDUCE_PARTIALS:
+            g_sched_reduce_wg.store(value, std::memory_order_relaxed);
+            break;
+        default: return CANON_EINVAL;
+    }
+    return CANON_OK;
+}
+
+uint64_t canon_get_schedule(int knob)
+{
+    switch (knob) {
+        case CANON_SCHED_GRID: return g_sched_grid_cap.load(std::memory_order_relaxed);
+        case CANON_SCHED_REDUCE_PARTIALS: return g_sched_reduce_wg.load(std::memory_order_relaxed);
+        default: return 0;
+    }
+}
+
 }  // extern "C"

@@ -13,6 +13,7 @@
 
 #include "../../include/canon.h"
 #include "device.hpp"
+#include "launch.hpp"
 #include "reduce.hpp"
 #include "scan.hpp"
 #include "scan_ip.hpp"
@@ -39,6 +40,14 @@ inline thread_local int g_last_hip_error = 0;
 
 inline constexpr uint64_t kReduceTargetWG = 256;  // one streaming workgroup per MI355X CU
 inline constexpr size_t kWsAlign = 256;
+
+// Workgroups the streaming reduce aims for: one per CU, or the schedule
+// override's value.
+inline uint64_t reduce_target_wg()
+{
+    const uint64_t v = g_sched_reduce_wg.load(std::memory_order_relaxed);
+    return v ? v : kReduceTargetWG;
+}
 
 inline bool is_pow2(uint64_t v) { return v && !(v & (v - 1)); }
 
@@ -73,8 +82,8 @@ inline size_t reduce_ws(uint64_t n, uint32_t L, size_t es)
 {
     if (L == 0 || L > CANON_MAX_L || (es != 4 && es != 8)) return 0;
     // the larger of the two possible plans (16-byte aligned input or not)
-    const ReducePlan a = plan_reduce(n, L, es, true, kReduceTargetWG);
-    const ReducePlan b = plan_reduce(n, L, es, false, kReduceTargetWG);
+    const ReducePlan a = plan_reduce(n, L, es, true, reduce_target_wg());
+    const ReducePlan b = plan_reduce(n, L, es, false, reduce_target_wg());
     uint64_t need = reduce_partials_bytes(a, L, es);
     const uint64_t nb = reduce_partials_bytes(b, L, es);
     if (nb > need) need = nb;
@@ -88,7 +97,7 @@ canon_status_t reduce_impl(const T* x, size_t n, uint32_t L, T init, T* out, voi
     if (out == nullptr || L == 0 || (n > 0 && x == nullptr)) return CANON_EINVAL;
     if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
     const ReducePlan pl =
-        plan_reduce(n, L, sizeof(T), aligned16(x), kReduceTargetWG);
+        plan_reduce(n, L, sizeof(T), aligned16(x), reduce_target_wg());
     // the documented size (covers either plan), so that a caller who sizes by
     // canon_reduce_workspace_bytes is never rejected and never overrun
     if (canon_status_t s = check_ws(ws, ws_bytes, reduce_ws(n, L, sizeof(T)))) return s;
@@ -105,7 +114,7 @@ canon_status_t reduce_rows_impl(const T* x, size_t rows, size_t cols, size_t ldx
     if (L == 0 || ldx < cols || (rows > 0 && out == nullptr) ||
         (rows > 0 && cols > 0 && x == nullptr))
         return CANON_EINVAL;
-    if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
+    if (L > CANON_MAX_L || !reduce_rows_supported(cols, L)) return CANON_EUNSUPPORTED;
     if (rows == 0) return CANON_OK;
     return hip_status(launch_reduce_rows<T>(x, rows, cols, ldx, L, init, out,
                                             static_cast<hipStream_t>(stream)));
@@ -266,6 +275,14 @@ canon_status_t scan_rows_impl(const T* x, size_t ldx, T* y, size_t ldy, size_t r
     if constexpr (is_order_free_v<T>) {
         const bool al = aligned16(x) && aligned16(y) && (ldx * sizeof(T)) % 16 == 0 &&
                         (ldy * sizeof(T)) % 16 == 0;
+        // this row kernel waits for nothing; a workspace it was given still
+        // gets a cleared error word (its first bytes), as every scan's does
+        if (ws != nullptr && ws_bytes >= sizeof(T)) {
+            using bits_t = typename Elem<T>::bits_t;
+            const hipError_t e = launch_put_column<T>(static_cast<T*>(ws), 1, 1,
+                                                      __builtin_bit_cast(T, bits_t(0)), st);
+            if (e != hipSuccess) return hip_status(e);
+        }
         return hip_status(launch_scan_rows<T, false, true>(x, ldx, y, ldy, rows, cols, true, 0, al,
                                                            out, st));
     } else if (is_ip(policy, param)) {

@@ -4,9 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 namespace canon {
+
+// Schedule override (canon_set_schedule; 0 = none), process-wide and meant
+// for tests: a cap on the workgroups of the persistent (ticket-driven) and
+// grid-stride kernels, and the workgroups the streaming reduce aims for.
+// Both change how the work is spread over workgroups, never the results.
+inline std::atomic<uint64_t> g_sched_grid_cap{0};
+inline std::atomic<uint64_t> g_sched_reduce_wg{0};
+
+// `grid` workgroups, or fewer under the schedule override.
+inline uint64_t capped_grid(uint64_t grid)
+{
+    const uint64_t cap = g_sched_grid_cap.load(std::memory_order_relaxed);
+    return (cap != 0 && grid > cap) ? cap : grid;
+}
 
 // Workgroups of kernel KERN (with `threads` threads and `shmem` bytes of
 // dynamic shared memory each) that fit on the current device at once, cached

@@ -88,6 +88,32 @@ inline ReducePlan plan_reduce(uint64_t n, uint32_t L, size_t elem_size, bool ali
     return pl;
 }
 
+// Rounds per row: fewer than 2^(kRowsRoundDepth + 1).  A round holds at least
+// 2^13 * S rows-of-L with L * S >= 128, so this covers rows of 2^45 elements,
+// far beyond device memory; longer rows are rejected before launch.
+constexpr int kRowsRoundDepth = 24;
+
+// Rows-of-L per thread segment: the smallest power of two with rs * S >= m,
+// capped so that a segment holds at most 2^kReduceStackDepth batches of 8.
+__host__ __device__ inline uint64_t rows_segment_len(uint64_t m, int S)
+{
+    uint64_t rs = 1;
+    while (rs * (uint64_t)S < m && rs < (8ull << kReduceStackDepth)) rs *= 2;
+    return rs;
+}
+
+// Whether the general row kernel can reduce rows of `cols` elements (its
+// round stack bounds the row length; see kRowsRoundDepth).
+inline bool reduce_rows_supported(uint64_t cols, uint32_t L)
+{
+    int lp_log = 0;
+    while ((1ull << lp_log) < L) ++lp_log;
+    const int S = kRowsThreads >> (lp_log < 8 ? lp_log : 8);
+    const uint64_t m = (cols + L - 1) / L;
+    const uint64_t span = rows_segment_len(m, S) * S;
+    return (m + span - 1) / span < (1ull << (kRowsRoundDepth + 1));
+}
+
 inline uint64_t reduce_partials_bytes(const ReducePlan& pl, uint32_t L, size_t elem_size)
 {
     return pl.P * (uint64_t)L * elem_size;

@@ -20,6 +20,7 @@
 //      in range order, PW over lanes, then init + R.
 #pragma once
 #include "device.hpp"
+#include "launch.hpp"
 #include "reduce.hpp"
 
 namespace canon {
@@ -331,14 +332,48 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_finish(const T* __res
 }
 
 // ============================================================================
-// Row-batched reduce: one workgroup per row.  Lanes
-// are processed in chunks of LW = min(Lp, 256); S = 256 / LW threads share a
-// lane, each over an aligned segment of the row's rows-of-L.  Lane values of
-// a chunk are merged in LDS to the chunk's complete subtree, and chunk values
-// are merged across chunks with a binary-counter stack (the cross-lane PW
-// over aligned chunks of lanes).
+// Row-batched reduce: one workgroup per row.  Lanes are processed in chunks
+// of LW = min(Lp, 256); S = 256 / LW threads share a lane, each over an
+// aligned segment of rs rows-of-L (rs a power of two, at most
+// 8 << kReduceStackDepth so that a segment's batches fit its stack).  The S
+// segments of a "round" (rs * S aligned rows) are merged in LDS to the
+// round's complete subtree per lane; LONG rows (more than one round) merge
+// their rounds, per lane, with a second binary-counter stack.  Lane values of
+// a chunk are then merged in LDS to the chunk's complete subtree, and chunk
+// values across chunks with a binary-counter stack (the cross-lane PW over
+// aligned chunks of lanes).
 // ============================================================================
 template <typename T>
+__device__ __forceinline__ T rows_segment(const T* __restrict__ xr, uint64_t cols, uint32_t L,
+                                          uint64_t j, uint64_t m, uint64_t r0, uint64_t r1)
+{
+    T v[1];
+    uint64_t nb = 0;
+    TreeStack<T, 1, kReduceStackDepth> st;
+    if (j < L && r0 < m) {
+        const uint64_t rend = r1 < m ? r1 : m;
+        nb = (rend - r0 + 7) / 8;
+        for (uint64_t k = 0; k < nb; ++k) {
+            T a[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint64_t r = r0 + k * 8 + u;
+                const uint64_t el = r * L + j;
+                a[u] = (r < r1 && el < cols) ? xr[el] : neg_zero<T>();
+            }
+#pragma unroll
+            for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+                for (int u = 0; u < 8; u += 2 * h) a[u] = a[u] + a[u + h];
+            v[0] = a[0];
+            st.push(k, v);
+        }
+    }
+    st.collapse(nb, v);
+    return v[0];
+}
+
+template <typename T, bool LONG>
 __global__ __launch_bounds__(kRowsThreads) void k_reduce_rows(const T* __restrict__ x,
                                                               uint64_t rows, uint64_t cols,
                                                               uint64_t ldx, uint32_t L, int lw_log,
@@ -349,8 +384,9 @@ __global__ __launch_bounds__(kRowsThreads) void k_reduce_rows(const T* __restric
     const int LW = 1 << lw_log, S = kRowsThreads >> lw_log;
     const int jl = t & (LW - 1), s = t >> lw_log;
     const uint64_t m = (cols + L - 1) / L;
-    uint64_t rs = 1;
-    while (rs * S < m) rs *= 2;
+    const uint64_t rs = rows_segment_len(m, S);
+    const uint64_t span = rs * S;  // rows of one round
+    const uint64_t nrounds = LONG ? (m + span - 1) / span : 1;
     const uint64_t nchunks = (L + LW - 1) / LW;
 
     for (uint64_t row = blockIdx.x; row < rows; row += gridDim.x) {
@@ -359,34 +395,26 @@ __global__ __launch_bounds__(kRowsThreads) void k_reduce_rows(const T* __restric
         T cv[1];
         for (uint64_t ch = 0; ch < nchunks; ++ch) {
             const uint64_t j = ch * LW + jl;
-            const uint64_t r0 = s * rs, r1 = r0 + rs;
-            T v[1];
-            uint64_t nb = 0;
-            TreeStack<T, 1, kReduceStackDepth> st;
-            if (j < L && r0 < m) {
-                const uint64_t rend = r1 < m ? r1 : m;
-                nb = (rend - r0 + 7) / 8;
-                for (uint64_t k = 0; k < nb; ++k) {
-                    T a[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const uint64_t r = r0 + k * 8 + u;
-                        const uint64_t el = r * L + j;
-                        a[u] = (r < r1 && el < cols) ? xr[el] : neg_zero<T>();
-                    }
-#pragma unroll
-                    for (int h = 1; h < 8; h *= 2)
-#pragma unroll
-                        for (int u = 0; u < 8; u += 2 * h) a[u] = a[u] + a[u + h];
-                    v[0] = a[0];
-                    st.push(k, v);
+            TreeStack<T, 1, LONG ? kRowsRoundDepth : 0> rst;
+            T rv[1];
+            for (uint64_t rd = 0; rd < nrounds; ++rd) {
+                const uint64_t r0 = rd * span + s * rs;
+                s_v[t] = rows_segment(xr, cols, L, j, m, r0, r0 + rs);
+                __syncthreads();
+                for (int h = 1; h < S; h *= 2) {
+                    if (s % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h * LW];
+                    __syncthreads();
+                }
+                if constexpr (LONG) {
+                    // the round's subtree of lane j, at s_v[jl]
+                    rv[0] = s_v[jl];
+                    rst.push(rd, rv);
+                    __syncthreads();  // s_v is rewritten by the next round
                 }
             }
-            st.collapse(nb, v);
-            s_v[t] = v[0];
-            __syncthreads();
-            for (int h = 1; h < S; h *= 2) {
-                if (s % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h * LW];
+            if constexpr (LONG) {
+                rst.collapse(nrounds, rv);
+                if (s == 0) s_v[t] = rv[0];
                 __syncthreads();
             }
             for (int h = 1; h < LW; h *= 2) {
@@ -473,6 +501,7 @@ static hipError_t launch_rows_pow2(const T* x, uint64_t rows, uint64_t cols, uin
     constexpr int RPB = kRowsThreads / 64;  // rows per workgroup
     uint64_t grid = (rows + RPB - 1) / RPB;
     if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
+    grid = capped_grid(grid);
     hipLaunchKernelGGL((k_reduce_rows_pow2<T, LOGL>), dim3((unsigned)grid), dim3(kRowsThreads), 0,
                        s, x, rows, cols, ldx, init, out);
     return hipGetLastError();
@@ -550,12 +579,17 @@ hipError_t launch_reduce_rows(const T* x, uint64_t rows, uint64_t cols, uint64_t
     if ((1ull << lp_log) == L && lp_log <= Elem<T>::LOGE + 6 && aligned &&
         cols <= (batch_elems << kRowsStackDepth))
         return launch_rows_pow2_dispatch<T, 0>(lp_log, x, rows, cols, ldx, init, out, s);
-    int lw_log = lp_log < 8 ? lp_log : 8;
-    constexpr auto kern = k_reduce_rows<T>;
+    const int lw_log = lp_log < 8 ? lp_log : 8;
+    const int S = kRowsThreads >> lw_log;
+    const uint64_t m = (cols + L - 1) / L;
     // one workgroup per row (the kernel strides over rows past the grid limit)
-    const uint64_t grid = rows < 0x7FFFFFFFull ? rows : 0x7FFFFFFFull;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRowsThreads), 0, s, x, rows, cols, ldx, L,
-                       lw_log, init, out);
+    const uint64_t grid = capped_grid(rows < 0x7FFFFFFFull ? rows : 0x7FFFFFFFull);
+    if (rows_segment_len(m, S) * S >= m)
+        hipLaunchKernelGGL((k_reduce_rows<T, false>), dim3((unsigned)grid), dim3(kRowsThreads), 0,
+                           s, x, rows, cols, ldx, L, lw_log, init, out);
+    else
+        hipLaunchKernelGGL((k_reduce_rows<T, true>), dim3((unsigned)grid), dim3(kRowsThreads), 0,
+                           s, x, rows, cols, ldx, L, lw_log, init, out);
     return hipGetLastError();
 }
 

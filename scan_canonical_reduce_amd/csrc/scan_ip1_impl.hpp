@@ -414,7 +414,7 @@ static hipError_t launch_ip1_al(const T* x, uint64_t ldx, T* y, uint64_t ldy, ui
     constexpr auto kern = k_ip_single<T, LOGRV, OUTX, PIPE, AL>;
     uint64_t grid = items;
     if (PIPE) {
-        const uint64_t fit = resident_grid<kern>(kIpThreads);
+        const uint64_t fit = capped_grid(resident_grid<kern>(kIpThreads));
         if (grid > fit) grid = fit;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kIpThreads), 0, s, x, ldx, y, ldy, cols,

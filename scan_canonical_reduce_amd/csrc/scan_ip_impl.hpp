@@ -33,6 +33,7 @@
 // Row-batched scans run the same kernels with one segment per row.
 #pragma once
 #include "device.hpp"
+#include "launch.hpp"
 #include "scan.hpp"
 #include "scan_ip.hpp"
 
@@ -209,7 +210,7 @@ static hipError_t launch_ip_nodes(T* nodes, const IpLayout& lay, hipStream_t s)
     for (int k0 = 0; k0 + 1 < lay.levels; k0 += kIpLevelsPerPass) {
         const uint64_t blocks = (lay.cnt[k0] + (1u << kIpLevelsPerPass) - 1) >> kIpLevelsPerPass;
         const uint64_t nit = lay.nseg * blocks;
-        const unsigned g = (unsigned)(nit < kIpMaxGrid ? nit : kIpMaxGrid);
+        const unsigned g = (unsigned)capped_grid(nit < kIpMaxGrid ? nit : kIpMaxGrid);
         hipLaunchKernelGGL((k_ip_nodes<T>), dim3(g), dim3(kIpThreads), 0, s, nodes, lay, k0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -225,7 +226,7 @@ static hipError_t launch_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64
 {
     if (lay.fast_logrv >= 0) return hipErrorInvalidValue;  // the single pass serves it
     const uint64_t items = lay.nseg * lay.tps;
-    const unsigned grid = (unsigned)(items < kIpMaxGrid ? items : kIpMaxGrid);
+    const unsigned grid = (unsigned)capped_grid(items < kIpMaxGrid ? items : kIpMaxGrid);
     hipLaunchKernelGGL((k_ip_totals<T>), dim3(grid), dim3(kIpThreads), 0, s, x, ldx, cols, err,
                        nodes, lay);
     hipError_t e = hipGetLastError();

@@ -769,7 +769,7 @@ static hipError_t launch_k(const T* x, T* y, uint64_t n, int b_log, uint64_t* ws
                            hipStream_t s)
 {
     constexpr auto kern = k_scan<P, T>;
-    uint64_t grid = resident_grid<kern>(kScanThreads, shmem);
+    uint64_t grid = capped_grid(resident_grid<kern>(kScanThreads, shmem));
     if (grid > lay.ntiles) grid = lay.ntiles;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), shmem, s, x, y, n, b_log,
                        ws, lay, out.init, out.kind);

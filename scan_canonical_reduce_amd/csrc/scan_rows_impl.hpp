@@ -3,6 +3,7 @@
 // "Key Design Points").  The in-tile network is ScanTile (scan_tile.hpp).
 #pragma once
 #include "device.hpp"
+#include "launch.hpp"
 #include "scan.hpp"
 #include "scan_tile.hpp"
 
@@ -78,7 +79,7 @@ static hipError_t launch_scan_rows_k(const T* x, uint64_t ldx, T* y, uint64_t ld
 {
     constexpr auto kern = k_scan_rows<T, MODE, ALIGNED, scan_rows_log_v<T>(), OUTX>;
     // one workgroup per row (the kernel strides over rows past the grid limit)
-    const uint64_t grid = rows < 0x7FFFFFFFull ? rows : 0x7FFFFFFFull;
+    const uint64_t grid = capped_grid(rows < 0x7FFFFFFFull ? rows : 0x7FFFFFFFull);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kScanThreads), 0, s, x, ldx, y, ldy, rows,
                        cols, b_log, out.init, out.kind);
     return hipGetLastError();

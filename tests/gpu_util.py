@@ -35,3 +35,20 @@ def assert_bit_exact(got, want, what=""):
         raise AssertionError(
             f"{what}: {bad.size} of {g.size} values differ; first at {i}: "
             f"got {g[i]!r} ({bits(g[i:i+1])[0]:#x}) want {w[i]!r} ({bits(w[i:i+1])[0]:#x})")
+
+
+def scan_tile(dtype, policy="pairwise", param=0) -> int:
+    """Elements per tile of the library's 1-d scans for this element type
+    (canon_scan_tile_elems): the edge cases sit on its multiples."""
+    import scan_canonical_reduce_amd as c
+    t = c.scan_tile_elems(policy, param, np.dtype(dtype).itemsize)
+    assert t > 0
+    return t
+
+
+def scan_rows_tile(dtype, policy="pairwise", param=0) -> int:
+    """Elements per tile within a row of the library's row scans."""
+    import scan_canonical_reduce_amd as c
+    t = c.scan_rows_tile_elems(policy, param, np.dtype(dtype).itemsize)
+    assert t > 0
+    return t

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(canon):
 
 def test_version_and_status_strings(canon):
     L = canon.lib()
-    assert L.canon_abi_version() == 3
+    assert L.canon_abi_version() == 4
     for s in range(5):
         assert L.canon_status_str(s).decode().startswith("CANON_")
     assert L.canon_last_hip_error() == 0
@@ -82,6 +82,10 @@ def test_reduce_argument_errors(canon):
     assert _call_reduce(L, fake, 1 << 20, 16, fake, fake, need - 1) == 3
     assert L.canon_reduce_rows_f64(fake, 4, 10, 9, 4, 0.0, fake, None, 0, None) == 1  # ld < cols
     assert L.canon_reduce_rows_f64(fake, 4, 10, 10, 0, 0.0, fake, None, 0, None) == 1
+    # rows longer than the general row kernel's round stack covers (2^25
+    # rounds of 2^21 rows-of-1): rejected before launch
+    big = 1 << 47
+    assert L.canon_reduce_rows_f64(fake, 2, big, big, 1, 0.0, fake, None, 0, None) == 2
 
 
 def test_scan_argument_errors(canon):
@@ -141,6 +145,74 @@ def test_operator_argument_errors(canon):
     assert L.canon_scan_rows_op_f64(fake, 10, fake, 10, 3, 10, 0, 0, 3, 2, 0.0, None, 0,
                                     None) == 1                                   # ldy < cols+1
     assert L.canon_reduce_rows_op_f32(fake, 4, 10, 9, 4, 1, 0.0, fake, None, 0, None) == 1
+
+
+def test_tile_geometry(canon):
+    """Tile sizes the tests place their edge cases on: 4 waves x 64 lanes x
+    16 vectors of 16 bytes for the 1-d scans, 8 vectors for double rows;
+    iterated_pairwise tiles of 64 / RV rows (register geometry) or of the
+    rows whose lane trees fit the LDS budget."""
+    L = canon.lib()
+    for pol, par in ((0, 0), (2, 1), (2, 16), (2, 256), (2, 65536), (1, 1)):
+        assert L.canon_scan_tile_elems(pol, par, 8) == 8192
+        assert L.canon_scan_tile_elems(pol, par, 4) == 16384
+    assert L.canon_scan_rows_tile_elems(2, 16, 8) == 4096
+    assert L.canon_scan_rows_tile_elems(0, 0, 4) == 16384
+    assert L.canon_scan_tile_elems(1, 128, 8) == 64 * 128     # RV = 1
+    assert L.canon_scan_tile_elems(1, 512, 8) == 16 * 512     # RV = 4
+    assert L.canon_scan_tile_elems(1, 256, 4) == 64 * 256
+    assert L.canon_scan_tile_elems(1, 3, 8) == 64 * 3         # LDS path, 64 rows
+    assert L.canon_scan_tile_elems(1, 2048, 8) == 1 * 2048    # LDS path, 1 row
+    assert L.canon_scan_rows_tile_elems(1, 16, 8) == 64 * 16
+    assert L.canon_scan_tile_elems(7, 0, 8) == 0
+    assert L.canon_scan_tile_elems(2, 12, 8) == 0
+    assert L.canon_scan_tile_elems(0, 0, 2) == 0
+
+
+def test_schedule_override(canon):
+    L = canon.lib()
+    assert L.canon_get_schedule(0) == 0 and L.canon_get_schedule(1) == 0
+    with canon.schedule(grid=3, reduce_partials=7):
+        assert L.canon_get_schedule(0) == 3
+        assert L.canon_get_schedule(1) == 7
+    assert L.canon_get_schedule(0) == 0 and L.canon_get_schedule(1) == 0
+    default = L.canon_reduce_workspace_bytes(1 << 24, 16, 8)
+    with canon.schedule(reduce_partials=4096):
+        assert L.canon_reduce_workspace_bytes(1 << 24, 16, 8) > default
+    assert L.canon_set_schedule(2, 1) == 1
+    assert L.canon_get_schedule(9) == 0
+
+
+def _gpu_count():
+    import torch
+    return torch.cuda.device_count()  # counts devices without initialising HIP
+
+
+@pytest.mark.skipif(_gpu_count() > 0, reason="needs a host without a GPU: the launch must fail")
+def test_launch_failure_maps_to_ehip(canon):
+    """Valid arguments on a host with no GPU: the enqueue fails, the call
+    returns CANON_EHIP and the HIP code is kept for this thread only."""
+    import threading
+    L = canon.lib()
+    fake = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x100000)
+    n = 1 << 20
+    need = L.canon_reduce_workspace_bytes(n, 16, 8)
+    assert L.canon_reduce_f64(fake, n, 16, 0.0, fake, ws, need, None) == 4
+    code = L.canon_last_hip_error()
+    assert code != 0
+    assert "HIP" in L.canon_status_str(4).decode()
+    need = L.canon_scan_workspace_bytes(n, 2, 256, 8)
+    assert L.canon_scan_f64(fake, fake, n, 2, 256, ws, need, None) == 4
+    assert L.canon_scan_rows_f64(fake, 4096, fake, 4096, 16, 4096, 0, 0, None, 0, None) == 4
+    other = []
+    t = threading.Thread(target=lambda: other.append(L.canon_last_hip_error()))
+    t.start()
+    t.join()
+    assert other == [0]
+    # the binding turns it into an exception naming the HIP code
+    with pytest.raises(canon.CanonError, match="hip error"):
+        canon._check(4, "reduce")
 
 
 def test_binding_refuses_cpu_tensors(canon):

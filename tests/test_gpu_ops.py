@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_bit_exact, to_dev, to_host  # noqa: E402
+from gpu_util import assert_bit_exact, scan_tile, to_dev, to_host  # noqa: E402
 
 OPS = ["mul", "min", "max"]
 KINDS = ["inclusive", "exclusive", "include_initial"]
@@ -36,7 +36,7 @@ def data(op, n, seed, dtype):
 
 
 def tile(dtype):
-    return 4096 if dtype == np.float64 else 16384
+    return scan_tile(dtype)  # elements per single-pass tile
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])

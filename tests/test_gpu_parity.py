@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_bit_exact, to_dev, to_host  # noqa: E402
+from gpu_util import assert_bit_exact, scan_rows_tile, scan_tile, to_dev, to_host  # noqa: E402
 
 DT = {np.float64: torch.float64, np.float32: torch.float32}
 
@@ -143,6 +143,22 @@ def test_reduce_rows_long_rows(canon, dtype):
         assert_bit_exact(got, oracle.reduce_rows(X, 16, -2.5, cols=cols), f"cols={cols}")
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [1, 3, 16])
+def test_reduce_rows_several_rounds(canon, dtype, L):
+    """Rows the general row kernel covers in several rounds: each thread's
+    segment is capped at 2^13 rows-of-L (its batch stack's depth), so a row
+    of more than 2^13 * S rows-of-L (S = 256 / min(Lp, 256) threads per lane)
+    is reduced round by round, the rounds merged per lane.  2^21 + 17
+    columns: two rounds for L = 1, 3 and 16; 3 * 2^21 + 5: four to six."""
+    for cols in ((1 << 21) + 17, 3 * (1 << 21) + 5):
+        rows, ld = 2, cols + 3
+        X = synth.generate(rows * ld, "mixed_magnitude", 48 + L + cols % 7, dtype).reshape(rows, ld)
+        print(f"[rows rounds] L={L} cols={cols} {np.dtype(dtype).name}", flush=True)
+        got = to_host(canon.reduce_rows(to_dev(X)[:, :cols], L, 0.1))
+        assert_bit_exact(got, oracle.reduce_rows(X, L, 0.1, cols=cols), f"cols={cols}")
+
+
 def test_reduce_rows_shape_of_workload(canon):
     rows, cols = 2048, 4096
     X = synth.generate(rows * cols, "uniform_pm1", 1004).reshape(rows, cols)
@@ -177,7 +193,7 @@ def test_scan_1m_uniform(canon, policy, param):
                                           ("block_dyadic", 256), ("block_dyadic", 4096),
                                           ("block_dyadic", 8192), ("block_dyadic", 65536)])
 def test_scan_tails(canon, dtype, policy, param):
-    S = 4096 if dtype == np.float64 else 16384  # elements per scan tile
+    S = scan_tile(dtype, policy, param)  # elements per scan tile
     x = synth.generate(70 * S + 999, "mixed_magnitude", 12, dtype)
     want_all = oracle.scan(x, policy, param)
     for n in (1, 2, 3, 17, S - 1, S, S + 1, 3 * S + 5, 64 * S - 1, 64 * S, 64 * S + 1, 65 * S + 17,
@@ -190,7 +206,7 @@ def test_scan_tails(canon, dtype, policy, param):
 def test_scan_every_block_size(canon, dtype):
     """Every B = 2^b from 1 to beyond one tile: the fork to block values falls
     at every level inside and above the tile; several tiles, a ragged tail."""
-    S = 4096 if dtype == np.float64 else 16384
+    S = scan_tile(dtype)
     x = synth.generate(5 * S + 123, "mixed_magnitude", 18, dtype)
     for b in range(0, 17):
         B = 1 << b
@@ -256,7 +272,7 @@ def test_scan_rows(canon, dtype, policy, param):
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_scan_rows_every_block_size(canon, dtype):
-    S = 4096 if dtype == np.float64 else 16384
+    S = scan_rows_tile(dtype)
     rows, cols, ld = 5, 2 * S + 77, 2 * S + 128
     X = synth.generate(rows * ld, "mixed_magnitude", 19, dtype).reshape(rows, ld)
     Xd = to_dev(X)

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_bit_exact, to_dev, to_host  # noqa: E402
+from gpu_util import assert_bit_exact, scan_tile, to_dev, to_host  # noqa: E402
 
 KINDS = ["inclusive", "exclusive", "include_initial"]
 
@@ -29,7 +29,7 @@ def canon():
 
 
 def tile(dtype):
-    return 4096 if dtype == np.float64 else 16384  # elements per single-pass tile
+    return scan_tile(dtype)  # elements per single-pass tile
 
 
 def expect(x, policy, param, kind, init, n):

@@ -123,6 +123,60 @@ def test_scan(skew, canon, dtype, policy, param):
     assert_bit_exact(got, oracle.scan(x[1:], policy, param, "skew"), "unaligned")
 
 
+# Every kernel family past 64 tiles (the 64-tile group rebuild, climbs to
+# node levels 7 and 8, the right-spine composition, iterated_pairwise node
+# levels 3 and up): FullTile (pairwise; block_dyadic<2> in float),
+# SplitTile (block_dyadic<16>, and B of four tiles: one block over several
+# tiles), WideTile (block_dyadic<256>), the one-pass iterated_pairwise kernel
+# (L = 128 double, 256 both: pipelined and one tile per workgroup), the
+# three-kernel iterated_pairwise path (L = 3, 100).
+LARGE_SCANS = [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16), ("block_dyadic", 256),
+               ("block_dyadic", 65536), ("iterated_pairwise", 128), ("iterated_pairwise", 256),
+               ("iterated_pairwise", 3), ("iterated_pairwise", 100)]
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("policy,param", LARGE_SCANS)
+def test_scan_large(skew, canon, dtype, policy, param):
+    """2^22 + 4097 elements (512 double or 256 float tiles and a ragged
+    tail), every output kind, and an unaligned start."""
+    n = (1 << 22) + 4097
+    x = data(n + 1, 94, dtype)
+    xd = to_dev(x)
+    for kind in KINDS:
+        print(f"[skew large] {np.dtype(dtype).name} {policy}<{param}> {kind}", flush=True)
+        got = scan(skew, canon, xd[:n], policy, param, kind, 0.5)
+        want = oracle.scan_with_init(x[:n], policy, param, 0.5, kind, "skew")
+        assert_bit_exact(got, want, f"{kind}")
+    got = scan(skew, canon, xd[1:], policy, param, "inclusive", -0.0)
+    assert_bit_exact(got, oracle.scan(x[1:], policy, param, "skew"), "unaligned")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_rows_many_tiles(skew, canon, dtype):
+    """Row scans whose rows span many tiles (the row kernel's stack of tile
+    nodes up to level 6; the iterated_pairwise row segments), every kind."""
+    rows, cols = 6, (1 << 19) + 4099
+    ld = cols + 1
+    X = data(rows * ld, 95, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    e = Xd.element_size()
+    for policy, param in (("pairwise", 0), ("block_dyadic", 16), ("block_dyadic", 256),
+                          ("iterated_pairwise", 128), ("iterated_pairwise", 3)):
+        for kind in KINDS:
+            print(f"[skew rows] {np.dtype(dtype).name} {policy}<{param}> {kind}", flush=True)
+            Y = torch.empty(rows, ld, dtype=Xd.dtype, device="cuda")
+            nb = canon.scan_rows_workspace_bytes(rows, cols, policy, param, e)
+            ws = ws_tensor(nb)
+            st = getattr(skew, f"canon_skew_scan_rows_{sfx(Xd)}")(
+                Xd.data_ptr(), ld, Y.data_ptr(), ld, rows, cols, POL[policy], param, KINDS[kind],
+                0.75, ws.data_ptr(), nb, stream())
+            assert st == 0, st
+            want = oracle.scan_rows_with_init(X, policy, param, 0.75, kind, cols=cols, op="skew")
+            ycols = cols + (kind == "include_initial")
+            assert_bit_exact(to_host(Y)[:, :ycols], want[:, :ycols], f"{policy} {kind}")
+
+
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_rows(skew, canon, dtype):
     rows = 19
