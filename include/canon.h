@@ -262,6 +262,25 @@ canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* st
 size_t canon_scan_tile_elems(int policy, uint32_t param, size_t elem_size);
 size_t canon_scan_rows_tile_elems(int policy, uint32_t param, size_t elem_size);
 
+/* ------------------------------------------------------- no allocation */
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the plain
+ * scan canon_scan_f64 with its workspace in a static device array of the
+ * library, CANON_NOALLOC_SCRATCH_BYTES (8 MiB) per device, held from the
+ * first call on a device until the process ends.  Nothing is allocated by
+ * the call.  Same arguments (minus ws / ws_bytes), results (bit for bit) and
+ * errors as canon_scan_f64, plus CANON_EUNSUPPORTED when the scan needs more
+ * than the array, i.e. canon_scan_workspace_bytes(n, policy, param, 8) >
+ * CANON_NOALLOC_SCRATCH_BYTES (pairwise and block_dyadic up to about 8.4e9
+ * elements, iterated_pairwise<128> up to 2^23, iterated_pairwise<16> up to
+ * about 3.3e7).  Every call on one
+ * device shares the array, which keeps the last call's contents: calls that
+ * may overlap on one device (other streams, other host threads) race, and
+ * the error word of canon_workspace_error is not available. */
+#define CANON_NOALLOC_SCRATCH_BYTES (8u << 20)
+canon_status_t canon_scan_noalloc_f64(const double* x, double* y, size_t n, int policy,
+                                      uint32_t param, void* stream);
+
 /* ------------------------------------------------------ schedule override */
 /* Process-wide override of how work is spread over workgroups, for tests
  * that show the results do not depend on the schedule (P4016R0 "Summary":

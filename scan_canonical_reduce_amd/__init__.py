@@ -69,7 +69,7 @@ EXPORTS = [
     "canon_reduce_rows_op_f32", "canon_scan_op_f64", "canon_scan_op_f32",
     "canon_scan_rows_op_f64", "canon_scan_rows_op_f32",
     "canon_workspace_error", "canon_scan_tile_elems", "canon_scan_rows_tile_elems",
-    "canon_set_schedule", "canon_get_schedule",
+    "canon_set_schedule", "canon_get_schedule", "canon_scan_noalloc_f64",
 ]
 
 ABI_VERSION = 4
@@ -133,6 +133,7 @@ def lib() -> ctypes.CDLL:
     L.canon_set_schedule.argtypes = [I, ctypes.c_uint64]
     L.canon_get_schedule.argtypes = [I]
     L.canon_get_schedule.restype = ctypes.c_uint64
+    L.canon_scan_noalloc_f64.argtypes = [P, P, S, I, U, P]
     for name in EXPORTS:
         if name not in ("canon_abi_version", "canon_status_str", "canon_last_hip_error",
                         "canon_scan_tile_elems", "canon_scan_rows_tile_elems",

@@ -19,7 +19,7 @@ SOURCES = [
     "api.cpp", "reduce.hip", "scan.hip", "scan_with_init.hip", "scan_wide.hip",
     "scan_wide_init.hip", "scan_rows.hip", "scan_ip.hip", "scan_ip1.hip",
     "ops_mul_f64.hip", "ops_mul_f32.hip", "ops_min_f64.hip", "ops_min_f32.hip",
-    "ops_max_f64.hip", "ops_max_f32.hip",
+    "ops_max_f64.hip", "ops_max_f32.hip", "scan_noalloc.cpp",
 ]
 
 # -ffp-contract=off: no FMA contraction; no fast-math; subnormals kept (no

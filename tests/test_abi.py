@@ -215,6 +215,27 @@ def test_launch_failure_maps_to_ehip(canon):
         canon._check(4, "reduce")
 
 
+def test_noalloc_scan_limits(canon):
+    """The allocation-free scan checks its arguments as canon_scan_f64 does
+    and rejects scans whose workspace exceeds its static array, before
+    anything is enqueued."""
+    L = canon.lib()
+    fake = ctypes.c_void_p(0x1000)
+    cap = 8 << 20
+    f = L.canon_scan_noalloc_f64
+    assert f(fake, fake, 10, 7, 0, None) == 1            # bad policy
+    assert f(fake, fake, 10, 2, 12, None) == 1           # B not a power of two
+    assert f(None, fake, 10, 0, 0, None) == 1            # no input
+    assert f(None, None, 0, 0, 0, None) == 0             # nothing to do
+    for pol, par in ((0, 0), (2, 256), (1, 128)):
+        n = 1 << 20
+        while L.canon_scan_workspace_bytes(n, pol, par, 8) <= cap:
+            n *= 2
+        assert f(fake, fake, n, pol, par, None) == 2     # beyond the static array
+    assert L.canon_scan_workspace_bytes(1 << 32, 0, 0, 8) <= cap
+    assert L.canon_scan_workspace_bytes(1 << 23, 1, 128, 8) <= cap
+
+
 def test_binding_refuses_cpu_tensors(canon):
     import torch
     x = torch.zeros(8, dtype=torch.float64)
