@@ -11,9 +11,20 @@ synthetic input:
   rows_reduce     16384 rows x 4096, L = 16                (f64)
   rows_scan_bd16  16384 rows x 4096, block_dyadic<16>      (f64)
 value = algorithmic bytes of the step / time of the step (GB/s); reduce
-reads N*8 bytes, a scan reads and writes N*8 bytes each.  Before timing,
-every result is checked bit for bit against the CPU oracle (full reduce,
-sampled scan prefixes evaluated from scratch).
+reads N*8 bytes, a scan reads and writes N*8 bytes each (value_n2e28: the
+same over the N = 2^28 ops alone).  Before timing, every result is checked
+bit for bit against the CPU oracle: the full reduce and row reduce, 64 rows
+of the row scan in full, and for every scan 24 mid-block prefixes evaluated
+from scratch (the witness method of the canonical-scan README: output hash
+and mid-block probe values) plus the scan's back element against the GPU
+reduce of the same expression; the witness (output SHA-256, probes PASS
+count) goes into the JSON line.
+
+The practical ceilings (bw_probe.hip: a streaming read and a streaming copy
+with the scans' tile pattern) are measured in the same run and every op is
+also reported as a fraction of its ceiling; the benchmark spec's target, the
+float block_dyadic<256> scan at N = 2^28 (>= 60% of peak), is timed on its
+own input (median and 90th percentile of 50 calls) under "targets".
 
 Inside the timed steps every op is bracketed by HIP events on the stream it
 runs on; the op with the largest mean time is the dominant kernel of the
@@ -24,6 +35,7 @@ kernel sources as they are now (their SHA-256 is stored with it), else null.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-check]
        python bench.py --only copy ...   (a 2 GiB device copy: the reference
                                           for scaling the PMC byte counters)
+       python bench.py --only ceiling    (the read and copy ceiling probes)
 """
 from __future__ import annotations
 
@@ -54,6 +66,8 @@ def kernel_sources_sha256() -> str:
     d = os.path.join(ROOT, "scan_canonical_reduce_amd", "csrc")
     for p in sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.hpp")) +
                     glob.glob(os.path.join(d, "*.cpp"))):
+        if os.path.basename(p) == "bw_probe.hip":  # the benchmark's probe, not the library
+            continue
         h.update(os.path.basename(p).encode())
         h.update(open(p, "rb").read())
     return h.hexdigest()
@@ -84,6 +98,110 @@ def read_traffic(op: str):
                 "source": os.path.relpath(path, ROOT)}
     except (KeyError, ValueError):
         return None
+
+
+PROBE_LIB = os.path.join(ROOT, "scan_canonical_reduce_amd", "libcanon_bwprobe.so")
+N_PROBES = 24
+
+
+def mid_block_probes(n: int, k: int = N_PROBES) -> np.ndarray:
+    """k prefix positions, each in the middle of one of k equal blocks of the
+    output (the README's mid-block probes), as int64."""
+    return np.array([((2 * j + 1) * n) // (2 * k) for j in range(k)], dtype=np.int64)
+
+
+def parallel_values(fn, idx, dtype, threads=8):
+    """fn(i) for every index on a few host threads (the oracle's C code runs
+    outside the GIL), as an array of dtype."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        vals = list(ex.map(lambda i: fn(int(i)), idx))
+    return np.array(vals, dtype=dtype)
+
+
+def literal_prefixes(oracle, x_np, idx, policy, param, threads=8):
+    """oracle.scan_prefix (each prefix evaluated from scratch) at every index."""
+    return parallel_values(lambda i: oracle.scan_prefix(x_np, i, policy, param), idx,
+                           x_np.dtype, threads)
+
+
+def hex_bits(a) -> list:
+    a = np.asarray(a)
+    u = np.uint64 if a.dtype == np.float64 else np.uint32
+    w = 16 if a.dtype == np.float64 else 8
+    return [f"{int(v):0{w}x}" for v in a.view(u)]
+
+
+def bits_equal(a, b) -> np.ndarray:
+    a = np.asarray(a)
+    b = np.asarray(b, dtype=a.dtype)
+    u = np.uint64 if a.dtype == np.float64 else np.uint32
+    return a.view(u) == b.view(u)
+
+
+# (vectors per thread, grid (0: one tile per workgroup), unused LDS bytes per
+# workgroup capping the workgroups per CU): the probe variants measured
+READ_VARIANTS = ((4, 512, 0), (8, 256, 0), (4, 0, 0))
+COPY_VARIANTS = ((2, 0, 40 << 10), (1, 0, 0), (4, 0, 32 << 10))
+
+
+def measure_ceiling(torch, dev, nbytes=N_MAIN * 8, reps=20, warmup=5):
+    """Read and copy ceilings (bw_probe.hip) over `nbytes`: for each variant
+    the median of `reps` calls bracketed by HIP events on the current stream;
+    the best variant of each kind is the ceiling."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, S, I, U = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
+    lib.canon_probe_read.argtypes = [P, S, I, U, U, P, P]
+    lib.canon_probe_copy.argtypes = [P, P, S, I, U, U, P]
+    a = torch.ones(nbytes // 8, dtype=torch.float64, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.empty(nbytes // (16 * 256) + 1, dtype=torch.int32, device=dev)  # per workgroup
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    def rate(fn, moved):
+        for _ in range(warmup):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda._sleep(HOST_AHEAD_SPIN)
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return moved / (ms[reps // 2] * 1e-3) / 1e9
+
+    out = {"variants": {}}
+    for kind, variants in (("read", READ_VARIANTS), ("copy", COPY_VARIANTS)):
+        best = None
+        for v, g, sh in variants:
+            if kind == "read":
+                fn = (lambda v=v, g=g, sh=sh: lib.canon_probe_read(
+                    a.data_ptr(), nbytes, v, g, sh, sink.data_ptr(), st))
+                r = rate(fn, nbytes)
+            else:
+                fn = (lambda v=v, g=g, sh=sh: lib.canon_probe_copy(
+                    a.data_ptr(), b.data_ptr(), nbytes, v, g, sh, st))
+                r = rate(fn, 2 * nbytes)
+            label = f"{kind} {v} vectors/thread, " + \
+                (f"grid {g}" if g else "one tile per workgroup") + \
+                (f", {sh >> 10} KiB LDS per workgroup" if sh else "")
+            out["variants"][label] = round(r, 1)
+            log(f"[bench] ceiling {label}: {r:.0f} GB/s")
+            if best is None or r > best[0]:
+                best = (r, label)
+        out[f"{kind}_GBps"] = round(best[0], 1)
+        out[f"{kind}_variant"] = best[1]
+    out["bytes"] = nbytes
+    out["probe"] = "scan_canonical_reduce_amd/csrc/bw_probe.hip"
+    del a, b, sink
+    return out
 
 
 def parse():
@@ -127,6 +245,9 @@ def main():
         return
 
     only = set(args.only.split(",")) if args.only else None
+    if only == {"ceiling"}:
+        print(json.dumps({"ceiling": measure_ceiling(torch, dev)}), flush=True)
+        return
     want_rows = only is None or bool(only & {"rows_reduce", "rows_scan_bd16"})
 
     # ------------------------------------------------------------ inputs
@@ -167,40 +288,58 @@ def main():
         ops = {k: v for k, v in ops.items() if k in only}
 
     # ------------------------------------------------------- parity gate
-    parity = {}
+    parity, witness = {}, {}
     if not args.no_check:
         import oracle
         t0 = time.time()
         rng = np.random.default_rng(2024)
-        probes = np.unique(np.concatenate([[0, 1, 4095, 4096, N_MAIN - 1],
-                                           rng.integers(0, N_MAIN, 3)]))
+        probes = mid_block_probes(N_MAIN)
         for name, (fn, _) in ops.items():
             if name == "copy":
                 continue
             fn()
             torch.cuda.synchronize()
+            w = {}
             if name == "reduce":
                 want = oracle.reduce(x_np, 128, 1.0)
-                ok = np.float64(r0.item()).tobytes() == np.float64(want).tobytes()
+                got = r0.cpu().numpy().reshape(1)
+                ok = bool(bits_equal(got, [want]).all())
+                w["sha256"] = synth.sha256(got)
             elif name == "rows_reduce":
                 want = oracle.reduce_rows(X_np, 16, 0.0)
-                ok = np.array_equal(rr.cpu().numpy().view(np.uint64), want.view(np.uint64))
+                got = rr.cpu().numpy()
+                ok = bool(bits_equal(got, want).all())
+                w["sha256"] = synth.sha256(got)
             elif name == "rows_scan_bd16":
                 idx = rng.integers(0, ROWS, 64)
-                got = Y[idx].cpu().numpy()
+                got = Y[torch.from_numpy(idx).to(dev)].cpu().numpy()
                 want = oracle.scan_rows(X_np[idx], "block_dyadic", 16)
-                ok = np.array_equal(got.view(np.uint64), want.view(np.uint64))
+                ok = bool(bits_equal(got, want).all())
+                w["rows_checked"] = 64
+                w["sha256"] = synth.sha256(Y.cpu().numpy())
             else:
                 _, p, q = [s for s in scans if s[0] == name][0]
                 err = canon.workspace_error(ws)
                 got = y[torch.from_numpy(probes).to(dev)].cpu().numpy()
-                want = np.array([oracle.scan_prefix(x_np, int(i), p, q) for i in probes])
-                ok = err == 0 and np.array_equal(got.view(np.uint64), want.view(np.uint64))
+                want = literal_prefixes(oracle, x_np, probes, p, q)
+                hits = bits_equal(got, want)
+                # the back element is the reduce of the same expression (a
+                # different kernel); every block size here divides 2^28
+                L = q if p == "iterated_pairwise" else 1
+                back = canon.reduce(x, L, -0.0).cpu().numpy().reshape(1)
+                back_ok = bool(bits_equal(y[-1:].cpu().numpy(), back).all())
+                ok = err == 0 and bool(hits.all()) and back_ok
+                w.update({"sha256": synth.sha256(y.cpu().numpy()), "probes": int(hits.size),
+                          "probes_pass": int(hits.sum()), "back_eq_reduce": back_ok,
+                          "error_word": int(err)})
             parity[name] = bool(ok)
-            log(f"[bench] parity {name}: {'PASS' if ok else 'FAIL'}")
+            w["pass"] = bool(ok)
+            witness[name] = w
+            log(f"[bench] parity {name}: {'PASS' if ok else 'FAIL'} {w}")
         log(f"[bench] parity gate {time.time() - t0:.1f}s")
         if not all(parity.values()):
-            print(json.dumps({"error": "parity gate failed", "parity": parity}))
+            print(json.dumps({"error": "parity gate failed", "parity": parity,
+                              "witness": witness}))
             sys.exit(1)
 
     # ------------------------------------------------------ step timing
@@ -250,6 +389,22 @@ def main():
         log(f"[bench] {name:15s} mean {mean * 1e3:9.1f} us  "
             f"{per_op[name]['GBps']:8.1f} GB/s  {per_op[name]['pct_hbm_peak']:5.1f}% of peak")
 
+    # the N = 2^28 ops alone (the rows ops are another shape)
+    n28 = [k for k in per_op if not k.startswith("rows_") and k != "copy"]
+    value_n2e28 = (sum(per_op[k]["bytes"] for k in n28) /
+                   (sum(per_op[k]["ms_mean"] for k in n28) * 1e-3) / 1e9) if n28 else None
+
+    # practical ceilings, and every op against its own (read for the
+    # reduces, copy for the scans)
+    ceiling = measure_ceiling(torch, dev)
+    if ceiling:
+        for k, v in per_op.items():
+            c = ceiling["read_GBps"] if "reduce" in k else ceiling["copy_GBps"]
+            v["pct_ceiling"] = 100.0 * v["GBps"] / c
+
+    targets = {} if only is not None else north_star_targets(torch, canon, synth, dev,
+                                                              args.no_check, x, x_np)
+
     # dominant kernel: the op with the largest mean time in the timed steps
     dom = max(per_op, key=lambda k: per_op[k]["ms_mean"])
     d = per_op[dom]
@@ -284,13 +439,83 @@ def main():
                    "n": N_MAIN, "rows": ROWS, "cols": COLS,
                    "ops": list(ops.keys())},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "value_n2e28": None if value_n2e28 is None else round(value_n2e28, 1),
+        "pct_hbm_peak_n2e28": None if value_n2e28 is None else
+        round(100.0 * value_n2e28 / HBM_PEAK_GBS, 2),
+        "ceiling": ceiling,
+        "targets": targets,
         "parity": parity,
+        "witness": witness,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in per_op.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def north_star_targets(torch, canon, synth, dev, no_check, x64, x64_np, reps=50, warmup=5):
+    """The two per-op targets of the workloads, each timed on its own input:
+    the f64 reduce at N = 2^28 (L = 128, init 1; >= 80% of peak) and the f32
+    block_dyadic<256> scan at N = 2^28 (>= 60% of peak).  `reps` calls each
+    bracketed by HIP events: median, p10, p90, and the fraction of peak at
+    the median and at p90.  The scan is checked first (24 mid-block prefixes
+    evaluated from scratch, back element against the GPU reduce)."""
+    import oracle
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda._sleep(HOST_AHEAD_SPIN)
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)  # us
+
+    def entry(t, nbytes, goal, ok):
+        med, p10, p90 = t[len(t) // 2], t[len(t) // 10], t[(9 * len(t)) // 10]
+        frac = nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS
+        frac90 = nbytes / (p90 * 1e-6) / 1e9 / HBM_PEAK_GBS
+        return {"us_median": round(med, 1), "us_p10": round(p10, 1), "us_p90": round(p90, 1),
+                "bytes": nbytes, "frac": round(frac, 4), "frac_at_p90": round(frac90, 4),
+                "target_frac": goal, "met_at_median": frac >= goal, "met_at_p90": frac90 >= goal,
+                "bit_exact": ok}
+
+    xn = synth.config_input("scan_2e28_f32")
+    x = torch.from_numpy(xn).to(dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(canon.scan_workspace_bytes(xn.size, "block_dyadic", 256, 4),
+                     dtype=torch.uint8, device=dev)
+    canon.scan(x, "block_dyadic", 256, out=y, ws=ws)
+    ok = canon.workspace_error(ws) == 0
+    if not no_check:
+        idx = mid_block_probes(xn.size)
+        got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
+        want = literal_prefixes(oracle, xn, idx, "block_dyadic", 256)
+        back = canon.reduce(x, 1, -0.0).cpu().numpy().reshape(1)
+        ok = ok and bool(bits_equal(got, want).all()) and \
+            bool(bits_equal(y[-1:].cpu().numpy(), back).all())
+    t = timed(lambda: canon.scan(x, "block_dyadic", 256, out=y, ws=ws))
+    out["scan_bd256_f32_n2e28"] = entry(t, 2 * xn.nbytes, 0.60, ok)
+    log(f"[bench] target scan_bd256_f32_n2e28: {out['scan_bd256_f32_n2e28']}")
+    del x, y, ws
+    xn, x = x64_np, x64  # the step's own N = 2^28 input
+    r = torch.empty((), dtype=x.dtype, device=dev)
+    ws = torch.empty(canon.reduce_workspace_bytes(xn.size, 128, 8), dtype=torch.uint8, device=dev)
+    canon.reduce(x, 128, 1.0, out=r, ws=ws)
+    ok = no_check or bool(bits_equal(r.cpu().numpy().reshape(1),
+                                     [oracle.reduce(xn, 128, 1.0)]).all())
+    t = timed(lambda: canon.reduce(x, 128, 1.0, out=r, ws=ws))
+    out["reduce_f64_n2e28"] = entry(t, xn.nbytes, 0.80, ok)
+    log(f"[bench] target reduce_f64_n2e28: {out['reduce_f64_n2e28']}")
+    return out
 
 
 SCRUB_BYTES = 512 << 20  # twice the 256 MB Infinity Cache (MALL)
@@ -308,7 +533,6 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
     neither L2 nor the MALL holds them ("MALL scrubbed" rows).  Prints one
     markdown table."""
     import oracle
-    rng = np.random.default_rng(7)
     stream = torch.cuda.current_stream()
     rows = []
     scrub_buf = []
@@ -350,10 +574,14 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
         u = np.uint64 if got.dtype == np.float64 else np.uint32
         return bool(np.array_equal(got.view(u), want.view(u)))
 
-    def add(cfg, op, dt, n, nbytes, t, ok):
+    witness = []
+
+    def add(cfg, op, dt, n, nbytes, t, ok, wit=None):
         us = t["median"]
         gbs = nbytes / (us * 1e-6) / 1e9
         rows.append((cfg, op, dt, n, t, gbs, 100.0 * gbs / HBM_PEAK_GBS, n / (us * 1e-6), ok))
+        if wit is not None and not cfg.endswith("MALL scrubbed"):
+            witness.append((cfg, op, dt, n, wit, ok))
         log(f"[configs] {cfg} {op}: median {us:.1f} us (p10 {t['p10']:.1f}, p90 {t['p90']:.1f}) "
             f"{gbs:.0f} GB/s parity {'PASS' if ok else 'FAIL'}")
 
@@ -365,9 +593,11 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
             ws = torch.empty(max(canon.reduce_workspace_bytes(xn.size, L, xn.itemsize), 1),
                              dtype=torch.uint8, device=dev)
             canon.reduce(x, L, init, out=out, ws=ws)
-            ok = same(out.cpu().numpy().reshape(1), [oracle.reduce(xn, L, init)])
+            got = out.cpu().numpy().reshape(1)
+            ok = same(got, [oracle.reduce(xn, L, init)])
+            wit = {"sha256": synth.sha256(got), "checked": "the result", "values": hex_bits(got)}
             us = timed(lambda: canon.reduce(x, L, init, out=out, ws=ws))
-            add(cfg, f"reduce L={L} init={init}", str(xn.dtype), xn.size, xn.nbytes, us, ok)
+            add(cfg, f"reduce L={L} init={init}", str(xn.dtype), xn.size, xn.nbytes, us, ok, wit)
             if scrubbed:
                 us = timed(lambda: canon.reduce(x, L, init, out=out, ws=ws), scrubbed=True)
                 add(cfg + " MALL scrubbed", f"reduce L={L} init={init}", str(xn.dtype), xn.size,
@@ -382,21 +612,27 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
                              dtype=torch.uint8, device=dev)
             canon.scan(x, pol, q, out=y, ws=ws)
             ok = canon.workspace_error(ws) == 0
+            yn = y.cpu().numpy()
+            idx = mid_block_probes(xn.size)
+            # the mid-block probes, each evaluated from scratch
+            pv = literal_prefixes(oracle, xn, idx, pol, q)
+            hits = bits_equal(yn[idx], pv)
+            wit = {"sha256": synth.sha256(yn), "probes": int(hits.size),
+                   "probes_pass": int(hits.sum()), "values": hex_bits(yn[idx])}
+            ok = ok and bool(hits.all())
             if full:
-                yn = y.cpu().numpy()
                 ok = ok and same(yn, oracle.scan(xn, pol, q))
-                # scan back == reduce under the same expression
-                L = q if pol == "iterated_pairwise" else 1
-                if pol != "block_dyadic" or xn.size % q == 0:
-                    ok = ok and same(yn[-1:], [oracle.reduce(xn, L, -0.0)])
+                wit["checked"] = "every prefix and the probes"
             else:
-                idx = np.unique(np.concatenate([[0, xn.size - 1], rng.integers(0, xn.size, 30)]))
-                got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
-                want = [oracle.scan_prefix(xn, int(i), pol, q) for i in idx]
-                ok = ok and same(got, want)
+                wit["checked"] = "the probes and the back element"
+            # scan back == reduce under the same expression (GPU reduce)
+            L = q if pol == "iterated_pairwise" else 1
+            if pol != "block_dyadic" or xn.size % q == 0:
+                back = canon.reduce(x, L, -0.0).cpu().numpy().reshape(1)
+                ok = ok and same(yn[-1:], back)
             us = timed(lambda: canon.scan(x, pol, q, out=y, ws=ws))
             label = pol if pol == "pairwise" else f"{pol}<{q}>"
-            add(cfg, f"scan {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok)
+            add(cfg, f"scan {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok, wit)
             if scrubbed:
                 us = timed(lambda: canon.scan(x, pol, q, out=y, ws=ws), scrubbed=True)
                 add(cfg + " MALL scrubbed", f"scan {label}", str(xn.dtype), xn.size,
@@ -412,23 +648,28 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
     rr = torch.empty(Xn.shape[0], dtype=X.dtype, device=dev)
     Y = torch.empty_like(X)
     canon.reduce_rows(X, 16, 0.0, out=rr)
-    ok = same(rr.cpu().numpy(), oracle.reduce_rows(Xn, 16, 0.0))
+    got = rr.cpu().numpy()
+    ok = same(got, oracle.reduce_rows(Xn, 16, 0.0))
+    sel = mid_block_probes(Xn.shape[0])
+    wit = {"sha256": synth.sha256(got), "checked": "every row", "values": hex_bits(got[sel])}
     add("C4", "row reduce L=16", "float64", Xn.size, Xn.nbytes,
-        timed(lambda: canon.reduce_rows(X, 16, 0.0, out=rr)), ok)
+        timed(lambda: canon.reduce_rows(X, 16, 0.0, out=rr)), ok, wit)
     canon.scan_rows(X, "block_dyadic", 16, out=Y)
-    sel = rng.integers(0, Xn.shape[0], 64)
-    ok = same(Y[torch.from_numpy(sel).to(dev)].cpu().numpy(),
-              oracle.scan_rows(Xn[sel], "block_dyadic", 16))
+    Yn = Y.cpu().numpy()
+    ok = same(Yn, oracle.scan_rows(Xn, "block_dyadic", 16))
+    cells = mid_block_probes(Xn.size)
+    wit = {"sha256": synth.sha256(Yn), "checked": "every element",
+           "values": hex_bits(Yn.reshape(-1)[cells])}
     add("C4", "row scan block_dyadic<16>", "float64", Xn.size, 2 * Xn.nbytes,
-        timed(lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y)), ok)
+        timed(lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y)), ok, wit)
     del X, Y, rr
     scan_cfg("C5", "scan_2e27_f64", (("iterated_pairwise", 128), ("block_dyadic", 16),
                                      ("block_dyadic", 256)), False)
     scan_cfg("C5", "scan_2e28_f32", (("block_dyadic", 256),), False)
 
     def scan_init_cfg(cfg, name, cases):
-        """Scans with an initial value on a workload's input: 34 sampled
-        outputs (first, last and random) evaluated from scratch."""
+        """Scans with an initial value on a workload's input: the first, the
+        last and 24 mid-block outputs evaluated from scratch."""
         xn = synth.config_input(name)
         x = torch.from_numpy(xn).to(dev)
         y = torch.empty(xn.size + 1, dtype=x.dtype, device=dev)
@@ -438,14 +679,21 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
                              dtype=torch.uint8, device=dev)
             canon.scan_with_init(x, pol, q, kind, init, out=y[:m], ws=ws)
             ok = canon.workspace_error(ws) == 0
-            idx = np.unique(np.concatenate([[0, 1, m - 1], rng.integers(0, m, 31)]))
-            got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
-            want = [oracle.scan_with_init_output(xn, int(k), pol, q, init, kind) for k in idx]
-            ok = ok and same(got, want)
+            yn = y[:m].cpu().numpy()
+            idx = mid_block_probes(m)
+            pv = parallel_values(
+                lambda k: oracle.scan_with_init_output(xn, k, pol, q, init, kind), idx, xn.dtype)
+            hits = bits_equal(yn[idx], pv)
+            ends = [0, 1, m - 1]
+            ok = ok and bool(hits.all()) and same(yn[ends], [
+                oracle.scan_with_init_output(xn, k, pol, q, init, kind) for k in ends])
+            wit = {"sha256": synth.sha256(yn), "probes": int(hits.size),
+                   "probes_pass": int(hits.sum()), "values": hex_bits(yn[idx]),
+                   "checked": "the probes and the first, second and last outputs"}
             us = timed(lambda: canon.scan_with_init(x, pol, q, kind, init, out=y[:m], ws=ws))
             label = pol if pol == "pairwise" else f"{pol}<{q}>"
             add(cfg, f"scan {kind} init={init} {label}", str(xn.dtype), xn.size,
-                xn.nbytes + m * xn.itemsize, us, ok)
+                xn.nbytes + m * xn.itemsize, us, ok, wit)
 
     scan_init_cfg("C5 with init", "scan_2e27_f64",
                   (("block_dyadic", 16, "exclusive", 1.0),
@@ -474,26 +722,36 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
                                  dtype=torch.uint8, device=dev)
                 out = torch.empty((), dtype=x.dtype, device=dev)
                 canon.reduce_op(x, q, op, 1.0, out=out, ws=ws)
-                ok = same(out.cpu().numpy().reshape(1), [oracle.reduce(xn, q, 1.0, op)])
+                got = out.cpu().numpy().reshape(1)
+                ok = same(got, [oracle.reduce(xn, q, 1.0, op)])
+                wit = {"sha256": synth.sha256(got), "checked": "the result",
+                       "values": hex_bits(got)}
                 us = timed(lambda: canon.reduce_op(x, q, op, 1.0, out=out, ws=ws))
                 add(cfg, f"reduce op={op} L={q} init=1.0", str(xn.dtype), xn.size, xn.nbytes, us,
-                    ok)
+                    ok, wit)
             else:
                 y = torch.empty_like(x)
                 ws = torch.empty(max(canon.scan_workspace_bytes(xn.size, pol, q, xn.itemsize), 1),
                                  dtype=torch.uint8, device=dev)
                 canon.scan_op(x, pol, q, op, out=y, ws=ws)
                 ok = canon.workspace_error(ws) == 0
-                idx = np.unique(np.concatenate([[0, 1, xn.size - 1],
-                                                rng.integers(0, xn.size, 31)]))
-                got = y[torch.from_numpy(idx).to(dev)].cpu().numpy()
+                yn = y.cpu().numpy()
+                idx = mid_block_probes(xn.size)
                 ident = canon.IDENTITY[op]
-                want = [oracle.scan_with_init_output(xn, int(k), pol, q, ident, "inclusive", op)
-                        for k in idx]
-                ok = ok and same(got, want)
+                pv = parallel_values(lambda k: oracle.scan_with_init_output(
+                    xn, k, pol, q, ident, "inclusive", op), idx, xn.dtype)
+                hits = bits_equal(yn[idx], pv)
+                ends = [0, 1, xn.size - 1]
+                ok = ok and bool(hits.all()) and same(yn[ends], [
+                    oracle.scan_with_init_output(xn, k, pol, q, ident, "inclusive", op)
+                    for k in ends])
+                wit = {"sha256": synth.sha256(yn), "probes": int(hits.size),
+                       "probes_pass": int(hits.sum()), "values": hex_bits(yn[idx]),
+                       "checked": "the probes and the first, second and last outputs"}
                 us = timed(lambda: canon.scan_op(x, pol, q, op, out=y, ws=ws))
                 label = pol if pol == "pairwise" else f"{pol}<{q}>"
-                add(cfg, f"scan op={op} {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok)
+                add(cfg, f"scan op={op} {label}", str(xn.dtype), xn.size, 2 * xn.nbytes, us, ok,
+                    wit)
             del x
 
     op_cfg("C3 ops", "reduce_2e28_f64", (("mul", "reduce", None, 128), ("min", "reduce", None, 128),
@@ -512,6 +770,16 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
         print(f"| {cfg} | {op} | {dt} | {n} | {t['median']:.1f} | {t['p10']:.1f} | "
               f"{t['p90']:.1f} | {chain} | {gbs:.0f} | {pct:.1f} | {eps:.3g} | "
               f"{'yes' if ok else 'NO'} |")
+    # the witness of every config row, in the manner of the canonical-scan
+    # README's witness runs: the output's SHA-256, the PASS count of the
+    # mid-block probes evaluated from scratch, and the probe values' bits
+    print()
+    print("| config | op | N | output SHA-256 | checked | probes PASS | mid-block values (bits) |")
+    print("|---|---|---|---|---|---|---|")
+    for cfg, op, dt, n, wit, ok in witness:
+        pr = (f"{wit['probes_pass']}/{wit['probes']}" if "probes" in wit else "n/a")
+        print(f"| {cfg} | {op} | {n} | {wit['sha256']} | {wit['checked']} | {pr} | "
+              f"{' '.join(wit['values'])} |")
 
 
 def run_contrast(torch, canon, synth, dev, repeats=10):

@@ -53,6 +53,10 @@ def _compile(src: str) -> str:
 ROOT = os.path.dirname(HERE)
 USER_OP_LIBS = [("tests/user_op/skew_op.hip", "tests/user_op/libcanon_skew.so")]
 
+# The benchmark's bandwidth probes (their own library, not libcanon's ABI).
+PROBE_LIB = ("scan_canonical_reduce_amd/csrc/bw_probe.hip",
+             "scan_canonical_reduce_amd/libcanon_bwprobe.so")
+
 
 def _build_user_op(pair) -> str:
     src, out = (os.path.join(ROOT, p) for p in pair)
@@ -71,6 +75,7 @@ def build(verbose: bool = False) -> str:
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
         user = [ex.submit(_build_user_op, p) for p in USER_OP_LIBS]  # longest first
+        user.append(ex.submit(_build_user_op, PROBE_LIB))
         objs = list(ex.map(_compile, srcs))
         for f in user:
             f.result()
