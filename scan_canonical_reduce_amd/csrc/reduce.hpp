@@ -6,13 +6,26 @@
 
 namespace canon {
 
-constexpr int kReduceThreads = 1024;  // streaming and finishing workgroups
+constexpr int kReduceThreads = 1024;  // general streaming workgroups
 constexpr int kReduceWaves = kReduceThreads / 64;
+constexpr int kFinishThreads = 1024;  // the finishing workgroup
 constexpr int kReduceBatch = 8;        // 16-byte vectors per thread per batch
 constexpr int kReduceStackDepth = 10;  // batches per wave <= 2^10
 constexpr int kRowsThreads = 256;      // row-batched workgroups
 constexpr int kMaxLogL = 16;
 constexpr uint64_t kPartialBudget = 1ull << 16;  // partial values (P * Lp) aimed for
+
+// Threads of the register-path streaming workgroup (one workgroup per CU),
+// by layout (measured on MI355X at N = 2^28): 256 for the row-group layout
+// (rows of at least 8 vectors: four waves keep about 32 KiB of loads in
+// flight per CU, which streams fastest), 512 for the interleaved layouts,
+// whose cross-lane swizzles want more waves to hide their latency, and 1024
+// for the interleaved layout with whole vectors of lanes across all 64
+// lanes (the most swizzles per element).
+constexpr int pow2_reduce_threads(int logc, bool whole_vectors)
+{
+    return logc >= 3 ? 256 : ((logc == 0 && whole_vectors) ? 1024 : 512);
+}
 
 struct ReducePlan {
     bool pow2;       // register path (L = 2^logl, 16-byte aligned input)
@@ -56,18 +69,19 @@ inline ReducePlan plan_reduce(uint64_t n, uint32_t L, size_t elem_size, bool ali
         const int log_cw = logc < 6 ? logc : 6;
         const int logg = 6 - log_cw;
         const uint64_t GU = (uint64_t)kReduceBatch << logg;
+        const uint64_t waves = pow2_reduce_threads(logc, pl.logl >= loge) / 64;
         pl.slices = 1ull << (logc - log_cw);
         const uint64_t msr = (n + (1ull << log_sr) - 1) >> log_sr;
         uint64_t pt = target_wg / pl.slices;
         if (pt < 1) pt = 1;
         if (pt > budgetP) pt = budgetP;
-        uint64_t want = (msr + pt * kReduceWaves - 1) / (pt * kReduceWaves);
+        uint64_t want = (msr + pt * waves - 1) / (pt * waves);
         uint64_t rw = GU;
         while (rw < want) rw *= 2;
         const uint64_t rw_max = GU << kReduceStackDepth;
         if (rw > rw_max) rw = rw_max;
         pl.rw_log = ceil_log2(rw);
-        pl.P = (msr + rw * kReduceWaves - 1) / (rw * kReduceWaves);
+        pl.P = (msr + rw * waves - 1) / (rw * waves);
     } else {
         const uint64_t m = (n + L - 1) / L;
         const uint64_t LW = Lp < (uint64_t)kReduceThreads ? Lp : (uint64_t)kReduceThreads;

@@ -57,6 +57,9 @@ struct Pow2Geom {
     static constexpr int GU = G * U;
     static constexpr bool INTERLEAVED = LOGC < 3;
     static constexpr int SW = CW * VE;  // lanes of one column slice
+    static constexpr int THREADS = pow2_reduce_threads(LOGC, VE == E);
+    static constexpr int WAVES = THREADS / 64;
+    static_assert(SW <= THREADS, "one thread per lane of a column slice in the wave merge");
 };
 
 // Reduce the E elements of one vector to VE lane values: the vector holds E/VE
@@ -142,20 +145,20 @@ __device__ __forceinline__ void pow2_batch(const T* __restrict__ x, uint64_t n, 
 }
 
 template <typename T, int LOGL>
-__global__ __launch_bounds__(kReduceThreads) void k_reduce_pow2(const T* __restrict__ x, uint64_t n,
-                                                                int rw_log, T* __restrict__ partial)
+__global__ __launch_bounds__((Pow2Geom<T, LOGL>::THREADS)) void k_reduce_pow2(
+    const T* __restrict__ x, uint64_t n, int rw_log, T* __restrict__ partial)
 {
     using GM = Pow2Geom<T, LOGL>;
     constexpr int VE = GM::VE;
     constexpr uint64_t L = 1ull << LOGL;
-    __shared__ T s_wave[kReduceWaves][GM::SW];
+    __shared__ T s_wave[GM::WAVES][GM::SW];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane & (GM::CW - 1), g = lane >> GM::LOG_CW;
     const uint64_t p = blockIdx.x;
     const int slice = blockIdx.y;
     const uint64_t rw = 1ull << rw_log;  // super-rows per wave (multiple of GU)
-    const uint64_t sr0 = (p * kReduceWaves + wave) * rw;
+    const uint64_t sr0 = (p * GM::WAVES + wave) * rw;
     const uint64_t msr = (n + (1ull << GM::LOG_SR) - 1) >> GM::LOG_SR;
 
     uint64_t nb = 0, nfull = 0;  // batches holding data / entirely inside x
@@ -184,13 +187,13 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_pow2(const T* __restr
     }
     __syncthreads();
     if (threadIdx.x < GM::SW) {
-        T t[kReduceWaves];
+        T t[GM::WAVES];
 #pragma unroll
-        for (int w = 0; w < kReduceWaves; ++w) t[w] = s_wave[w][threadIdx.x];
+        for (int w = 0; w < GM::WAVES; ++w) t[w] = s_wave[w][threadIdx.x];
 #pragma unroll
-        for (int h = 1; h < kReduceWaves; h *= 2)
+        for (int h = 1; h < GM::WAVES; h *= 2)
 #pragma unroll
-            for (int w = 0; w < kReduceWaves; w += 2 * h) t[w] = t[w] + t[w + h];
+            for (int w = 0; w < GM::WAVES; w += 2 * h) t[w] = t[w] + t[w + h];
         partial[p * L + (uint64_t)slice * GM::SW + threadIdx.x] = t[0];
     }
 }
@@ -284,16 +287,16 @@ __device__ __forceinline__ T pw_partials(const T* __restrict__ partial, uint64_t
 }
 
 template <typename T>
-__global__ __launch_bounds__(kReduceThreads) void k_reduce_finish(const T* __restrict__ partial,
+__global__ __launch_bounds__(kFinishThreads) void k_reduce_finish(const T* __restrict__ partial,
                                                                   uint64_t P, uint32_t L,
                                                                   int lp_log, uint64_t n, T init,
                                                                   T* __restrict__ out)
 {
-    __shared__ T s_v[kReduceThreads];
+    __shared__ T s_v[kFinishThreads];
     const int t = threadIdx.x;
     const uint64_t Lp = 1ull << lp_log;
-    if (Lp <= kReduceThreads) {
-        const int S = kReduceThreads >> lp_log;
+    if (Lp <= kFinishThreads) {
+        const int S = kFinishThreads >> lp_log;
         const uint64_t j = t & (Lp - 1);
         const int s = t >> lp_log;
         uint64_t ps = 1;
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_finish(const T* __res
             __syncthreads();
         }
     } else {
-        const uint64_t K = Lp >> 10;
+        const uint64_t K = Lp / kFinishThreads;
         TreeStack<T, 1, 17> st;
         T v[1];
         for (uint64_t k = 0; k < K; ++k) {
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_finish(const T* __res
         st.collapse(K, v);
         s_v[t] = v[0];
         __syncthreads();
-        for (int h = 1; h < kReduceThreads; h *= 2) {
+        for (int h = 1; h < kFinishThreads; h *= 2) {
             if (t % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h];
             __syncthreads();
         }
@@ -527,8 +530,8 @@ static hipError_t launch_pow2_one(const T* x, uint64_t n, const ReducePlan& pl, 
                                   hipStream_t s)
 {
     dim3 grid((unsigned)pl.P, (unsigned)pl.slices);
-    hipLaunchKernelGGL((k_reduce_pow2<T, LOGL>), grid, dim3(kReduceThreads), 0, s, x, n,
-                       pl.rw_log, partial);
+    hipLaunchKernelGGL((k_reduce_pow2<T, LOGL>), grid, dim3(Pow2Geom<T, LOGL>::THREADS), 0, s, x,
+                       n, pl.rw_log, partial);
     return hipGetLastError();
 }
 
@@ -561,7 +564,7 @@ hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, T* 
         }
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_reduce_finish<T>), dim3(1), dim3(kReduceThreads), 0, s, partial, pl.P,
+    hipLaunchKernelGGL((k_reduce_finish<T>), dim3(1), dim3(kFinishThreads), 0, s, partial, pl.P,
                        L, pl.lp_log, n, init, out);
     return hipGetLastError();
 }
