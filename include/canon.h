@@ -68,9 +68,8 @@ extern "C" {
  * size B for block_dyadic.  Larger values return CANON_EUNSUPPORTED. */
 #define CANON_MAX_L 65536u
 #define CANON_MAX_B 65536u
-/* Largest lane count L of the iterated_pairwise scan (the per-row lane trees
- * of a tile are kept in LDS). */
-#define CANON_MAX_IP_L 2048u
+/* Largest lane count L of the iterated_pairwise scan. */
+#define CANON_MAX_IP_L 65536u
 
 typedef enum {
     CANON_OK = 0,

@@ -16,6 +16,24 @@ namespace canon {
 inline std::atomic<uint64_t> g_sched_grid_cap{0};
 inline std::atomic<uint64_t> g_sched_reduce_wg{0};
 
+// Compute units of the current device (cached per device; 256 if unknown).
+inline uint64_t device_cus()
+{
+    static uint64_t cache[64] = {};
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cache[dev] = (uint64_t)cus;
+    }
+    return cache[dev];
+}
+
 // `grid` workgroups, or fewer under the schedule override.
 inline uint64_t capped_grid(uint64_t grid)
 {

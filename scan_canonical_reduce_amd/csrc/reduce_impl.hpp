@@ -502,8 +502,12 @@ static hipError_t launch_rows_pow2(const T* x, uint64_t rows, uint64_t cols, uin
                                    T* out, hipStream_t s)
 {
     constexpr int RPB = kRowsThreads / 64;  // rows per workgroup
+    // at most one workgroup per CU, each wave walking rows grid-stride: four
+    // waves per CU keep about 32 KiB of loads in flight, where streaming
+    // reads are fastest (16384 x 4096 f64, L = 16: 86 -> 81 us)
     uint64_t grid = (rows + RPB - 1) / RPB;
-    if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
+    const uint64_t cus = device_cus();
+    if (grid > cus) grid = cus;
     grid = capped_grid(grid);
     hipLaunchKernelGGL((k_reduce_rows_pow2<T, LOGL>), dim3((unsigned)grid), dim3(kRowsThreads), 0,
                        s, x, rows, cols, ldx, init, out);

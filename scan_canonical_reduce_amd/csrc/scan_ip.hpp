@@ -11,24 +11,36 @@ constexpr int kIpMaxRLog = 6;         // at most 64 rows per tile
 constexpr int kIpLevelsPerPass = 4;   // node levels built per launch
 constexpr int kIpMaxLevels = 48;
 constexpr uint64_t kIpMaxGrid = 0x7FFFFFFFull;  // one workgroup per item
-constexpr uint32_t kIpMaxL = 2048;    // largest lane count of the scan
+constexpr uint32_t kIpMaxL = 65536;   // largest lane count of the scan
+// Lane counts above kIpWholeRowMaxL keep only chunks of 2^kIpChunkLog lanes'
+// trees in LDS; the trees above the chunks live in the workspace.
+constexpr uint32_t kIpWholeRowMaxL = 2048;
+constexpr int kIpChunkLog = 9;
 
 // Geometry of an iterated_pairwise scan over nseg independent segments of
 // `cols` elements (one segment for a plain scan, one per row for the row
 // scan), and the layout of the node arrays in the workspace (in elements):
 // level k holds, per segment, cnt[k] nodes of L values: the complete
 // pairwise trees, lane by lane, over tiles [u 2^k, (u+1) 2^k).
+// Chunked geometry (Lp > kIpWholeRowMaxL): the lanes of a row form
+// nchunks = Lp / C chunks of C = 2^chunk_log lanes; after the nodes, the
+// workspace holds per segment and row the tree over that row's chunk totals
+// (2 nchunks values: level 0, the chunk totals, at [0, nchunks), level l at
+// 2 nchunks - (2 nchunks >> l)).
 struct IpLayout {
     uint32_t L;
-    int lp_log;  // Lp = 2^lp_log >= L
-    int r_log;   // R = 2^r_log rows of L lanes per tile
+    int lp_log;     // Lp = 2^lp_log >= L
+    int r_log;      // R = 2^r_log rows of L lanes per tile
+    int chunk_log;  // lanes per chunk (== lp_log: the whole row is one chunk)
     uint64_t nseg;
-    uint64_t tps;  // tiles per segment
-    int levels;    // node levels with at least one node
+    uint64_t rows;  // rows of L per segment
+    uint64_t tps;   // tiles per segment
+    int levels;     // node levels with at least one node
     uint64_t cnt[kIpMaxLevels];
     uint64_t off[kIpMaxLevels];
-    uint64_t total;  // elements of node storage
-    int fast_logrv;  // >= 0: register path with L = 64 * E * 2^fast_logrv; -1: LDS path
+    uint64_t cl_off;  // chunked: offset of the chunk trees (elements)
+    uint64_t total;   // elements of node (and chunk tree) storage
+    int fast_logrv;   // >= 0: register path with L = 64 * E * 2^fast_logrv; -1: LDS path
 };
 
 // LDS budget (elements) for the per-row trees of one tile: (R + 1) * 2 * Lp
@@ -46,17 +58,21 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
     const uint64_t Lp = 1ull << lp;
     const int loge = elem_size == 8 ? 1 : 2;
     lay.fast_logrv = -1;
+    lay.chunk_log = lp;
     int rl;
     if (aligned && Lp == L && lp >= loge + 6 && lp <= loge + 9) {
         lay.fast_logrv = lp - loge - 6;
         rl = 6 - lay.fast_logrv;  // 64 / RV rows per tile
     } else {
+        if (Lp > kIpWholeRowMaxL) lay.chunk_log = kIpChunkLog;
+        const uint64_t Lc = 1ull << lay.chunk_log;
         rl = kIpMaxRLog;
-        while (rl > 0 && ((1ull << rl) + 1) * 2 * Lp > ip_lds_elems(elem_size)) --rl;
+        while (rl > 0 && ((1ull << rl) + 1) * 2 * Lc > ip_lds_elems(elem_size)) --rl;
     }
     lay.r_log = rl;
     lay.nseg = nseg;
     const uint64_t rows = (cols + L - 1) / L;
+    lay.rows = rows;
     lay.tps = (rows + (1ull << rl) - 1) >> rl;
     uint64_t off = 0;
     lay.levels = 0;
@@ -66,6 +82,8 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
         if (lay.cnt[k] > 0) lay.levels = k + 1;
         off += nseg * lay.cnt[k] * L;
     }
+    lay.cl_off = off;
+    if (lay.chunk_log < lay.lp_log) off += nseg * rows * 2 * (Lp >> lay.chunk_log);
     lay.total = off;
     return lay;
 }
@@ -106,7 +124,7 @@ inline IpSingleLayout make_ip_single_layout(const IpLayout& g)
 
 inline size_t ip_lds_bytes(const IpLayout& lay, size_t elem_size)
 {
-    return (size_t)((1ull << lay.r_log) + 1) * 2 * (1ull << lay.lp_log) * elem_size;
+    return (size_t)((1ull << lay.r_log) + 1) * 2 * (1ull << lay.chunk_log) * elem_size;
 }
 
 // out == null: the plain inclusive scan; else the scan with an initial

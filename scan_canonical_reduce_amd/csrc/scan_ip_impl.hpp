@@ -204,6 +204,217 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_scan(const T* __restrict__ x,
     }
 }
 
+// ============================================================================
+// Chunked rows (Lp > kIpWholeRowMaxL).  A row's lane tree is too large for
+// LDS, so its lanes are cut into chunks of C = 2^chunk_log; a chunk's lanes
+// hold the complete subtrees of level chunk_log.  The walk of lane r climbs
+// first inside r's chunk (the chunk's trees in LDS, as k_ip_scan), then
+// above it, where every sibling is a whole aligned group of chunks: pure A
+// (left) or pure B (right) values of the tree over the row's chunk totals,
+// which the workspace holds per row (A: the row's, B: the row above's).
+//   3a. chunk totals: per (tile, chunk), the chunk's A values of every row
+//       of the tile and their complete tree's root;
+//   3b. chunk trees: per row, the levels above the chunk totals;
+//   3c. the scan: per (tile, chunk), the chunk's trees again and the walk.
+// ============================================================================
+
+// Chunk tree of row `row` of segment `seg` (2 nchunks values).
+template <typename T>
+__device__ __forceinline__ T* ip_chunk_tree(T* nodes, const IpLayout& lay, uint64_t seg,
+                                            uint64_t row)
+{
+    const uint64_t nc = 1ull << (lay.lp_log - lay.chunk_log);
+    return nodes + lay.cl_off + (seg * lay.rows + row) * 2 * nc;
+}
+
+// The leaves of the per-row trees of one chunk of one tile, as k_ip_scan
+// builds them for a whole row: tree ri (row ri - 1 of the tile; ri = 0 is
+// the row above the tile) at lvl(ri, 0)[jj] for the chunk's lanes
+// jj = j - c C; lanes past L are -0.0.
+template <typename T, class Lvl>
+__device__ __forceinline__ void ip_chunk_leaves(const T* __restrict__ xs, uint64_t cols,
+                                                const T* __restrict__ nodes, const IpLayout& lay,
+                                                uint64_t seg, uint64_t t, uint64_t c, Lvl lvl)
+{
+    const int R = 1 << lay.r_log;
+    const uint64_t C = 1ull << lay.chunk_log;
+    const uint64_t L = lay.L;
+    for (uint64_t jj = threadIdx.x; jj < C; jj += kIpThreads) {
+        const uint64_t j = c * C + jj;
+        TreeStack<T, 1, kIpMaxRLog> st;
+        T v[1];
+        for (int r = 0; r < R; ++r) {
+            v[0] = ip_load(xs, cols, (uint32_t)L, t * R + r, j);
+            st.push(r, v);
+            st.collapse(r + 1, v);
+            lvl(r + 1, 0)[jj] = v[0];
+        }
+        T b = neg_zero<T>();
+        for (int k = 0; k < lay.levels && (t >> k) != 0; ++k) {
+            if (!((t >> k) & 1)) continue;
+            const T h = j < L ? ip_node(nodes, lay, k, seg, (t >> k) - 1)[j] : neg_zero<T>();
+            for (int r = 0; r < R; ++r) lvl(r + 1, 0)[jj] = h + lvl(r + 1, 0)[jj];
+            b = h + b;
+        }
+        lvl(0, 0)[jj] = b;
+    }
+}
+
+// Levels 1 .. chunk_log of trees ri0 .. R of the chunk (complete subtrees,
+// lower lanes on the left); ends with a barrier.
+template <typename T, class Lvl>
+__device__ __forceinline__ void ip_chunk_levels(const IpLayout& lay, int ri0, Lvl lvl)
+{
+    const int R = 1 << lay.r_log;
+    const uint64_t C = 1ull << lay.chunk_log;
+    for (int l = 1; l <= lay.chunk_log; ++l) {
+        const uint64_t width = C >> l;
+        const uint64_t total = (uint64_t)(R + 1 - ri0) * width;
+        for (uint64_t e = threadIdx.x; e < total; e += kIpThreads) {
+            const int ri = ri0 + (int)(e / width);
+            const uint64_t u = e % width;
+            lvl(ri, l)[u] = lvl(ri, l - 1)[2 * u] + lvl(ri, l - 1)[2 * u + 1];
+        }
+        __syncthreads();
+    }
+}
+
+// Kernel 3a: the chunk totals of every row of every tile (level 0 of the
+// rows' chunk trees).
+template <typename T>
+__global__ __launch_bounds__(kIpThreads) void k_ip_chunk_totals(const T* __restrict__ x,
+                                                                uint64_t ldx, uint64_t cols,
+                                                                T* __restrict__ nodes,
+                                                                IpLayout lay)
+{
+    extern __shared__ unsigned char ip_smem[];
+    T* tree = reinterpret_cast<T*>(ip_smem);
+    const int R = 1 << lay.r_log;
+    const uint64_t C = 1ull << lay.chunk_log;
+    const uint64_t nc = 1ull << (lay.lp_log - lay.chunk_log);
+    const uint64_t items = lay.nseg * lay.tps * nc;
+    auto lvl = [&](int ri, int l) -> T* { return tree + (uint64_t)ri * 2 * C + (2 * C - ((2 * C) >> l)); };
+    for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const uint64_t seg = item / (lay.tps * nc), rem = item % (lay.tps * nc);
+        const uint64_t t = rem / nc, c = rem % nc;
+        ip_chunk_leaves<T>(x + seg * ldx, cols, nodes, lay, seg, t, c, lvl);
+        __syncthreads();
+        ip_chunk_levels<T>(lay, 1, lvl);
+        for (int r = (int)threadIdx.x; r < R; r += kIpThreads) {
+            const uint64_t row = t * R + r;
+            if (row < lay.rows) ip_chunk_tree(nodes, lay, seg, row)[c] = lvl(r + 1, lay.chunk_log)[0];
+        }
+        __syncthreads();  // the trees are rebuilt for the next item
+    }
+}
+
+// Kernel 3b: levels 1 .. log2(nchunks) of every row's chunk tree, one
+// thread per row.
+template <typename T>
+__global__ __launch_bounds__(kIpThreads) void k_ip_chunk_rows(T* __restrict__ nodes, IpLayout lay)
+{
+    const int lc = lay.lp_log - lay.chunk_log;
+    const uint64_t nc = 1ull << lc;
+    const uint64_t items = lay.nseg * lay.rows;
+    for (uint64_t item = (uint64_t)blockIdx.x * kIpThreads + threadIdx.x; item < items;
+         item += (uint64_t)gridDim.x * kIpThreads) {
+        T* ct = ip_chunk_tree(nodes, lay, item / lay.rows, item % lay.rows);
+        for (int l = 1; l <= lc; ++l) {
+            T* lo = ct + (2 * nc - ((2 * nc) >> (l - 1)));
+            T* hi = ct + (2 * nc - ((2 * nc) >> l));
+            for (uint64_t u = 0; u < (nc >> l); ++u) hi[u] = lo[2 * u] + lo[2 * u + 1];
+        }
+    }
+}
+
+// Kernel 3c: the scan of one chunk of one tile at a time.
+template <typename T, bool OUTX>
+__global__ __launch_bounds__(kIpThreads) void k_ip_scan_chunked(const T* __restrict__ x,
+                                                                uint64_t ldx, T* __restrict__ y,
+                                                                uint64_t ldy, uint64_t cols,
+                                                                T* __restrict__ nodes,
+                                                                IpLayout lay, T init, int kind)
+{
+    extern __shared__ unsigned char ip_smem[];
+    T* tree = reinterpret_cast<T*>(ip_smem);
+    const int R = 1 << lay.r_log;
+    const uint64_t C = 1ull << lay.chunk_log;
+    const int lc = lay.lp_log - lay.chunk_log;
+    const uint64_t nc = 1ull << lc;
+    const uint64_t L = lay.L;
+    const uint64_t items = lay.nseg * lay.tps * nc;
+    auto lvl = [&](int ri, int l) -> T* { return tree + (uint64_t)ri * 2 * C + (2 * C - ((2 * C) >> l)); };
+
+    for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const uint64_t seg = item / (lay.tps * nc), rem = item % (lay.tps * nc);
+        const uint64_t t = rem / nc, c = rem % nc;
+        T* ys = y + seg * ldy;
+        ip_chunk_leaves<T>(x + seg * ldx, cols, nodes, lay, seg, t, c, lvl);
+        __syncthreads();
+        ip_chunk_levels<T>(lay, 0, lvl);
+
+        // above the chunk: level lv of the chunk tree of row `row` (A side)
+        // or of the row above (B side; -0.0 above the segment's first row)
+        auto above = [&](int r, uint64_t i, T val) {
+            const uint64_t row = t * R + r;
+            const T* a = ip_chunk_tree(nodes, lay, seg, row);
+            const T* b = row > 0 ? ip_chunk_tree(nodes, lay, seg, row - 1) : nullptr;
+            for (int l = lay.chunk_log + 1; l <= lay.lp_log; ++l) {
+                const int lv = l - 1 - lay.chunk_log;
+                const uint64_t pos = i >> (l - 1);
+                const uint64_t sib = (pos ^ 1) + (2 * nc - ((2 * nc) >> lv));
+                if (pos & 1) val = a[sib] + val;                 // left sibling: A values
+                else val = val + (b ? b[sib] : neg_zero<T>());   // right sibling: B values
+            }
+            return val;
+        };
+        // the walk from lane i (in chunk c) to the root
+        auto walk = [&](int r, uint64_t i) {
+            const uint64_t jj = i - c * C;
+            T val = lvl(r + 1, 0)[jj];
+            for (int l = 1; l <= lay.chunk_log; ++l) {
+                const uint64_t pos = jj >> (l - 1);
+                const uint64_t sib = pos ^ 1;
+                if (pos & 1) val = lvl(r + 1, l - 1)[sib] + val;
+                else val = val + lvl(r, l - 1)[sib];
+            }
+            return above(r, i, val);
+        };
+        const uint64_t lo = c * C, hi = (c + 1) * C < L ? (c + 1) * C : L;
+        const uint64_t elems = (uint64_t)R * (hi > lo ? hi - lo : 0);
+        for (uint64_t e = threadIdx.x; e < elems; e += kIpThreads) {
+            const int r = (int)(e / (hi - lo));
+            const uint64_t i = lo + e % (hi - lo);
+            const uint64_t gi = (t * R + r) * L + i;
+            if (gi >= cols) continue;
+            if constexpr (!OUTX) {
+                ys[gi] = walk(r, i);
+            } else if (kind == kScanInclusive) {
+                ys[gi] = init + walk(r, i);
+            } else {
+                // the value before element (r, i): lane i - 1 of the same row
+                // (at a chunk's first lane, the last lane of the chunk before,
+                // whose walk inside its chunk gives that chunk's A total), or
+                // at lane 0 the end of the row above, the root of its chunk
+                // tree (-0.0 before the segment's first element)
+                T before;
+                if (i > lo) {
+                    before = walk(r, i - 1);
+                } else if (i > 0) {
+                    before = above(r, i - 1, ip_chunk_tree(nodes, lay, seg, t * R + r)[c - 1]);
+                } else {
+                    const uint64_t row = t * R + r;
+                    before = row > 0 ? ip_chunk_tree(nodes, lay, seg, row - 1)[2 * nc - 2]
+                                     : neg_zero<T>();
+                }
+                ys[gi] = init + before;
+                if (kind == kScanIncludeInitial && gi + 1 == cols) ys[cols] = init + walk(r, i);
+            }
+        }
+        __syncthreads();  // the trees are rebuilt for the next item
+    }
+}
+
 template <typename T>
 static hipError_t launch_ip_nodes(T* nodes, const IpLayout& lay, hipStream_t s)
 {
@@ -234,6 +445,24 @@ static hipError_t launch_ip(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64
     e = launch_ip_nodes<T>(nodes, lay, s);
     if (e != hipSuccess) return e;
     const size_t lds = ip_lds_bytes(lay, sizeof(T));
+    if (lay.chunk_log < lay.lp_log) {
+        const uint64_t citems = items << (lay.lp_log - lay.chunk_log);
+        const unsigned cgrid = (unsigned)capped_grid(citems < kIpMaxGrid ? citems : kIpMaxGrid);
+        hipLaunchKernelGGL((k_ip_chunk_totals<T>), dim3(cgrid), dim3(kIpThreads), lds, s, x, ldx,
+                           cols, nodes, lay);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const uint64_t rows = lay.nseg * lay.rows;
+        uint64_t rgrid = (rows + kIpThreads - 1) / kIpThreads;
+        if (rgrid > 4096) rgrid = 4096;
+        hipLaunchKernelGGL((k_ip_chunk_rows<T>), dim3((unsigned)capped_grid(rgrid)),
+                           dim3(kIpThreads), 0, s, nodes, lay);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_ip_scan_chunked<T, OUTX>), dim3(cgrid), dim3(kIpThreads), lds, s, x,
+                           ldx, y, ldy, cols, nodes, lay, out.init, out.kind);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_ip_scan<T, OUTX>), dim3(grid), dim3(kIpThreads), lds, s, x, ldx, y, ldy,
                        cols, nodes, lay, out.init, out.kind);
     return hipGetLastError();

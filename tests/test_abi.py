@@ -98,7 +98,8 @@ def test_scan_argument_errors(canon):
     assert L.canon_scan_f64(fake, fake, 10, 2, 1 << 17, None, 0, None) == 2  # B too large
     assert L.canon_scan_f64(fake, fake, 10, 1, 0, None, 0, None) == 1      # L = 0
     assert L.canon_scan_f64(fake, fake, 10, 1, (1 << 16) + 1, None, 0, None) == 2
-    assert L.canon_scan_f64(fake, fake, 10, 1, 4096, None, 0, None) == 2    # L > CANON_MAX_IP_L
+    assert L.canon_scan_f64(fake, fake, 10, 1, 65537, None, 0, None) == 2   # L > CANON_MAX_IP_L
+    assert L.canon_scan_f64(fake, fake, 10, 1, 65536, None, 0, None) == 3   # no workspace
     assert L.canon_scan_f64(fake, fake, 1 << 20, 1, 128, None, 0, None) == 3  # no workspace
     assert L.canon_scan_rows_f64(fake, 4096, fake, 4096, 8, 4096, 1, 16, None, 0, None) == 3
     assert L.canon_scan_f64(None, fake, 10, 0, 0, None, 0, None) == 1

@@ -343,6 +343,95 @@ def test_scan_iterated_pairwise_unaligned_register_geometry(canon, dtype, L):
                                                        "exclusive"), "exclusive")
 
 
+# iterated_pairwise with L > 2048: the lanes of a row are cut into chunks of
+# 512 (their trees in LDS), the trees above the chunks come from the
+# workspace; tiles of 4 rows (double) or 8 rows (float).
+CHUNK = 512
+
+
+def chunk_edge_probes(n, L, rows, seed, sparse_rows=()):
+    """Outputs at chunk edges (first and last lanes of chunks, the lanes
+    either side) of every chunk in `rows` and of a few chunks (the first,
+    the middle and the last ones) in `sparse_rows`, at row starts and ends,
+    and random ones, below n."""
+    rng = np.random.default_rng(seed)
+    nc = (L + CHUNK - 1) // CHUNK
+
+    def lanes(chunks):
+        v = {0, 1, L - 1, L - 2}
+        for c in chunks:
+            v |= {c * CHUNK - 1, c * CHUNK, c * CHUNK + 1}
+        return [u for u in v if 0 <= u < L]
+
+    idx = {r * L + v for r in rows for v in lanes(range(1, nc))}
+    few = {1, 2, nc // 2 - 1, nc // 2, nc // 2 + 1, nc - 1}
+    idx |= {r * L + v for r in sparse_rows for v in lanes(c for c in few if 0 < c < nc)}
+    idx |= set(rng.integers(0, n, 64).tolist()) | {n - 1}
+    return np.array(sorted(i for i in idx if 0 <= i < n), dtype=np.int64)
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [4096, 5000])
+def test_scan_iterated_pairwise_chunked_lanes(canon, dtype, L):
+    """Every prefix over 20 to 40 tiles and a ragged tail, ragged shorter
+    inputs at tile and row edges, and the back element against the GPU
+    reduce with the same L."""
+    x = synth.generate(656_137, "mixed_magnitude", 420 + L, dtype)
+    want_all = oracle.scan(x, "iterated_pairwise", L)
+    S = scan_tile(dtype, "iterated_pairwise", L)
+    for n in (1, L - 1, L, L + 1, 3 * L + 5, S - 1, S, S + 1, 5 * S + 3, x.size):
+        print(f"[ip chunked] {np.dtype(dtype).name} L={L} n={n}", flush=True)
+        y = gpu_scan(canon, x[:n], "iterated_pairwise", L)
+        assert_bit_exact(y, want_all[:n], f"n={n}")
+    assert_bit_exact(y[-1:], gpu_reduce(canon, x, L, -0.0), "back == reduce")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_scan_iterated_pairwise_largest_L(canon, dtype):
+    """L = 65536 (128 chunks per row) over several tiles: outputs at every
+    chunk edge of several rows, row starts and ends and random ones,
+    evaluated from scratch; the back element against the GPU reduce."""
+    L = 65536
+    n = 9 * 4 * L + 12345
+    x = synth.generate(n, "mixed_magnitude", 430, dtype)
+    y = gpu_scan(canon, x, "iterated_pairwise", L)
+    idx = chunk_edge_probes(n, L, (0, 1), 431, sparse_rows=(4, 5, 17, 35, 36))
+    want = np.array([oracle.scan_prefix(x, int(i), "iterated_pairwise", L) for i in idx])
+    assert_bit_exact(y[idx], want, "chunk-edge probes")
+    assert_bit_exact(y[-1:], gpu_reduce(canon, x, L, -0.0), "back == reduce")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("kind", ["exclusive", "include_initial", "inclusive"])
+def test_scan_iterated_pairwise_chunked_with_init(canon, dtype, kind):
+    """The shifted kinds read the value before a chunk's first lane from the
+    chunk trees: every output at L = 4096, chunk-edge outputs at 65536."""
+    x = synth.generate(200_003, "mixed_magnitude", 432, dtype)
+    got = to_host(canon.scan_with_init(to_dev(x), "iterated_pairwise", 4096, kind, 0.375))
+    assert_bit_exact(got, oracle.scan_with_init(x, "iterated_pairwise", 4096, 0.375, kind),
+                     f"L=4096 {kind}")
+    L = 65536
+    n = 5 * L + 777
+    x = synth.generate(n, "mixed_magnitude", 433, dtype)
+    got = to_host(canon.scan_with_init(to_dev(x), "iterated_pairwise", L, kind, 0.375))
+    m = n + (kind == "include_initial")
+    idx = chunk_edge_probes(m, L, (0, 1), 434, sparse_rows=(4, 5))
+    want = np.array([oracle.scan_with_init_output(x, int(k), "iterated_pairwise", L, 0.375, kind)
+                     for k in idx])
+    assert_bit_exact(got[idx], want, f"L=65536 {kind}")
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_scan_rows_iterated_pairwise_chunked_lanes(canon, dtype):
+    rows, ld = 3, 2 * 16384 + 4200
+    X = synth.generate(rows * ld, "mixed_magnitude", 435, dtype).reshape(rows, ld)
+    Xd = to_dev(X)
+    for L, cols in ((4096, 2 * 16384 + 4097), (4097, ld), (8192, 8191)):
+        got = to_host(canon.scan_rows(Xd[:, :cols], "iterated_pairwise", L))
+        want = oracle.scan_rows(X, "iterated_pairwise", L, cols=cols)[:, :cols]
+        assert_bit_exact(got, want, f"L={L} cols={cols}")
+
+
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("L", [3, 16, 128])
 def test_scan_rows_iterated_pairwise(canon, dtype, L):

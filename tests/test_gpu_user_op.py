@@ -136,6 +136,21 @@ LARGE_SCANS = [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16), ("blo
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("L", [4096, 6000])
+def test_scan_chunked_lanes(skew, canon, dtype, L):
+    """iterated_pairwise with the lanes of a row in chunks (L > 2048): the
+    walk above the chunks and the chunk-edge shift, every kind."""
+    n = 300_007
+    x = data(n, 96, dtype)
+    xd = to_dev(x)
+    for kind in KINDS:
+        print(f"[skew chunked] {np.dtype(dtype).name} L={L} {kind}", flush=True)
+        got = scan(skew, canon, xd, "iterated_pairwise", L, kind, 0.5)
+        want = oracle.scan_with_init(x, "iterated_pairwise", L, 0.5, kind, "skew")
+        assert_bit_exact(got, want, kind)
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("policy,param", LARGE_SCANS)
 def test_scan_large(skew, canon, dtype, policy, param):
     """2^22 + 4097 elements (512 double or 256 float tiles and a ragged
