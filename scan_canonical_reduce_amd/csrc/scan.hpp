@@ -15,7 +15,8 @@ constexpr int kMaxLevels = 48;
 // Workspace layout of a single-pass scan (offsets in 64-bit words).
 //   word 0: error word (low 32 bits); word 1: tile counter (low 32 bits)
 //   [tiles_off, +ntiles): published tile totals (tile-level 0 nodes)
-//   [level_off[k], +ceil(ntiles / 2^k)): published tile-level k nodes, k > kGroupLog
+//   [level_off[k], +ceil(ntiles / 2^k)): published tile-level k nodes,
+//       k >= kGroupLog
 // Each published word holds one value (one lane value for the
 // iterated_pairwise scan, whose nodes are vectors of L words).
 struct ScanLayout {
@@ -35,10 +36,7 @@ inline ScanLayout make_scan_layout(uint64_t ntiles, uint64_t width)
     uint64_t off = l.tiles_off + ntiles * width;
     for (int k = 0; k < kMaxLevels; ++k) {
         l.level_off[k] = off;
-        if (k > kGroupLog) {
-            uint64_t cnt = (ntiles + (1ull << k) - 1) >> k;
-            off += cnt * width;
-        }
+        if (k >= kGroupLog) off += ((ntiles + (1ull << k) - 1) >> k) * width;
     }
     l.total_words = off;
     return l;

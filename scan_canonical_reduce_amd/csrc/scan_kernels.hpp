@@ -33,14 +33,15 @@ namespace canon {
 //           i.e. the right spine of the node, whose left siblings end at least
 //           two groups back and are read as published nodes (wave 3), as are
 //           the nodes of the bits above k0.
-// Published nodes: the last tile of each odd group forms node (6, G) from
-// its rebuilt low nodes and its own total (node (6, G) itself is never read:
-// later tiles rebuild it) and climbs, publishing node (k+1, t >> (k+1)) =
-// node (k, (t >> k) - 1) + node (k, t >> k) while bit k of t is set.  The
-// published nodes a tile reads all end before group G-1, and a climb to
-// level k waits only on one node of each lower level, so no wait is ever
-// on a chain of look-backs that grows with the number of tiles.  Every value
-// is fixed by position only.
+// Published nodes: the workgroup of the last tile of each group G (tile
+// 64 G + 63) builds node (6, G) from the group's 64 published totals right
+// after that tile's front, before anything of its own look-back, and climbs:
+// while the node built is a right child, parent = published left sibling +
+// node.  A build waits only on other tiles' totals (a front never waits) and
+// on nodes of earlier builds, never on a look-back, so a node is out about
+// one front after its last tile's total and no wait is ever on a chain of
+// look-backs.  The published nodes a tile reads all end before group G-1.
+// Every value is fixed by position only.
 //
 // The words are read once right after the loads of the workgroup's next
 // tile are issued (lookback_issue), so that they arrive with that data;
@@ -127,48 +128,17 @@ __device__ __forceinline__ void lookback_collect(uint64_t t, LookbackWords lw,
     }
 }
 
-// Wave 3 resolves the published nodes of levels klo <= k < khi (lane
-// k - 6) into s_w3[k - 6].
+// Wave 3 resolves the published nodes (lane k - 6 for level k) into
+// s_w3[k - 6].
 template <typename T>
 __device__ __forceinline__ void lookback_collect_high(uint64_t t, LookbackWords lw,
                                                       uint64_t* __restrict__ ws,
                                                       const ScanLayout& lay, uint32_t* err,
-                                                      T* s_w3, int lane, int klo, int khi)
+                                                      T* s_w3, int lane)
 {
-    const int k = kGroupLog + lane;
-    if (k < klo || k >= khi) return;
     uint64_t* slot = lookback_slot(t, ws, lay, 3, lane);
     const T a = slot ? ready_or_wait<T>(lw.w, slot, err) : neg_zero<T>();
     if (lane < kMaxLevels - kGroupLog) s_w3[lane] = a;
-}
-
-// Tiles that publish: the last tile of an odd group (bits 0..6 of t set).
-// It publishes node (k+1, t >> (k+1)) for 6 <= k < climb_top(t), the first
-// clear bit of t above bit 5; other tiles get climb_top == 6.
-__device__ __forceinline__ int climb_top(uint64_t t)
-{
-    if ((t & 127) != 127) return kGroupLog;
-    const int top = kGroupLog + __builtin_ctzll(~(t >> kGroupLog));
-    return top < kMaxLevels - 1 ? top : kMaxLevels - 1;
-}
-
-// One thread of a publishing tile: node (6, G) from the low nodes and the
-// tile's own total, then node (k+1) = node (k, (t >> k) - 1) + node (k, t >> k)
-// for k = 6 .. top-1.  Uses only the values this climb needs, so a publish
-// never waits on nodes of the bits above the climb.
-template <typename T>
-__device__ __forceinline__ void lookback_climb(uint64_t t, int top, T tile_total,
-                                               uint64_t* __restrict__ ws, const ScanLayout& lay,
-                                               const T* s_low, const T* s_g6, const T* s_w3)
-{
-    T acc = tile_total;
-    for (int k = 0; k < kGroupLog; ++k) acc = s_low[k] + acc;
-    acc = s_g6[0] + acc;
-    publish(ws + lay.level_off[kGroupLog + 1] + (t >> (kGroupLog + 1)), acc);
-    for (int k = kGroupLog + 1; k < top; ++k) {
-        acc = s_w3[k - kGroupLog] + acc;
-        publish(ws + lay.level_off[k + 1] + (t >> (k + 1)), acc);
-    }
 }
 
 // One thread: the node of every set bit of t into s_h[k].
@@ -193,6 +163,7 @@ __device__ __forceinline__ void lookback_combine(uint64_t t, const T* s_low, con
     }
 }
 
+// Header words zeroed, every published word marked not ready.
 template <typename T>
 __global__ void k_scan_init(uint64_t* __restrict__ ws, uint64_t total)
 {
@@ -202,26 +173,55 @@ __global__ void k_scan_init(uint64_t* __restrict__ ws, uint64_t total)
         ws[i] = i < 32 ? 0ull : nr;
 }
 
-// Every thread of the workgroup of tile t > 0: resolves the look-back into
-// s_h[k] = node (k, (t >> k) - 1) for every set bit k of t.  A publishing
-// tile first resolves what its climb needs, publishes, and only then waits
-// for the rest.
 template <typename T>
-__device__ __forceinline__ void run_lookback(uint64_t t, T tile_total, LookbackWords lw,
+inline void launch_scan_init(uint64_t* ws, const ScanLayout& lay, hipStream_t s)
+{
+    uint64_t blocks = (lay.total_words + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL((k_scan_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws,
+                       lay.total_words);
+}
+
+// Whether tile t ends its group (its workgroup then runs group_build).
+__device__ __forceinline__ bool ends_group(uint64_t t)
+{
+    return (t & ((1u << kGroupLog) - 1)) == (1u << kGroupLog) - 1;
+}
+
+// One wave, right after the front of tile e = 64 G + 63: node (6, G) from
+// the group's 64 totals (each published by a front, so every wait here
+// ends), then, while the node built is the right child of its parent
+// (bit k of G set), parent = published left sibling + node.
+template <typename T>
+__device__ __forceinline__ void group_build(uint64_t e, uint64_t* __restrict__ ws,
+                                            const ScanLayout& lay, uint32_t* err, int lane)
+{
+    const uint64_t G = e >> kGroupLog;
+    uint64_t* slot = ws + lay.tiles_off + (G << kGroupLog) + lane;
+    const uint64_t w0 = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    T node[kGroupLog];
+    T acc = wave_tree(ready_or_wait<T>(w0, slot, err), lane, 0, node);
+    uint64_t u = G;
+    if (lane == 0) publish(ws + lay.level_off[kGroupLog] + u, acc);
+    for (int k = kGroupLog; (u & 1) && k + 1 < kMaxLevels; ++k) {
+        acc = wait_word<T>(ws + lay.level_off[k] + (u - 1), err) + acc;
+        u >>= 1;
+        if (lane == 0) publish(ws + lay.level_off[k + 1] + u, acc);
+    }
+}
+
+// Every thread of the workgroup of tile t > 0: resolves the look-back into
+// s_h[k] = node (k, (t >> k) - 1) for every set bit k of t.
+template <typename T>
+__device__ __forceinline__ void run_lookback(uint64_t t, LookbackWords lw,
                                              uint64_t* __restrict__ ws, const ScanLayout& lay,
                                              uint32_t* err, T* s_low, T* s_g6, T* s_w3, T* s_h,
                                              int w, int lane)
 {
-    const int top = climb_top(t);
     if (w < 3)
         lookback_collect<T>(t, lw, ws, lay, err, s_low, s_g6, w, lane);
     else if (w == 3)
-        lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, 0, top);
-    if (top > kGroupLog) {
-        __syncthreads();
-        if (threadIdx.x == 0) lookback_climb<T>(t, top, tile_total, ws, lay, s_low, s_g6, s_w3);
-    }
-    if (w == 3) lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane, top, 1 << 30);
+        lookback_collect_high<T>(t, lw, ws, lay, err, s_w3, lane);
     __syncthreads();
     if (threadIdx.x == 0) lookback_combine<T>(t, s_low, s_g6, s_w3, s_h);
     __syncthreads();
@@ -703,25 +703,27 @@ struct WideTile {
 // front done (total published).  Takes the next ticket and issues its loads
 // into `nxt`, reads t's look-back words afresh right behind them, runs the
 // next tile's front (so a tile's total never waits for another tile's
-// look-back), then resolves t's look-back (its words have had the whole
-// front to arrive) and finishes t.  Returns false when no tile is left.
+// look-back; when that tile ends its group, wave 0 then builds the group's
+// node), then resolves t's look-back (its words have had the whole front
+// to arrive) and finishes t.  Returns false when no tile is left.
 template <class P, typename T>
 __device__ __forceinline__ bool pipe_step(typename P::State& cur, typename P::State& nxt,
-                                          uint64_t& t, T& total, const ScanCtx<T>& c)
+                                          uint64_t& t, const ScanCtx<T>& c)
 {
     const uint64_t tn = next_ticket(c);
     const bool more = tn < c.lay->ntiles;
     if (more) P::load(nxt, tn, c);
     LookbackWords lw{};
     if (t > 0) lw = lookback_issue<T>(t, c.ws, *c.lay, c.w, c.lane);
-    T totn = total;
-    if (more) totn = P::front(nxt, tn, c);
+    if (more) {
+        P::front(nxt, tn, c);
+        if (ends_group(tn) && c.w == 0) group_build<T>(tn, c.ws, *c.lay, c.err, c.lane);
+    }
     if (t > 0)
-        run_lookback<T>(t, total, lw, c.ws, *c.lay, c.err, c.sh->lb.low, c.sh->lb.g6,
-                        c.sh->lb.w3, c.sh->lb.h, c.w, c.lane);
+        run_lookback<T>(t, lw, c.ws, *c.lay, c.err, c.sh->lb.low, c.sh->lb.g6, c.sh->lb.w3,
+                        c.sh->lb.h, c.w, c.lane);
     P::back(cur, t, c);
     t = tn;
-    total = totn;
     return more;
 }
 
@@ -755,10 +757,11 @@ __attribute__((amdgpu_waves_per_eu(P::kMinWavesPerEu))) void k_scan(const T* x, 
     if (t >= lay.ntiles) return;
     typename P::State a, b;
     P::load(a, t, c);
-    T total = P::front(a, t, c);
+    P::front(a, t, c);
+    if (ends_group(t) && c.w == 0) group_build<T>(t, c.ws, lay, c.err, c.lane);
     for (;;) {
-        if (!pipe_step<P, T>(a, b, t, total, c)) break;
-        if (!pipe_step<P, T>(b, a, t, total, c)) break;
+        if (!pipe_step<P, T>(a, b, t, c)) break;
+        if (!pipe_step<P, T>(b, a, t, c)) break;
     }
 }
 
@@ -860,10 +863,7 @@ hipError_t launch_scan_impl(const T* x, T* y, uint64_t n, bool pairwise, int b_l
                             uint64_t* ws, const ScanLayout& lay, const ScanOut<T>& out,
                             hipStream_t s)
 {
-    uint64_t blocks = (lay.total_words + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL((k_scan_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws,
-                       lay.total_words);
+    launch_scan_init<T>(ws, lay, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (pairwise || b_log == 0)

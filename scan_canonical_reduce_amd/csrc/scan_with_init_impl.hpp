@@ -47,10 +47,7 @@ hipError_t launch_scan_order_free(const T* x, T* y, uint64_t n, bool aligned, ui
     if (n == 0)
         return out.kind == kScanIncludeInitial ? launch_put_column(y, 1, 1, out.init, s)
                                                : hipSuccess;
-    uint64_t blocks = (lay.total_words + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL((k_scan_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws,
-                       lay.total_words);
+    launch_scan_init<T>(ws, lay, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int LOGV = scan_log_v<T>();
