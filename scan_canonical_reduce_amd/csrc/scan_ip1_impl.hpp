@@ -48,16 +48,26 @@ constexpr bool ip1_pipelined()
     return LOGRV == 0;
 }
 
-__device__ __forceinline__ uint64_t* ip1_word(uint64_t* ws, const IpSingleLayout& lay, int k,
+// The per-level arrays of the layout, copied to LDS by every workgroup: a
+// level-indexed read of the kernel argument compiles to a vector load, and
+// waiting for one would also wait for every tile load issued before it.
+struct Ip1Levels {
+    uint64_t woff[kIpMaxLevels];
+    uint64_t coff[kIpMaxLevels];
+    uint64_t cnt[kIpMaxLevels];
+};
+
+__device__ __forceinline__ uint64_t* ip1_word(uint64_t* ws, const Ip1Levels& lv, uint64_t L, int k,
                                               uint64_t seg, uint64_t u, uint64_t col)
 {
-    return ws + lay.woff[k] + (seg * lay.g.cnt[k] + u) * (uint64_t)lay.g.L + col;
+    return ws + lv.woff[k] + (seg * lv.cnt[k] + u) * L + col;
 }
 
-__device__ __forceinline__ uint32_t* ip1_counter(uint64_t* ws, const IpSingleLayout& lay, int k,
-                                                 uint64_t seg, uint64_t v)
+__device__ __forceinline__ uint32_t* ip1_counter(uint64_t* ws, const IpSingleLayout& lay,
+                                                 const Ip1Levels& lv, int k, uint64_t seg,
+                                                 uint64_t v)
 {
-    return reinterpret_cast<uint32_t*>(ws + lay.cbase) + lay.coff[k] + seg * lay.g.cnt[k] + v;
+    return reinterpret_cast<uint32_t*>(ws + lay.cbase) + lv.coff[k] + seg * lv.cnt[k] + v;
 }
 
 // Header (error word, ticket), every node word not ready, counters zero.
@@ -78,6 +88,7 @@ struct Ip1Shared {
     static constexpr int STAGE = L > kIp1Stage ? L : kIp1Stage;
     alignas(16) T row[4][L];  // per-wave rows exchanged between the waves
     alignas(16) T h[STAGE];   // node values of the earlier tiles, a batch at a time
+    Ip1Levels lvl;
     uint32_t ticket;
 };
 
@@ -112,7 +123,10 @@ __device__ __forceinline__ uint64_t ip1_ticket(const Ip1Ctx<T, LOGRV>& c)
         c.sh->ticket = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(c.ws + 1), 1u,
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const uint64_t it = c.sh->ticket;
+    // uniform: kept in scalar registers, so that the node addresses derived
+    // from it (layout arrays indexed by level) are scalar loads, which a
+    // wait for them does not order behind the tile's vector loads
+    const uint64_t it = __builtin_amdgcn_readfirstlane(c.sh->ticket);
     __syncthreads();  // the slot is rewritten by the next ticket
     return it;
 }
@@ -173,23 +187,25 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
     __syncthreads();  // every wave has read row[]
 
     if (w == 3) {
+        auto word = [&](int k, uint64_t u, uint64_t col) {
+            return ip1_word(c.ws, c.sh->lvl, lay.g.L, k, seg, u, col);
+        };
         T cur[RV][E];
 #pragma unroll
         for (int q = 0; q < RV; ++q)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 cur[q][e] = a[(RW - 1) * RV + q][e];
-                publish(ip1_word(c.ws, lay, 0, seg, t, (uint64_t)(q * 64 + lane) * E + e),
-                        cur[q][e]);
+                publish(word(0, t, (uint64_t)(q * 64 + lane) * E + e), cur[q][e]);
             }
         uint64_t u = t;
         for (int k = 0; k + 1 < lay.g.levels; ++k) {
             const uint64_t v = u >> 1;
-            if (v >= lay.g.cnt[k + 1]) break;  // the parent covers tiles past the end
+            if (v >= c.sh->lvl.cnt[k + 1]) break;  // the parent covers tiles past the end
             uint32_t before = 0;
             if (lane == 0)
-                before = __hip_atomic_fetch_add(ip1_counter(c.ws, lay, k + 1, seg, v), 1u,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                before = __hip_atomic_fetch_add(ip1_counter(c.ws, lay, c.sh->lvl, k + 1, seg, v),
+                                                1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             before = __builtin_amdgcn_readfirstlane(before);
             if (before == 0) break;  // the sibling completes the parent
             // the sibling's words: all reads issued, then each waited for
@@ -198,18 +214,16 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
             for (int q = 0; q < RV; ++q)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    sw[q][e] = __hip_atomic_load(
-                        ip1_word(c.ws, lay, k, seg, u ^ 1, (uint64_t)(q * 64 + lane) * E + e),
-                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sw[q][e] = __hip_atomic_load(word(k, u ^ 1, (uint64_t)(q * 64 + lane) * E + e),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
             for (int q = 0; q < RV; ++q)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const uint64_t col = (uint64_t)(q * 64 + lane) * E + e;
-                    const T sib = ready_or_wait<T>(
-                        sw[q][e], ip1_word(c.ws, lay, k, seg, u ^ 1, col), c.err);
+                    const T sib = ready_or_wait<T>(sw[q][e], word(k, u ^ 1, col), c.err);
                     cur[q][e] = (u & 1) ? sib + cur[q][e] : cur[q][e] + sib;
-                    publish(ip1_word(c.ws, lay, k + 1, seg, v, col), cur[q][e]);
+                    publish(word(k + 1, v, col), cur[q][e]);
                 }
             u = v;
         }
@@ -237,6 +251,10 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
     const uint64_t row0 = t * F::R;
     const bool full = (row0 + F::R) * F::L <= c.cols;
 
+    // word `col` of node (k, (t >> k) - 1)
+    auto node = [&](int k, int col) {
+        return ip1_word(c.ws, c.sh->lvl, lay.g.L, k, seg, (t >> k) - 1, (uint64_t)col);
+    };
     // The node words of up to NB set bits at a time, spread over the reading
     // threads (word idx of a batch: node idx / L, lane idx % L), every read
     // issued before any is waited for, then staged in LDS.
@@ -260,17 +278,15 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
                 const int m = idx / F::L, col = idx % F::L;
                 wv[i] = not_ready_word<T>();
                 if (idx < SH::STAGE && m < nb)
-                    wv[i] = __hip_atomic_load(
-                        ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col), __ATOMIC_RELAXED,
-                        __HIP_MEMORY_SCOPE_AGENT);
+                    wv[i] = __hip_atomic_load(node(lv[m], col), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
             }
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int idx = i * RT + (int)threadIdx.x;
                 const int m = idx / F::L, col = idx % F::L;
                 if (idx < SH::STAGE && m < nb)
-                    c.sh->h[idx] = ready_or_wait<T>(
-                        wv[i], ip1_word(c.ws, lay, lv[m], seg, (t >> lv[m]) - 1, col), c.err);
+                    c.sh->h[idx] = ready_or_wait<T>(wv[i], node(lv[m], col), c.err);
             }
         }
         __syncthreads();
@@ -377,7 +393,12 @@ __global__ __launch_bounds__(kIpThreads) void k_ip_single(const T* __restrict__ 
                              init,
                              kind};
     const uint64_t items = lay.g.nseg * lay.g.tps;
-    uint64_t it = ip1_ticket(c);
+    for (int i = (int)threadIdx.x; i < kIpMaxLevels; i += kIpThreads) {
+        sh.lvl.woff[i] = lay.woff[i];
+        sh.lvl.coff[i] = lay.coff[i];
+        sh.lvl.cnt[i] = lay.g.cnt[i];
+    }
+    uint64_t it = ip1_ticket(c);  // its barrier publishes sh.lvl
     if (it >= items) return;
     Ip1Tile<T, LOGRV> A, B;
     ip1_load<AL>(A, it, c);
