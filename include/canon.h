@@ -120,6 +120,12 @@ int canon_last_hip_error(void);
  *   x     device, n elements (may be NULL when n == 0)
  *   L     lane count, 1 <= L <= CANON_MAX_L
  *   out   device, one element; written on `stream`
+ *   ws    device, canon_reduce_workspace_bytes(n, L, elem_size) bytes
+ *         (none when that is 0), 256-byte aligned; its contents on entry do
+ *         not matter (each call tags what it writes with an id of its own);
+ *         calls that may overlap in time must not share a workspace.
+ * One kernel: the last workgroup finishes (canon_workspace_error reports a
+ * finish that gave up waiting for the others).
  * Source: P4016R0 "Key Design Points" (lanes i mod L, pairwise tree per lane,
  * lanes combined by the same rule, op(init, R)). */
 size_t canon_reduce_workspace_bytes(size_t n, uint32_t L, size_t elem_size);
@@ -243,12 +249,14 @@ canon_status_t canon_scan_rows_op_f32(const float* x, size_t ldx, float* y, size
                                       void* stream);
 
 /* -------------------------------------------------------------- checking */
-/* Every scan workspace begins with a 32-bit error word, which every scan
- * call given a workspace of nonzero size sets.  The single-pass scans wait
- * on values published by earlier workgroups with a bounded spin; if a bound
- * is ever exceeded the kernel stops waiting, records a nonzero error word
- * and finishes (the output is then invalid).  This call copies the word to
- * *err_out and synchronises `stream`.  0 means no error. */
+/* Every scan workspace, and every reduce workspace, begins with a 32-bit
+ * error word, which every scan or reduce call given a workspace of nonzero
+ * size sets.  The single-pass scans wait on values published by earlier
+ * workgroups, and the reduce's finishing workgroup on the other workgroups'
+ * partial values, with a bounded spin; if a bound is ever exceeded the
+ * kernel stops waiting, records a nonzero error word and finishes (the
+ * output is then invalid).  This call copies the word to *err_out and
+ * synchronises `stream`.  0 means no error. */
 canon_status_t canon_workspace_error(const void* ws, uint32_t* err_out, void* stream);
 
 /* -------------------------------------------------------------- geometry */

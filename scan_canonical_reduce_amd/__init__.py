@@ -195,8 +195,9 @@ def _ws(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor | None:
 
 
 def _check_ws(w: torch.Tensor | None, ws: torch.Tensor | None, check, what: str) -> None:
-    """Reads a scan's error word: when check is True, or when check is None
-    and the workspace is the binding's own (w is not the caller's ws)."""
+    """Reads a scan's or reduce's error word: when check is True, or when
+    check is None and the workspace is the binding's own (w is not the
+    caller's ws)."""
     if w is None or check is False or (check is None and w is ws):
         return
     err = workspace_error(w)
@@ -222,8 +223,9 @@ def scan_rows_workspace_bytes(rows: int, cols: int, policy, param: int, elem_siz
 
 
 def reduce(x: torch.Tensor, L: int, init: float = 0.0, out: torch.Tensor | None = None,
-           ws: torch.Tensor | None = None) -> torch.Tensor:
-    """init + CR_L(x) as a 0-d tensor on x's device (init when x is empty)."""
+           ws: torch.Tensor | None = None, check: bool | None = None) -> torch.Tensor:
+    """init + CR_L(x) as a 0-d tensor on x's device (init when x is empty).
+    check: read the workspace's error word (see scan)."""
     _need_gpu(x)
     if x.dim() != 1 or (x.numel() > 0 and x.stride(0) != 1):
         raise ValueError("reduce takes a contiguous 1-d tensor")
@@ -236,6 +238,7 @@ def reduce(x: torch.Tensor, L: int, init: float = 0.0, out: torch.Tensor | None 
         _ptr(x), x.numel(), L, float(init), out.data_ptr(), _ptr(w), nb if w is None else w.numel(),
         _stream())
     _check(st, "reduce")
+    _check_ws(w, ws, check, "reduce")
     return out
 
 
@@ -370,7 +373,7 @@ def _op_init(op, init):
 
 
 def reduce_op(x: torch.Tensor, L: int, op="add", init=None, out: torch.Tensor | None = None,
-              ws: torch.Tensor | None = None) -> torch.Tensor:
+              ws: torch.Tensor | None = None, check: bool | None = None) -> torch.Tensor:
     """op(init, expression of x) with the operator op; init defaults to the
     operator's identity."""
     _need_gpu(x)
@@ -385,6 +388,7 @@ def reduce_op(x: torch.Tensor, L: int, op="add", init=None, out: torch.Tensor | 
         _ptr(x), x.numel(), L, _op(op), float(_op_init(op, init)), out.data_ptr(), _ptr(w),
         nb if w is None else w.numel(), _stream())
     _check(st, "reduce_op")
+    _check_ws(w, ws, check, "reduce_op")
     return out
 
 

@@ -41,12 +41,22 @@ inline thread_local int g_last_hip_error = 0;
 inline constexpr uint64_t kReduceTargetWG = 256;  // one streaming workgroup per MI355X CU
 inline constexpr size_t kWsAlign = 256;
 
-// Workgroups the streaming reduce aims for: one per CU, or the schedule
-// override's value.
-inline uint64_t reduce_target_wg()
+// Workgroups the streaming reduce aims for (the schedule override's value
+// when set): one per CU, fewer for small inputs, where the call's time is
+// latency: as few as keep the finishing workgroup's partial values (one per
+// workgroup and lane) at 8192 or below, but no fewer than give each
+// workgroup at most 128 KiB of input (measured on MI355X at 2^20 doubles:
+// L = 128 with 64 workgroups 10.0 us a call back to back, with 256 12.4 us).
+inline uint64_t reduce_target_wg(uint64_t n, uint32_t L, size_t es)
 {
     const uint64_t v = g_sched_reduce_wg.load(std::memory_order_relaxed);
-    return v ? v : kReduceTargetWG;
+    if (v) return v;
+    uint64_t lp = 1;
+    while (lp < L) lp *= 2;
+    const uint64_t by_partials = lp < 8192 ? 8192 / lp : 1;
+    const uint64_t by_bytes = (n * es + (128u << 10) - 1) >> 17;
+    const uint64_t t = by_partials > by_bytes ? by_partials : by_bytes;
+    return t < kReduceTargetWG ? t : kReduceTargetWG;
 }
 
 inline bool is_pow2(uint64_t v) { return v && !(v & (v - 1)); }
@@ -82,12 +92,48 @@ inline size_t reduce_ws(uint64_t n, uint32_t L, size_t es)
 {
     if (L == 0 || L > CANON_MAX_L || (es != 4 && es != 8)) return 0;
     // the larger of the two possible plans (16-byte aligned input or not)
-    const ReducePlan a = plan_reduce(n, L, es, true, reduce_target_wg());
-    const ReducePlan b = plan_reduce(n, L, es, false, reduce_target_wg());
-    uint64_t need = reduce_partials_bytes(a, L, es);
-    const uint64_t nb = reduce_partials_bytes(b, L, es);
+    const ReducePlan a = plan_reduce(n, L, es, true, reduce_target_wg(n, L, es));
+    const ReducePlan b = plan_reduce(n, L, es, false, reduce_target_wg(n, L, es));
+    uint64_t need = reduce_ws_layout(a, L, es).bytes;
+    const uint64_t nb = reduce_ws_layout(b, L, es).bytes;
     if (nb > need) need = nb;
     return need ? round_up(need, kWsAlign) : 0;
+}
+
+// A 64-bit id unique to one reduction call: a per-instance start (the clock
+// and the address of the counter, which differs between library instances
+// in one process, mixed by the splitmix64 finaliser) plus a counter, never
+// 0, so that no earlier call of this or any other library instance, and no
+// other data left in a workspace, holds it (a collision needs two 64-bit
+// starts within the number of calls made).
+inline uint64_t splitmix64(uint64_t z)
+{
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+inline uint64_t next_reduce_call_id()
+{
+    static std::atomic<uint64_t> next{0};
+    static std::atomic<bool> seeded{false};
+    if (!seeded.load(std::memory_order_acquire)) {
+        static std::mutex mu;
+        std::lock_guard<std::mutex> lock(mu);
+        if (!seeded.load(std::memory_order_relaxed)) {
+            const uint64_t t =
+                (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+            next.store(splitmix64(t ^ splitmix64((uint64_t)(uintptr_t)&next)),
+                       std::memory_order_relaxed);
+            seeded.store(true, std::memory_order_release);
+        }
+    }
+    uint64_t v;
+    do {
+        v = next.fetch_add(1, std::memory_order_relaxed);
+    } while (v == 0);
+    return v;
 }
 
 template <typename T>
@@ -97,12 +143,13 @@ canon_status_t reduce_impl(const T* x, size_t n, uint32_t L, T init, T* out, voi
     if (out == nullptr || L == 0 || (n > 0 && x == nullptr)) return CANON_EINVAL;
     if (L > CANON_MAX_L) return CANON_EUNSUPPORTED;
     const ReducePlan pl =
-        plan_reduce(n, L, sizeof(T), aligned16(x), reduce_target_wg());
+        plan_reduce(n, L, sizeof(T), aligned16(x), reduce_target_wg(n, L, sizeof(T)));
     // the documented size (covers either plan), so that a caller who sizes by
     // canon_reduce_workspace_bytes is never rejected and never overrun
     if (canon_status_t s = check_ws(ws, ws_bytes, reduce_ws(n, L, sizeof(T)))) return s;
-    return hip_status(launch_reduce<T>(x, n, L, init, out, static_cast<T*>(ws), pl,
-                                       static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n == 0) return hip_status(launch_put_column<T>(out, 1, 1, init, st));
+    return hip_status(launch_reduce<T>(x, n, L, init, out, ws, pl, next_reduce_call_id(), st));
 }
 
 template <typename T>

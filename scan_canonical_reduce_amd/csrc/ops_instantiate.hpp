@@ -13,8 +13,8 @@
 #include "scan_with_init_impl.hpp"
 
 #define CANON_INSTANTIATE_OP(V)                                                                  \
-    template hipError_t launch_reduce<V, true>(const V*, uint64_t, uint32_t, V, V*, V*,           \
-                                               const ReducePlan&, hipStream_t);                    \
+    template hipError_t launch_reduce<V, true>(const V*, uint64_t, uint32_t, V, V*, void*,        \
+                                               const ReducePlan&, uint64_t, hipStream_t);          \
     template hipError_t launch_reduce_rows<V>(const V*, uint64_t, uint64_t, uint64_t, uint32_t, V, \
                                               V*, hipStream_t);                                    \
     template hipError_t launch_put_column<V>(V*, uint64_t, uint64_t, V, hipStream_t);             \
@@ -37,8 +37,8 @@
 // Minimum and maximum: every parenthesisation gives the same value, so one
 // scan kernel (block_dyadic with one-vector blocks) serves every policy.
 #define CANON_INSTANTIATE_ORDER_FREE_OP(V)                                                       \
-    template hipError_t launch_reduce<V, true>(const V*, uint64_t, uint32_t, V, V*, V*,           \
-                                               const ReducePlan&, hipStream_t);                    \
+    template hipError_t launch_reduce<V, true>(const V*, uint64_t, uint32_t, V, V*, void*,        \
+                                               const ReducePlan&, uint64_t, hipStream_t);          \
     template hipError_t launch_reduce_rows<V>(const V*, uint64_t, uint64_t, uint64_t, uint32_t, V, \
                                               V*, hipStream_t);                                    \
     template hipError_t launch_put_column<V>(V*, uint64_t, uint64_t, V, hipStream_t);             \

@@ -5,9 +5,10 @@
 namespace canon {
 
 template hipError_t launch_reduce<double, true>(const double*, uint64_t, uint32_t, double,
-                                                double*, double*, const ReducePlan&, hipStream_t);
+                                                double*, void*, const ReducePlan&, uint64_t,
+                                                hipStream_t);
 template hipError_t launch_reduce<float, true>(const float*, uint64_t, uint32_t, float, float*,
-                                               float*, const ReducePlan&, hipStream_t);
+                                               void*, const ReducePlan&, uint64_t, hipStream_t);
 template hipError_t launch_reduce_rows<double>(const double*, uint64_t, uint64_t, uint64_t,
                                                uint32_t, double, double*, hipStream_t);
 template hipError_t launch_reduce_rows<float>(const float*, uint64_t, uint64_t, uint64_t, uint32_t,

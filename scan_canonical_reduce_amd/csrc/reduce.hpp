@@ -8,7 +8,6 @@ namespace canon {
 
 constexpr int kReduceThreads = 1024;  // general streaming workgroups
 constexpr int kReduceWaves = kReduceThreads / 64;
-constexpr int kFinishThreads = 1024;  // the finishing workgroup
 constexpr int kReduceBatch = 8;        // 16-byte vectors per thread per batch
 constexpr int kReduceStackDepth = 10;  // batches per wave <= 2^10
 constexpr int kRowsThreads = 256;      // row-batched workgroups
@@ -128,16 +127,35 @@ inline bool reduce_rows_supported(uint64_t cols, uint32_t L)
     return (m + span - 1) / span < (1ull << (kRowsRoundDepth + 1));
 }
 
-inline uint64_t reduce_partials_bytes(const ReducePlan& pl, uint32_t L, size_t elem_size)
+// Workspace of a reduction (byte offsets), for a plan with P > 0:
+//   [0, 256): header; bytes 0-3 the error word, which the finishing
+//     workgroup writes on every call (0, or kErrSpin when its bounded wait
+//     for the other workgroups gave up);
+//   [partial_off, +P * L values): the partial lane values, row p of L values
+//     from row range p;
+//   [flags_off, +P * slices 64-bit words): one arrival flag per streaming
+//     workgroup, which holds the call's id once its partials are out.
+struct ReduceWs {
+    uint64_t partial_off, flags_off, bytes;
+};
+
+inline ReduceWs reduce_ws_layout(const ReducePlan& pl, uint32_t L, size_t elem_size)
 {
-    return pl.P * (uint64_t)L * elem_size;
+    ReduceWs w{};
+    if (pl.P == 0) return w;
+    w.partial_off = 256;
+    w.flags_off = w.partial_off + (pl.P * (uint64_t)L * elem_size + 255) / 256 * 256;
+    w.bytes = w.flags_off + pl.P * pl.slices * 8;
+    return w;
 }
 
-// POW2 = false: only the general streaming kernel is built; the plan must
-// then be one for unaligned input (pl.pow2 false).
+// n > 0.  call_id: unique to this call (never 0, never what an earlier call
+// or any other data left in the flags).  POW2 = false: only the general
+// streaming kernel is built; the plan must then be one for unaligned input
+// (pl.pow2 false).
 template <typename T, bool POW2 = true>
-hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, T* partial,
-                         const ReducePlan& pl, hipStream_t s);
+hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, void* ws,
+                         const ReducePlan& pl, uint64_t call_id, hipStream_t s);
 
 template <typename T>
 hipError_t launch_reduce_rows(const T* x, uint64_t rows, uint64_t cols, uint64_t ldx, uint32_t L,

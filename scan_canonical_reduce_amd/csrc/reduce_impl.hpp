@@ -13,17 +13,172 @@
 // complete subtree of an aligned power-of-two range of rows, padded at the
 // end with -0.0 where the input stops (exact: x + -0.0 == x).
 //
-// Two kernels per call:
-//   1. a streaming kernel: workgroup p computes, for every lane, the subtree
-//      over its aligned range of rows and writes partial[p][lane];
-//   2. a finishing kernel (one workgroup): PW over the partials of each lane
-//      in range order, PW over lanes, then init + R.
+// One kernel per call: workgroup p computes, for every lane, the subtree
+// over its aligned range of rows and writes partial[p][lane]; the last
+// workgroup (highest index) then waits for every other workgroup's arrival
+// flag and finishes: PW over the partials of each lane in range order, PW
+// over lanes, then init + R.
 #pragma once
 #include "device.hpp"
 #include "launch.hpp"
 #include "reduce.hpp"
 
 namespace canon {
+
+// What the finishing workgroup needs (the workspace layout of reduce.hpp).
+template <typename T>
+struct ReduceFin {
+    T* partial;       // P rows of L values
+    uint64_t* flags;  // one per streaming workgroup
+    uint32_t* err;    // the error word
+    uint64_t call_id;
+    uint64_t P;
+    uint32_t L;
+    int lp_log;
+    T init;
+    T* out;
+};
+
+// Partial values move between workgroups with device-coherent accesses
+// (relaxed device-scope atomics): they are performed at the device's
+// coherence point, so neither the writer's cache nor the reader's needs a
+// write-back or an invalidation.
+template <typename T>
+__device__ __forceinline__ void store_coherent(T* p, T v)
+{
+    using U = typename std::conditional<sizeof(T) == 8, uint64_t, uint32_t>::type;
+    __hip_atomic_store(reinterpret_cast<U*>(p), __builtin_bit_cast(U, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T load_coherent(const T* p)
+{
+    using U = typename std::conditional<sizeof(T) == 8, uint64_t, uint32_t>::type;
+    return __builtin_bit_cast(
+        T, __hip_atomic_load(reinterpret_cast<const U*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// PW over partial[q0..q1)[j] (rows in range order), batches of 8 merged with
+// a binary-counter stack; B batches' loads are in flight at a time.
+template <typename T, int B>
+__device__ __forceinline__ T pw_partials(const T* __restrict__ partial, uint64_t L, uint64_t j,
+                                         uint64_t q0, uint64_t q1)
+{
+    TreeStack<T, 1, kReduceStackDepth> st;
+    T v[1];
+    const uint64_t nb = q1 > q0 ? (q1 - q0 + 7) / 8 : 0;
+    for (uint64_t k0 = 0; k0 < nb; k0 += B) {
+        T a[B][8];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint64_t q = q0 + (k0 + b) * 8 + u;
+                a[b][u] = q < q1 ? load_coherent(partial + q * L + j) : neg_zero<T>();
+            }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (k0 + b >= nb) break;
+#pragma unroll
+            for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+                for (int u = 0; u < 8; u += 2 * h) a[b][u] = a[b][u] + a[b][u + h];
+            v[0] = a[b][0];
+            st.push(k0 + b, v);
+        }
+    }
+    st.collapse(nb, v);
+    return v[0];
+}
+
+// The finish, by one workgroup of FT threads: lane value = PW over the
+// partials of the lane; R = PW over lanes 0..L-1 (padded to Lp = 2^lp_log
+// with -0.0 lanes); out = init + R.
+//   Lp <= FT: S = FT / Lp threads per lane, each over an aligned power-of-
+//     two segment of the partials; segments and then lanes merged in LDS.
+//   Lp > FT: thread t owns lanes [t*K, (t+1)*K), K = Lp / FT.
+template <typename T, int FT>
+__device__ __forceinline__ void finish_block(const ReduceFin<T>& f, T* s_v)
+{
+    constexpr int PB = 4;  // batches of partials in flight per thread
+    const int t = threadIdx.x;
+    const uint64_t Lp = 1ull << f.lp_log;
+    const uint64_t P = f.P, L = f.L;
+    if (Lp <= (uint64_t)FT) {
+        const int S = FT >> f.lp_log;
+        const uint64_t j = t & (Lp - 1);
+        const int s = t >> f.lp_log;
+        uint64_t ps = 1;
+        while (ps * S < P) ps *= 2;
+        const uint64_t q0 = s * ps, q1 = (q0 + ps) < P ? (q0 + ps) : P;
+        s_v[t] = (j < L) ? pw_partials<T, PB>(f.partial, L, j, q0, q1) : neg_zero<T>();
+        __syncthreads();
+        for (int h = 1; h < S; h *= 2) {
+            if (s % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h * (int)Lp];
+            __syncthreads();
+        }
+        // lanes 0..Lp-1 now at s_v[0..Lp)
+        for (uint64_t h = 1; h < Lp; h *= 2) {
+            if ((uint64_t)t < Lp && t % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h];
+            __syncthreads();
+        }
+    } else {
+        const uint64_t K = Lp / FT;
+        TreeStack<T, 1, kMaxLogL + 1> st;
+        T v[1];
+        for (uint64_t k = 0; k < K; ++k) {
+            const uint64_t j = t * K + k;
+            v[0] = (j < L) ? pw_partials<T, PB>(f.partial, L, j, 0, P) : neg_zero<T>();
+            st.push(k, v);
+        }
+        st.collapse(K, v);
+        s_v[t] = v[0];
+        __syncthreads();
+        for (int h = 1; h < FT; h *= 2) {
+            if (t % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h];
+            __syncthreads();
+        }
+    }
+    if (t == 0) f.out[0] = f.init + s_v[0];
+}
+
+// After a streaming workgroup has written its partials (store_coherent;
+// every thread calls this): every wave waits until its stores are performed,
+// then the workgroup's flag is set to the call id; the last workgroup
+// instead waits (bounded) for every other flag, finishes, and writes the
+// error word.  Only the last workgroup waits, and only for workgroups that
+// never wait, so the wait ends whatever the grid and however many
+// workgroups are resident.
+template <typename T, int FT>
+__device__ __forceinline__ void arrive_or_finish(const ReduceFin<T>& f, T* s_v)
+{
+    const uint64_t nwg = (uint64_t)gridDim.x * gridDim.y;
+    const uint64_t me = (uint64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores performed
+    __syncthreads();
+    if (me + 1 < nwg) {
+        if (threadIdx.x == 0)
+            __hip_atomic_store(f.flags + me, f.call_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    int late = 0;
+    for (uint64_t i = threadIdx.x; i + 1 < nwg && !late; i += FT) {
+        long it = 0;
+        while (__hip_atomic_load(f.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+               f.call_id) {
+            if (++it > kSpinLimit) {
+                late = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    late = __syncthreads_or(late);
+    finish_block<T, FT>(f, s_v);
+    if (threadIdx.x == 0) *f.err = late ? kErrSpin : 0u;
+}
 
 // ============================================================================
 // Streaming kernel for L = 2^LOGL and 16-byte aligned input.
@@ -146,12 +301,13 @@ __device__ __forceinline__ void pow2_batch(const T* __restrict__ x, uint64_t n, 
 
 template <typename T, int LOGL>
 __global__ __launch_bounds__((Pow2Geom<T, LOGL>::THREADS)) void k_reduce_pow2(
-    const T* __restrict__ x, uint64_t n, int rw_log, T* __restrict__ partial)
+    const T* __restrict__ x, uint64_t n, int rw_log, ReduceFin<T> f)
 {
     using GM = Pow2Geom<T, LOGL>;
     constexpr int VE = GM::VE;
     constexpr uint64_t L = 1ull << LOGL;
     __shared__ T s_wave[GM::WAVES][GM::SW];
+    __shared__ T s_fin[GM::THREADS];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane & (GM::CW - 1), g = lane >> GM::LOG_CW;
@@ -194,8 +350,9 @@ __global__ __launch_bounds__((Pow2Geom<T, LOGL>::THREADS)) void k_reduce_pow2(
         for (int h = 1; h < GM::WAVES; h *= 2)
 #pragma unroll
             for (int w = 0; w < GM::WAVES; w += 2 * h) t[w] = t[w] + t[w + h];
-        partial[p * L + (uint64_t)slice * GM::SW + threadIdx.x] = t[0];
+        store_coherent(f.partial + p * L + (uint64_t)slice * GM::SW + threadIdx.x, t[0]);
     }
+    arrive_or_finish<T, GM::THREADS>(f, s_fin);
 }
 
 // ============================================================================
@@ -209,7 +366,7 @@ template <typename T>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce_general(const T* __restrict__ x,
                                                                    uint64_t n, uint32_t L,
                                                                    int lw_log, int rs_log,
-                                                                   T* __restrict__ partial)
+                                                                   ReduceFin<T> f)
 {
     __shared__ T s_seg[kReduceThreads];
     const int LW = 1 << lw_log, S = kReduceThreads >> lw_log;
@@ -250,88 +407,9 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_general(const T* __re
         if (s % (2 * h) == 0) s_seg[threadIdx.x] = s_seg[threadIdx.x] + s_seg[threadIdx.x + h * LW];
         __syncthreads();
     }
-    if (s == 0 && j < L) partial[p * L + j] = s_seg[jl];
-}
-
-// ============================================================================
-// Finishing kernel (one workgroup): lane value = PW over partial[0..P)[lane];
-// R = PW over lanes 0..L-1; out = init + R (init alone when n == 0).
-// L is padded to Lp = 2^ceil(log2 L) with -0.0 lanes.
-//   Lp <= 1024: S = 1024/Lp threads per lane, each over an aligned power-of-
-//     two segment of the partials; segments and then lanes merged in LDS.
-//   Lp > 1024: thread t owns lanes [t*K, (t+1)*K), K = Lp/1024.
-// ============================================================================
-template <typename T>
-__device__ __forceinline__ T pw_partials(const T* __restrict__ partial, uint64_t L, uint64_t j,
-                                         uint64_t q0, uint64_t q1)
-{
-    TreeStack<T, 1, kReduceStackDepth> st;
-    T v[1];
-    const uint64_t nb = q1 > q0 ? (q1 - q0 + 7) / 8 : 0;
-    for (uint64_t k = 0; k < nb; ++k) {
-        T a[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint64_t q = q0 + k * 8 + u;
-            a[u] = q < q1 ? partial[q * L + j] : neg_zero<T>();
-        }
-#pragma unroll
-        for (int h = 1; h < 8; h *= 2)
-#pragma unroll
-            for (int u = 0; u < 8; u += 2 * h) a[u] = a[u] + a[u + h];
-        v[0] = a[0];
-        st.push(k, v);
-    }
-    st.collapse(nb, v);
-    return v[0];
-}
-
-template <typename T>
-__global__ __launch_bounds__(kFinishThreads) void k_reduce_finish(const T* __restrict__ partial,
-                                                                  uint64_t P, uint32_t L,
-                                                                  int lp_log, uint64_t n, T init,
-                                                                  T* __restrict__ out)
-{
-    __shared__ T s_v[kFinishThreads];
-    const int t = threadIdx.x;
-    const uint64_t Lp = 1ull << lp_log;
-    if (Lp <= kFinishThreads) {
-        const int S = kFinishThreads >> lp_log;
-        const uint64_t j = t & (Lp - 1);
-        const int s = t >> lp_log;
-        uint64_t ps = 1;
-        while (ps * S < P) ps *= 2;
-        const uint64_t q0 = s * ps, q1 = (q0 + ps) < P ? (q0 + ps) : P;
-        T v = (j < L) ? pw_partials(partial, L, j, q0, q1) : neg_zero<T>();
-        s_v[t] = v;
-        __syncthreads();
-        for (int h = 1; h < S; h *= 2) {
-            if (s % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h * (int)Lp];
-            __syncthreads();
-        }
-        // lanes 0..Lp-1 now at s_v[0..Lp)
-        for (uint64_t h = 1; h < Lp; h *= 2) {
-            if ((uint64_t)t < Lp && t % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h];
-            __syncthreads();
-        }
-    } else {
-        const uint64_t K = Lp / kFinishThreads;
-        TreeStack<T, 1, 17> st;
-        T v[1];
-        for (uint64_t k = 0; k < K; ++k) {
-            const uint64_t j = t * K + k;
-            v[0] = (j < L) ? pw_partials(partial, L, j, 0, P) : neg_zero<T>();
-            st.push(k, v);
-        }
-        st.collapse(K, v);
-        s_v[t] = v[0];
-        __syncthreads();
-        for (int h = 1; h < kFinishThreads; h *= 2) {
-            if (t % (2 * h) == 0) s_v[t] = s_v[t] + s_v[t + h];
-            __syncthreads();
-        }
-    }
-    if (t == 0) out[0] = (n == 0) ? init : init + s_v[0];
+    if (s == 0 && j < L) store_coherent(f.partial + p * L + j, s_seg[jl]);
+    __syncthreads();  // s_seg is the finish's LDS
+    arrive_or_finish<T, kReduceThreads>(f, s_seg);
 }
 
 // ============================================================================
@@ -530,46 +608,50 @@ static hipError_t launch_rows_pow2_dispatch(int logl, const T* x, uint64_t rows,
 // Host-side launchers (called from api.cpp).
 // ============================================================================
 template <typename T, int LOGL>
-static hipError_t launch_pow2_one(const T* x, uint64_t n, const ReducePlan& pl, T* partial,
-                                  hipStream_t s)
+static hipError_t launch_pow2_one(const T* x, uint64_t n, const ReducePlan& pl,
+                                  const ReduceFin<T>& f, hipStream_t s)
 {
     dim3 grid((unsigned)pl.P, (unsigned)pl.slices);
     hipLaunchKernelGGL((k_reduce_pow2<T, LOGL>), grid, dim3(Pow2Geom<T, LOGL>::THREADS), 0, s, x,
-                       n, pl.rw_log, partial);
+                       n, pl.rw_log, f);
     return hipGetLastError();
 }
 
 template <typename T, int LOGL>
 static hipError_t launch_pow2_dispatch(int logl, const T* x, uint64_t n, const ReducePlan& pl,
-                                       T* partial, hipStream_t s)
+                                       const ReduceFin<T>& f, hipStream_t s)
 {
     if constexpr (LOGL > kMaxLogL) {
         return hipErrorInvalidValue;
     } else {
-        if (logl == LOGL) return launch_pow2_one<T, LOGL>(x, n, pl, partial, s);
-        return launch_pow2_dispatch<T, LOGL + 1>(logl, x, n, pl, partial, s);
+        if (logl == LOGL) return launch_pow2_one<T, LOGL>(x, n, pl, f, s);
+        return launch_pow2_dispatch<T, LOGL + 1>(logl, x, n, pl, f, s);
     }
 }
 
 template <typename T, bool POW2>
-hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, T* partial,
-                         const ReducePlan& pl, hipStream_t s)
+hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, void* ws,
+                         const ReducePlan& pl, uint64_t call_id, hipStream_t s)
 {
-    if (pl.P > 0) {
-        hipError_t e;
-        if (pl.pow2) {
-            if constexpr (POW2) e = launch_pow2_dispatch<T, 0>(pl.logl, x, n, pl, partial, s);
-            else return hipErrorInvalidValue;
-        } else {
-            dim3 grid((unsigned)pl.P, (unsigned)pl.slices);
-            hipLaunchKernelGGL((k_reduce_general<T>), grid, dim3(kReduceThreads), 0, s, x, n, L,
-                               pl.lw_log, pl.rs_log, partial);
-            e = hipGetLastError();
-        }
-        if (e != hipSuccess) return e;
+    if (pl.P == 0) return hipErrorInvalidValue;
+    const ReduceWs w = reduce_ws_layout(pl, L, sizeof(T));
+    unsigned char* b = static_cast<unsigned char*>(ws);
+    const ReduceFin<T> f{reinterpret_cast<T*>(b + w.partial_off),
+                         reinterpret_cast<uint64_t*>(b + w.flags_off),
+                         reinterpret_cast<uint32_t*>(b),
+                         call_id,
+                         pl.P,
+                         L,
+                         pl.lp_log,
+                         init,
+                         out};
+    if (pl.pow2) {
+        if constexpr (POW2) return launch_pow2_dispatch<T, 0>(pl.logl, x, n, pl, f, s);
+        return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((k_reduce_finish<T>), dim3(1), dim3(kFinishThreads), 0, s, partial, pl.P,
-                       L, pl.lp_log, n, init, out);
+    dim3 grid((unsigned)pl.P, (unsigned)pl.slices);
+    hipLaunchKernelGGL((k_reduce_general<T>), grid, dim3(kReduceThreads), 0, s, x, n, L, pl.lw_log,
+                       pl.rs_log, f);
     return hipGetLastError();
 }
 

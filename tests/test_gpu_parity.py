@@ -99,6 +99,31 @@ def test_reduce_repeatable(canon):
         assert_bit_exact(to_host(canon.reduce(xd, 128, 1.0)).reshape(1), [want], "repeat")
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_reduce_workspace_reuse(canon, dtype):
+    """The finishing workgroup waits for flags tagged with the call's own id:
+    whatever a workspace holds on entry (all bits set, random bytes, the
+    flags and partials of earlier calls with larger and smaller grids, other
+    lane counts, the general kernel), every call gives the oracle's bits and
+    leaves its error word 0."""
+    n_big = 5_000_003
+    x = synth.generate(n_big + 1, "mixed_magnitude", 12, dtype)
+    xd = to_dev(x)
+    es = xd.element_size()
+    nb = max(canon.reduce_workspace_bytes(n, L, es) for n in (n_big, 777, 65_536)
+             for L in (1, 16, 128, 1000))
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    cases = [(n_big, 128), (777, 16), (n_big, 16), (65_536, 1000), (n_big, 1), (777, 128)]
+    for i, (n, L) in enumerate(cases):
+        if i == 3:
+            ws.copy_(torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda"))
+        for start in (0, 1):  # aligned: register kernel; start 1: general kernel
+            got = to_host(canon.reduce(xd[start:start + n], L, 0.5, ws=ws, check=True))
+            assert_bit_exact(got.reshape(1), [oracle.reduce(x[start:start + n], L, 0.5)],
+                             f"n={n} L={L} start={start}")
+            assert canon.workspace_error(ws) == 0
+
+
 # ------------------------------------------------------------ reduce rows
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("L", [1, 3, 16, 128, 300, 1024])
