@@ -303,8 +303,10 @@ def main():
             if name == "reduce":
                 want = oracle.reduce(x_np, 128, 1.0)
                 got = r0.cpu().numpy().reshape(1)
-                ok = bool(bits_equal(got, [want]).all())
+                err = canon.workspace_error(ws)
+                ok = bool(bits_equal(got, [want]).all()) and err == 0
                 w["sha256"] = synth.sha256(got)
+                w["error_word"] = int(err)
             elif name == "rows_reduce":
                 want = oracle.reduce_rows(X_np, 16, 0.0)
                 got = rr.cpu().numpy()
@@ -594,7 +596,7 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
                              dtype=torch.uint8, device=dev)
             canon.reduce(x, L, init, out=out, ws=ws)
             got = out.cpu().numpy().reshape(1)
-            ok = same(got, [oracle.reduce(xn, L, init)])
+            ok = same(got, [oracle.reduce(xn, L, init)]) and canon.workspace_error(ws) == 0
             wit = {"sha256": synth.sha256(got), "checked": "the result", "values": hex_bits(got)}
             us = timed(lambda: canon.reduce(x, L, init, out=out, ws=ws))
             add(cfg, f"reduce L={L} init={init}", str(xn.dtype), xn.size, xn.nbytes, us, ok, wit)
