@@ -303,10 +303,17 @@ canon_status_t canon_scan_noalloc_f64(const double* x, double* y, size_t n, int 
  *   CANON_SCHED_REDUCE_PARTIALS  workgroups (row ranges, hence partials) the
  *                                streaming reduce aims for; the reduce
  *                                workspace size follows it
+ *   CANON_SCHED_SPIN_LIMIT       polls of every bounded wait (single-pass
+ *                                scans, the reduce's finish) before it gives
+ *                                up and records the error word; for tests of
+ *                                that path only: a small value makes waits
+ *                                give up, and the output is then invalid
+ *                                (default 2^20)
  * Returns CANON_EINVAL for an unknown knob.  Not synchronised with calls in
  * flight on other host threads: set it between calls. */
 #define CANON_SCHED_GRID 0
 #define CANON_SCHED_REDUCE_PARTIALS 1
+#define CANON_SCHED_SPIN_LIMIT 2
 canon_status_t canon_set_schedule(int knob, uint64_t value);
 uint64_t canon_get_schedule(int knob);
 

@@ -36,7 +36,7 @@ CanonError.
 
     scan_tile_elems(policy, param, elem_size), scan_rows_tile_elems(...)
                                        -> elements per scan tile
-    set_schedule(knob, value), schedule(grid=..., reduce_partials=...)
+    set_schedule(knob, value), schedule(grid=..., reduce_partials=..., spin_limit=...)
                                        -> the schedule override (tests)
 """
 from __future__ import annotations
@@ -73,7 +73,7 @@ EXPORTS = [
 ]
 
 ABI_VERSION = 4
-SCHED = {"grid": 0, "reduce_partials": 1}
+SCHED = {"grid": 0, "reduce_partials": 1, "spin_limit": 2}
 
 _lib = None
 
@@ -478,7 +478,8 @@ def scan_rows_tile_elems(policy, param: int, elem_size: int) -> int:
 
 
 def set_schedule(knob, value: int) -> None:
-    """The schedule override ("grid" or "reduce_partials"; 0 = default)."""
+    """The schedule override ("grid", "reduce_partials" or "spin_limit";
+    0 = default)."""
     k = SCHED[knob] if isinstance(knob, str) else int(knob)
     _check(lib().canon_set_schedule(k, int(value)), "set_schedule")
 

@@ -299,6 +299,7 @@ canon_status_t canon_set_schedule(int knob, uint64_t value)
         case CANON_SCHED_REDUCE_PARTIALS:
             g_sched_reduce_wg.store(value, std::memory_order_relaxed);
             break;
+        case CANON_SCHED_SPIN_LIMIT: g_sched_spin_limit.store(value, std::memory_order_relaxed); break;
         default: return CANON_EINVAL;
     }
     return CANON_OK;
@@ -309,6 +310,7 @@ uint64_t canon_get_schedule(int knob)
     switch (knob) {
         case CANON_SCHED_GRID: return g_sched_grid_cap.load(std::memory_order_relaxed);
         case CANON_SCHED_REDUCE_PARTIALS: return g_sched_reduce_wg.load(std::memory_order_relaxed);
+        case CANON_SCHED_SPIN_LIMIT: return g_sched_spin_limit.load(std::memory_order_relaxed);
         default: return 0;
     }
 }

@@ -369,8 +369,18 @@ __device__ __forceinline__ void publish(uint64_t* slot, T v)
     __hip_atomic_store(slot, pack_word(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The bound of a wait: header word 2 of the workspace whose error word is
+// `err` (its first 32 bits), written by the call's init kernel (0: the
+// default, kSpinLimit).
+__device__ __forceinline__ long spin_limit_of(const uint32_t* err)
+{
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(err) + 2,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v ? (long)v : kSpinLimit;
+}
+
 // Poll a published word until it is ready.  The wait is bounded: after
-// kSpinLimit polls, or as soon as another wave has recorded an error, the
+// spin_limit_of(err) polls, or as soon as another wave has recorded an error, the
 // kernel's error word gets kErrSpin and -0.0 is returned, so that every wave
 // still runs to completion and the host can report the failure.
 template <typename T>
@@ -378,10 +388,12 @@ __device__ __forceinline__ T wait_word(uint64_t* slot, uint32_t* err)
 {
     const uint64_t nr = not_ready_word<T>();
     uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w != nr) return unpack_word<T>(w);
+    const long limit = spin_limit_of(err);
     long it = 0;
     while (w == nr) {
         ++it;
-        if (it > kSpinLimit ||
+        if (it > limit ||
             ((it & 63) == 0 &&
              __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
             __hip_atomic_fetch_or(err, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

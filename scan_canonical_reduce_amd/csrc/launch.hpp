@@ -15,6 +15,7 @@ namespace canon {
 // Both change how the work is spread over workgroups, never the results.
 inline std::atomic<uint64_t> g_sched_grid_cap{0};
 inline std::atomic<uint64_t> g_sched_reduce_wg{0};
+inline std::atomic<uint64_t> g_sched_spin_limit{0};  // polls of a bounded wait (0: default)
 
 // Compute units of the current device (cached per device; 256 if unknown).
 inline uint64_t device_cus()

@@ -37,6 +37,7 @@ struct ReduceFin {
     int lp_log;
     T init;
     T* out;
+    long spin_limit;  // polls of the finishing workgroup's wait
 };
 
 // Partial values move between workgroups with device-coherent accesses
@@ -168,7 +169,7 @@ __device__ __forceinline__ void arrive_or_finish(const ReduceFin<T>& f, T* s_v)
         long it = 0;
         while (__hip_atomic_load(f.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
                f.call_id) {
-            if (++it > kSpinLimit) {
+            if (++it > f.spin_limit) {
                 late = 1;
                 break;
             }
@@ -636,6 +637,7 @@ hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, voi
     if (pl.P == 0) return hipErrorInvalidValue;
     const ReduceWs w = reduce_ws_layout(pl, L, sizeof(T));
     unsigned char* b = static_cast<unsigned char*>(ws);
+    const uint64_t lim = g_sched_spin_limit.load(std::memory_order_relaxed);
     const ReduceFin<T> f{reinterpret_cast<T*>(b + w.partial_off),
                          reinterpret_cast<uint64_t*>(b + w.flags_off),
                          reinterpret_cast<uint32_t*>(b),
@@ -644,7 +646,8 @@ hipError_t launch_reduce(const T* x, uint64_t n, uint32_t L, T init, T* out, voi
                          L,
                          pl.lp_log,
                          init,
-                         out};
+                         out,
+                         lim ? (long)lim : kSpinLimit};
     if (pl.pow2) {
         if constexpr (POW2) return launch_pow2_dispatch<T, 0>(pl.logl, x, n, pl, f, s);
         return hipErrorInvalidValue;

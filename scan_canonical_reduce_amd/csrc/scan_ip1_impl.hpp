@@ -70,16 +70,18 @@ __device__ __forceinline__ uint32_t* ip1_counter(uint64_t* ws, const IpSingleLay
     return reinterpret_cast<uint32_t*>(ws + lay.cbase) + lv.coff[k] + seg * lv.cnt[k] + v;
 }
 
-// Header (error word, ticket), every node word not ready, counters zero.
+// Header (error word, ticket; word 2 the bound of the call's waits, 0 for
+// the default), every node word not ready, counters zero.
 template <typename T>
-__global__ __launch_bounds__(256) void k_ip1_init(uint64_t* __restrict__ ws, IpSingleLayout lay)
+__global__ __launch_bounds__(256) void k_ip1_init(uint64_t* __restrict__ ws, IpSingleLayout lay,
+                                                  uint64_t spin_limit)
 {
     const uint64_t nr = not_ready_word<T>();
     const uint64_t cw = (lay.counters + 1) / 2;
     const uint64_t total = lay.cbase + cw;
     for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < total;
          i += (uint64_t)gridDim.x * 256)
-        ws[i] = i < 32 ? 0ull : (i < lay.cbase ? nr : 0ull);
+        ws[i] = i < 32 ? (i == 2 ? spin_limit : 0ull) : (i < lay.cbase ? nr : 0ull);
 }
 
 template <typename T, int LOGRV>
@@ -476,7 +478,8 @@ hipError_t launch_scan_ip_single(const T* x, uint64_t ldx, T* y, uint64_t ldy, u
     const uint64_t words = lay.cbase + (lay.counters + 1) / 2;
     uint64_t blocks = (words + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL((k_ip1_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws, lay);
+    hipLaunchKernelGGL((k_ip1_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws, lay,
+                       g_sched_spin_limit.load(std::memory_order_relaxed));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (out) return launch_ip1_o<T, true>(x, ldx, y, ldy, cols, ws, lay, *out, aligned, s);

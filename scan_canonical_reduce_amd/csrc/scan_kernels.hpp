@@ -163,14 +163,15 @@ __device__ __forceinline__ void lookback_combine(uint64_t t, const T* s_low, con
     }
 }
 
-// Header words zeroed, every published word marked not ready.
+// Header words zeroed but word 2, the bound of the call's waits (0: the
+// default; spin_limit_of); every published word marked not ready.
 template <typename T>
-__global__ void k_scan_init(uint64_t* __restrict__ ws, uint64_t total)
+__global__ void k_scan_init(uint64_t* __restrict__ ws, uint64_t total, uint64_t spin_limit)
 {
     const uint64_t nr = not_ready_word<T>();
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (uint64_t)gridDim.x * blockDim.x)
-        ws[i] = i < 32 ? 0ull : nr;
+        ws[i] = i < 32 ? (i == 2 ? spin_limit : 0ull) : nr;
 }
 
 template <typename T>
@@ -179,7 +180,7 @@ inline void launch_scan_init(uint64_t* ws, const ScanLayout& lay, hipStream_t s)
     uint64_t blocks = (lay.total_words + 255) / 256;
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL((k_scan_init<T>), dim3((unsigned)blocks), dim3(256), 0, s, ws,
-                       lay.total_words);
+                       lay.total_words, g_sched_spin_limit.load(std::memory_order_relaxed));
 }
 
 // Whether tile t ends its group (its workgroup then runs group_build).

@@ -180,7 +180,10 @@ def test_schedule_override(canon):
     default = L.canon_reduce_workspace_bytes(1 << 24, 16, 8)
     with canon.schedule(reduce_partials=4096):
         assert L.canon_reduce_workspace_bytes(1 << 24, 16, 8) > default
-    assert L.canon_set_schedule(2, 1) == 1
+    with canon.schedule(spin_limit=5):
+        assert L.canon_get_schedule(2) == 5
+    assert L.canon_get_schedule(2) == 0
+    assert L.canon_set_schedule(3, 1) == 1  # unknown knob: CANON_EINVAL
     assert L.canon_get_schedule(9) == 0
 
 

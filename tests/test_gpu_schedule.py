@@ -32,6 +32,7 @@ def canon():
     yield c
     c.set_schedule("grid", 0)
     c.set_schedule("reduce_partials", 0)
+    c.set_schedule("spin_limit", 0)
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
@@ -89,3 +90,38 @@ def test_rows_grid(canon, dtype):
             for p, want in want_s.items():
                 assert_bit_exact(to_host(canon.scan_rows(Xd, *p, check=True)), want,
                                  f"scan_rows {p} grid={grid}")
+
+
+def test_bounded_wait_gives_up(canon):
+    """The failure path of the bounded waits, forced from the host (a wait
+    that cannot end must not hang the kernel, and the failure must reach
+    the caller).
+    With a bound of one poll, the reduce's finishing workgroup gives up on
+    the flags of workgroups still streaming: the kernel still finishes, its
+    error word is set and the binding raises.  Whether a given call waits at
+    all depends on timing, so five calls must give at least one error.  The
+    scans take the same path when a look-back word is late; they must finish
+    either way.  With the bound restored every call is exact again."""
+    n = (1 << 26) + 3
+    x = synth.generate(n, "mixed_magnitude", 74)
+    xd = to_dev(x)
+    errors = 0
+    with canon.schedule(spin_limit=1):
+        for _ in range(5):
+            try:
+                canon.reduce(xd, 128, 1.0, check=True)
+            except canon.CanonError:
+                errors += 1
+        for policy, param in (("pairwise", 0), ("iterated_pairwise", 128)):
+            for _ in range(3):
+                try:
+                    canon.scan(xd, policy, param, check=True)
+                except canon.CanonError:
+                    pass
+    assert errors >= 1, "no reduce call reported its bounded wait giving up"
+    assert canon.get_schedule("spin_limit") == 0
+    got = to_host(canon.reduce(xd, 128, 1.0, check=True)).reshape(1)
+    assert_bit_exact(got, [oracle.reduce(x, 128, 1.0)], "reduce after")
+    m = 1 << 22
+    got = to_host(canon.scan(xd[:m], "pairwise", 0, check=True))
+    assert_bit_exact(got, oracle.scan(x[:m], "pairwise", 0), "scan after")
