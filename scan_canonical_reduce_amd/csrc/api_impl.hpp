@@ -206,7 +206,7 @@ inline bool is_ip(int policy, uint32_t param) { return policy == CANON_ITERATED_
 
 // The register geometry of the iterated_pairwise scan runs in one pass (its
 // items must fit one launch); any other geometry in three kernels.
-inline bool ip_single(const IpLayout& ip) { return ip.fast_logrv >= 0; }
+inline bool ip_single(const IpLayout& ip) { return ip.fast_logrv != kIpNoFast; }
 inline bool ip_fits(const IpLayout& ip) { return ip.nseg * ip.tps < (1ull << 31); }
 
 // Workspace of an iterated_pairwise scan: the largest of its possible plans

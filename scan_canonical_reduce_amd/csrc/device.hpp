@@ -308,6 +308,22 @@ __device__ __forceinline__ T shfl_up1(T v)
     }
 }
 
+// Value of `v` held by lane `src` (0 .. 63), through the LDS crossbar.
+template <typename T>
+__device__ __forceinline__ T shfl_idx(T v, int src)
+{
+    const int addr = (int)(((uint32_t)src & 63u) << 2);
+    if constexpr (sizeof(T) == 8) {
+        uint64_t b = __builtin_bit_cast(uint64_t, v);
+        uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)b);
+        uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(b >> 32));
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    } else {
+        return __builtin_bit_cast(
+            T, (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)__builtin_bit_cast(uint32_t, v)));
+    }
+}
+
 // Value of `v` held by the last lane of the lower half of this lane's aligned
 // group of 2*H lanes: lane ((lane & ~(2H-1)) | (H-1)).  H in {1,...,32}.
 template <int H, typename T>

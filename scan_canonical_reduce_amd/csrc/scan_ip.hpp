@@ -7,7 +7,8 @@
 namespace canon {
 
 constexpr int kIpThreads = 256;
-constexpr int kIpMaxRLog = 6;         // at most 64 rows per tile
+constexpr int kIpMaxRLog = 6;         // LDS path: at most 64 rows per tile
+constexpr int kIpNoFast = -100;       // IpLayout::fast_logrv of the LDS path
 constexpr int kIpLevelsPerPass = 4;   // node levels built per launch
 constexpr int kIpMaxLevels = 48;
 constexpr uint64_t kIpMaxGrid = 0x7FFFFFFFull;  // one workgroup per item
@@ -40,7 +41,7 @@ struct IpLayout {
     uint64_t off[kIpMaxLevels];
     uint64_t cl_off;  // chunked: offset of the chunk trees (elements)
     uint64_t total;   // elements of node (and chunk tree) storage
-    int fast_logrv;   // >= 0: register path with L = 64 * E * 2^fast_logrv; -1: LDS path
+    int fast_logrv;   // register path with L = E * 2^(6 + fast_logrv), -6 .. 3; else kIpNoFast
 };
 
 // LDS budget (elements) for the per-row trees of one tile: (R + 1) * 2 * Lp
@@ -57,12 +58,12 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
     lay.lp_log = lp;
     const uint64_t Lp = 1ull << lp;
     const int loge = elem_size == 8 ? 1 : 2;
-    lay.fast_logrv = -1;
+    lay.fast_logrv = kIpNoFast;
     lay.chunk_log = lp;
     int rl;
-    if (aligned && Lp == L && lp >= loge + 6 && lp <= loge + 9) {
+    if (aligned && Lp == L && lp >= loge && lp <= loge + 9) {
         lay.fast_logrv = lp - loge - 6;
-        rl = 6 - lay.fast_logrv;  // 64 / RV rows per tile
+        rl = 6 - lay.fast_logrv;  // 4096 E / L rows per tile
     } else {
         if (Lp > kIpWholeRowMaxL) lay.chunk_log = kIpChunkLog;
         const uint64_t Lc = 1ull << lay.chunk_log;

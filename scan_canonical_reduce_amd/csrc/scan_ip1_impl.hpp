@@ -45,7 +45,7 @@ constexpr int kIp1Stage = 1024;
 template <int LOGRV>
 constexpr bool ip1_pipelined()
 {
-    return LOGRV == 0;
+    return LOGRV <= 0;
 }
 
 // The per-level arrays of the layout, copied to LDS by every workgroup: a
@@ -159,18 +159,23 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
     const IpSingleLayout& lay = *c.lay;
     const uint64_t seg = s.item / lay.g.tps, t = s.item % lay.g.tps;
     const int lane = c.lane, w = c.w;
+    // the lanes holding the wave's last rows (every lane for wide rows)
+    const bool last = F::group(lane) == F::G - 1;
     auto& a = s.a;
 
     ipf_columns_in_wave<T, LOGRV>(a);
+    if constexpr (F::G > 1) ipf_groups_in_wave<T, LOGRV>(a, lane);
+    if (last) {
 #pragma unroll
-    for (int q = 0; q < RV; ++q) lds_store_vec(&c.sh->row[w][(q * 64 + lane) * E], a[(RW - 1) * RV + q]);
+        for (int q = 0; q < RV; ++q) lds_store_vec(&c.sh->row[w][F::col(q, lane)], a[(RW - 1) * RV + q]);
+    }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < RV; ++q) {
         T r0[E], r1[E], r2[E];
-        lds_load_vec(&c.sh->row[0][(q * 64 + lane) * E], r0);
-        lds_load_vec(&c.sh->row[1][(q * 64 + lane) * E], r1);
-        lds_load_vec(&c.sh->row[2][(q * 64 + lane) * E], r2);
+        lds_load_vec(&c.sh->row[0][F::col(q, lane)], r0);
+        lds_load_vec(&c.sh->row[1][F::col(q, lane)], r1);
+        lds_load_vec(&c.sh->row[2][F::col(q, lane)], r2);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const T t0 = r0[e], t1 = r1[e], t2 = r2[e];
@@ -198,7 +203,7 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 cur[q][e] = a[(RW - 1) * RV + q][e];
-                publish(word(0, t, (uint64_t)(q * 64 + lane) * E + e), cur[q][e]);
+                if (last) publish(word(0, t, F::col(q, lane) + e), cur[q][e]);
             }
         uint64_t u = t;
         for (int k = 0; k + 1 < lay.g.levels; ++k) {
@@ -210,23 +215,25 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
                                                 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             before = __builtin_amdgcn_readfirstlane(before);
             if (before == 0) break;  // the sibling completes the parent
-            // the sibling's words: all reads issued, then each waited for
-            uint64_t sw[RV][E];
+            if (last) {
+                // the sibling's words: all reads issued, then each waited for
+                uint64_t sw[RV][E];
 #pragma unroll
-            for (int q = 0; q < RV; ++q)
+                for (int q = 0; q < RV; ++q)
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    sw[q][e] = __hip_atomic_load(word(k, u ^ 1, (uint64_t)(q * 64 + lane) * E + e),
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int e = 0; e < E; ++e)
+                        sw[q][e] = __hip_atomic_load(word(k, u ^ 1, F::col(q, lane) + e),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int q = 0; q < RV; ++q)
+                for (int q = 0; q < RV; ++q)
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint64_t col = (uint64_t)(q * 64 + lane) * E + e;
-                    const T sib = ready_or_wait<T>(sw[q][e], word(k, u ^ 1, col), c.err);
-                    cur[q][e] = (u & 1) ? sib + cur[q][e] : cur[q][e] + sib;
-                    publish(word(k + 1, v, col), cur[q][e]);
-                }
+                    for (int e = 0; e < E; ++e) {
+                        const uint64_t col = F::col(q, lane) + e;
+                        const T sib = ready_or_wait<T>(sw[q][e], word(k, u ^ 1, col), c.err);
+                        cur[q][e] = (u & 1) ? sib + cur[q][e] : cur[q][e] + sib;
+                        publish(word(k + 1, v, col), cur[q][e]);
+                    }
+            }
             u = v;
         }
     }
@@ -243,8 +250,9 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
     // The node words are read by waves 0-2 alone: wave 3 comes to the back
     // from the front's climb, and its reads would hold up the batch.
     constexpr int RT = kIpThreads - 64;                  // reading threads
-    constexpr int NB = SH::STAGE / F::L;                 // nodes per batch
-    constexpr int PER = (SH::STAGE + RT - 1) / RT;       // words per reading thread
+    constexpr int NB = SH::STAGE / F::L < 16 ? SH::STAGE / F::L : 16;  // nodes per batch
+    constexpr int WORDS = NB * F::L;                     // words per batch
+    constexpr int PER = (WORDS + RT - 1) / RT;           // words per reading thread
     const IpSingleLayout& lay = *c.lay;
     const uint64_t seg = s.item / lay.g.tps, t = s.item % lay.g.tps;
     const int lane = c.lane, w = c.w;
@@ -279,7 +287,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
                 const int idx = i * RT + (int)threadIdx.x;
                 const int m = idx / F::L, col = idx % F::L;
                 wv[i] = not_ready_word<T>();
-                if (idx < SH::STAGE && m < nb)
+                if (idx < WORDS && m < nb)
                     wv[i] = __hip_atomic_load(node(lv[m], col), __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -287,7 +295,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
             for (int i = 0; i < PER; ++i) {
                 const int idx = i * RT + (int)threadIdx.x;
                 const int m = idx / F::L, col = idx % F::L;
-                if (idx < SH::STAGE && m < nb)
+                if (idx < WORDS && m < nb)
                     c.sh->h[idx] = ready_or_wait<T>(wv[i], node(lv[m], col), c.err);
             }
         }
@@ -296,7 +304,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
 #pragma unroll
             for (int q = 0; q < RV; ++q) {
                 T hv[E];
-                lds_load_vec(&c.sh->h[m * F::L + (q * 64 + lane) * E], hv);
+                lds_load_vec(&c.sh->h[m * F::L + F::col(q, lane)], hv);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
 #pragma unroll
@@ -307,13 +315,25 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         }
         __syncthreads();  // h is refilled by the next batch
     }
-    // the B row of each wave's first row: the A row just above it
+    // the B row of each thread's first row: the A row just above it (the
+    // group before in the wave, else the last rows of the wave before)
+    const int g = F::group(lane);
+    if (g == F::G - 1) {
 #pragma unroll
-    for (int q = 0; q < RV; ++q) lds_store_vec(&c.sh->row[w][(q * 64 + lane) * E], a[(RW - 1) * RV + q]);
+        for (int q = 0; q < RV; ++q) lds_store_vec(&c.sh->row[w][F::col(q, lane)], a[(RW - 1) * RV + q]);
+    }
     __syncthreads();
-    if (w > 0) {
+    if (w > 0 && g == 0) {
 #pragma unroll
-        for (int q = 0; q < RV; ++q) lds_load_vec(&c.sh->row[w - 1][(q * 64 + lane) * E], b[q]);
+        for (int q = 0; q < RV; ++q) lds_load_vec(&c.sh->row[w - 1][F::col(q, lane)], b[q]);
+    }
+    if constexpr (F::G > 1) {
+        const int src = (lane - F::TPR) & 63;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const T up = shfl_idx(a[RW - 1][e], src);
+            if (g > 0) b[0][e] = up;
+        }
     }
     __syncthreads();  // row[] is rewritten by the next front
 
@@ -326,7 +346,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         ta.template build<F::NV>(a, r * RV, lane);
         T val[RV][E];
         ip_walk<T, LOGRV>(a, r * RV, ta, tb, lane, val);
-        const uint64_t row = row0 + (uint64_t)w * RW + r;
+        const uint64_t row = row0 + F::row(w, lane, r);
         if constexpr (OUTX) {
             if (c.kind != kScanInclusive) {
                 // one position up, the value before a row's first lane being
@@ -338,14 +358,14 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
                     for (int q = 0; q < RV; ++q)
 #pragma unroll
                         for (int e = 0; e < E; ++e)
-                            if (row * F::L + (uint64_t)(q * 64 + lane) * E + e + 1 == c.cols)
+                            if (row * F::L + F::col(q, lane) + e + 1 == c.cols)
                                 ys[c.cols] = c.init + val[q][e];
                 }
                 T prev = tb.root;
 #pragma unroll
                 for (int q = 0; q < RV; ++q) {
                     const T up = shfl_up1(val[q][E - 1]);
-                    const T before = lane == 0 ? prev : up;
+                    const T before = F::sub(lane) == 0 ? prev : up;
                     prev = readlane(val[q][E - 1], 63);
 #pragma unroll
                     for (int e = E - 1; e > 0; --e) val[q][e] = val[q][e - 1];
@@ -359,7 +379,7 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         }
 #pragma unroll
         for (int q = 0; q < RV; ++q) {
-            const uint64_t gi = row * F::L + (uint64_t)(q * 64 + lane) * E;
+            const uint64_t gi = row * F::L + F::col(q, lane);
             if (AL && (full || gi + E <= c.cols)) {
                 store_vec(ys + gi, val[q]);
             } else {
@@ -454,11 +474,31 @@ static hipError_t launch_ip1(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint6
     return launch_ip1_al<T, LOGRV, OUTX, false>(x, ldx, y, ldy, cols, ws, lay, out, s);
 }
 
+// Narrow rows (L < 64 E), kept apart so that the plain double and float
+// kernels compile in units of their own (scan_ip1_narrow_*.hip).
+template <typename T, bool OUTX>
+hipError_t launch_ip1_narrow(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
+                             uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
+                             bool al, hipStream_t s)
+{
+    switch (lay.g.fast_logrv) {
+        case -6: return launch_ip1<T, -6, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case -5: return launch_ip1<T, -5, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case -4: return launch_ip1<T, -4, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case -3: return launch_ip1<T, -3, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case -2: return launch_ip1<T, -2, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        case -1: return launch_ip1<T, -1, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, bool OUTX>
 static hipError_t launch_ip1_o(const T* x, uint64_t ldx, T* y, uint64_t ldy, uint64_t cols,
                                uint64_t* ws, const IpSingleLayout& lay, const ScanOut<T>& out,
                                bool al, hipStream_t s)
 {
+    if (lay.g.fast_logrv < 0)
+        return launch_ip1_narrow<T, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
     switch (lay.g.fast_logrv) {
         case 0: return launch_ip1<T, 0, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);
         case 1: return launch_ip1<T, 1, OUTX>(x, ldx, y, ldy, cols, ws, lay, out, al, s);

@@ -1,5 +1,5 @@
-// Register geometry and lane trees of the iterated_pairwise scan's fast path
-// (shared by the three-kernel and the single-pass scans).
+// Register geometry and lane trees of the iterated_pairwise scan's
+// single-pass kernel.
 #pragma once
 
 #include "device.hpp"
@@ -8,24 +8,48 @@
 namespace canon {
 
 // ============================================================================
-// Fast path: L = 64 * E * RV with RV = 2^LOGRV in {1, ..., 8} (a row is RV
-// wave-wide 16-byte loads), 16-byte aligned rows.  A tile is 64 / RV rows;
-// each thread holds 16 vectors: wave w owns rows w*RW .. w*RW + RW-1
-// (RW = 16 / RV), vector u = row-in-wave u / RV, row-vector q = u % RV, lanes
-// (q * 64 + lane) * E + e.  The lane tree of a row has three kinds of levels:
-// inside a vector (static), across the 64 lanes (xor butterfly), across the
-// RV vectors of the row (in the thread).
+// Register geometry: L = E * 2^(6 + LOGRV) lanes, LOGRV in {-6, ..., 3},
+// 16-byte aligned rows; each thread holds 16 vectors of 16 bytes.
+//   LOGRV >= 0 (wide rows): a row is RV = 2^LOGRV wave-wide vectors; wave w
+//     owns rows w*RW .. w*RW + RW-1 (RW = 16 / RV), vector u = row-in-wave
+//     u / RV, row-vector q = u % RV, lanes (q * 64 + lane) * E + e.
+//   LOGRV < 0 (narrow rows): a row is the vectors of TPR = 2^(6 + LOGRV)
+//     consecutive lanes; the wave's lanes form G = 64 / TPR groups, group g
+//     (lanes g*TPR ..) owning 16 consecutive rows, so a wave holds 16 G rows
+//     and vector u of a thread is row (w*G + g)*16 + u, lanes
+//     (lane % TPR) * E + e.
+// A tile is 4 waves' rows (64 G / RV rows, 4096 E elements).  The lane tree
+// of a row has three kinds of levels: inside a vector (static), across the
+// TPR lanes of the row (xor butterfly), across the RV vectors of the row
+// (in the thread).
 // ============================================================================
 template <typename T, int LOGRV>
 struct IpFast {
+    static_assert(LOGRV >= -6 && LOGRV <= 3, "register geometry");
     static constexpr int E = Elem<T>::E;
     static constexpr int LOGE = Elem<T>::LOGE;
-    static constexpr int RV = 1 << LOGRV;
+    static constexpr int LOGT = LOGRV >= 0 ? 6 : 6 + LOGRV;  // lanes of a row vector
+    static constexpr int TPR = 1 << LOGT;
+    static constexpr int G = 64 / TPR;                        // row groups per wave
+    static constexpr int LOGV = LOGRV >= 0 ? LOGRV : 0;       // vectors per row
+    static constexpr int RV = 1 << LOGV;
     static constexpr int NV = 16;
-    static constexpr int RW = NV / RV;
-    static constexpr int LOGRW = 4 - LOGRV;
-    static constexpr int R = 4 * RW;  // rows per tile
-    static constexpr int L = 64 * E * RV;
+    static constexpr int RW = NV / RV;  // rows per thread
+    static constexpr int LOGRW = 4 - LOGV;
+    static constexpr int R = 4 * G * RW;  // rows per tile
+    static constexpr int L = TPR * E * RV;
+
+    // (constants for wide rows: one group, the column is the lane)
+    __device__ static int group(int lane) { return G == 1 ? 0 : lane >> LOGT; }
+    __device__ static int sub(int lane) { return TPR == 64 ? lane : lane & (TPR - 1); }
+    // first lane of the row held by vector q of a row of this thread, and
+    // the tile row of this thread's row-in-thread r (64-bit, so that the
+    // addresses of a thread's vectors stay one base and constant offsets)
+    __device__ static uint64_t col(int q, int lane) { return ((uint64_t)q * TPR + sub(lane)) * E; }
+    __device__ static uint64_t row(int w, int lane, int r)
+    {
+        return ((uint64_t)w * G + group(lane)) * RW + r;
+    }
 };
 
 // butterfly partner value of `v` held by lane ^ 2^K (VALU lane moves: the
@@ -43,8 +67,8 @@ __device__ __forceinline__ void ipf_load(const T* __restrict__ xs, uint64_t cols
     using F = IpFast<T, LOGRV>;
 #pragma unroll
     for (int u = 0; u < F::NV; ++u) {
-        const uint64_t row = row0 + (uint64_t)w * F::RW + u / F::RV;
-        const uint64_t gi = row * F::L + (uint64_t)((u % F::RV) * 64 + lane) * F::E;
+        const uint64_t row = row0 + F::row(w, lane, u / F::RV);
+        const uint64_t gi = row * F::L + F::col(u % F::RV, lane);
         if (!GUARD || gi + F::E <= cols) {
             load_vec(xs + gi, a[u]);
         } else {
@@ -73,6 +97,32 @@ __device__ __forceinline__ void ipf_columns_in_wave(T (&a)[16][Elem<T>::E])
                                               a[r * F::RV + q][e];
 }
 
+// Narrow rows: the pairwise prefix down each lane continued across the
+// wave's G row groups (Sklansky over groups, lower blocks first as inside
+// the thread): a group in the upper half of an aligned block of 2h groups
+// receives, on the left of every row, the end of the lower half, held by
+// the same column of group (g & ~(2h-1)) + h - 1.
+template <typename T, int LOGRV>
+__device__ __forceinline__ void ipf_groups_in_wave(T (&a)[16][Elem<T>::E], int lane)
+{
+    using F = IpFast<T, LOGRV>;
+    static_assert(F::RV == 1, "narrow rows only");
+    const int g = F::group(lane);
+#pragma unroll
+    for (int h = 1; h < F::G; h *= 2) {
+        const int src = (((g & ~(2 * h - 1)) + h - 1) << F::LOGT) | F::sub(lane);
+        T v[F::E];
+#pragma unroll
+        for (int e = 0; e < F::E; ++e) v[e] = shfl_idx(a[F::RW - 1][e], src);
+        if (g & h) {
+#pragma unroll
+            for (int r = 0; r < F::RW; ++r)
+#pragma unroll
+                for (int e = 0; e < F::E; ++e) a[r][e] = v[e] + a[r][e];
+        }
+    }
+}
+
 // The sibling values one row contributes to the walks of the lanes of a
 // row (its own, as the A side, or the next one, as the B side), per 16-byte
 // vector q of the row held by this thread:
@@ -82,10 +132,11 @@ __device__ __forceinline__ void ipf_columns_in_wave(T (&a)[16][Elem<T>::E])
 //   pv[l][q]:    this thread's subtree of vector q at vector level l.
 template <typename T, int LOGRV>
 struct IpRowTree {
-    static constexpr int E = Elem<T>::E, LOGE = Elem<T>::LOGE, RV = 1 << LOGRV;
+    using F = IpFast<T, LOGRV>;
+    static constexpr int E = F::E, LOGE = F::LOGE, RV = F::RV, LOGT = F::LOGT, LOGV = F::LOGV;
     T sv[LOGE][RV][E];
-    T o[6][RV];
-    T pv[LOGRV > 0 ? LOGRV : 1][RV];
+    T o[LOGT > 0 ? LOGT : 1][RV];
+    T pv[LOGV > 0 ? LOGV : 1][RV];
     T root;  // the complete tree over the whole row (the same in every lane)
 
     // row = vectors rows[v0 .. v0 + RV)
@@ -108,7 +159,7 @@ struct IpRowTree {
             p[q] = cur[0];
         }
 #define CANON_IP_TREE_LANE(K)                                                           \
-    {                                                                                   \
+    if constexpr ((K) < LOGT) {                                                         \
         const bool right = (lane >> (K)) & 1;                                           \
         _Pragma("unroll") for (int q = 0; q < RV; ++q)                                  \
         {                                                                               \
@@ -124,7 +175,7 @@ struct IpRowTree {
         CANON_IP_TREE_LANE(5)
 #undef CANON_IP_TREE_LANE
 #pragma unroll
-        for (int l = 0; l < LOGRV; ++l) {
+        for (int l = 0; l < LOGV; ++l) {
             const int h = 1 << l;
 #pragma unroll
             for (int q = 0; q < RV; ++q) pv[l][q] = p[q];
@@ -142,9 +193,10 @@ template <typename T, int LOGRV, int NV>
 __device__ __forceinline__ void ip_walk(const T (&rows)[NV][Elem<T>::E], int v0,
                                         const IpRowTree<T, LOGRV>& A,
                                         const IpRowTree<T, LOGRV>& B, int lane,
-                                        T (&val)[1 << LOGRV][Elem<T>::E])
+                                        T (&val)[IpFast<T, LOGRV>::RV][Elem<T>::E])
 {
-    constexpr int E = Elem<T>::E, LOGE = Elem<T>::LOGE, RV = 1 << LOGRV;
+    using F = IpFast<T, LOGRV>;
+    constexpr int E = F::E, LOGE = F::LOGE, RV = F::RV, LOGT = F::LOGT, LOGV = F::LOGV;
 #pragma unroll
     for (int q = 0; q < RV; ++q)
 #pragma unroll
@@ -159,7 +211,7 @@ __device__ __forceinline__ void ip_walk(const T (&rows)[NV][Elem<T>::E], int v0,
                 val[q][e] = (node & 1) ? A.sv[l][q][sib] + val[q][e] : val[q][e] + B.sv[l][q][sib];
             }
 #pragma unroll
-    for (int K = 0; K < 6; ++K) {
+    for (int K = 0; K < LOGT; ++K) {
         const bool right = (lane >> K) & 1;
 #pragma unroll
         for (int q = 0; q < RV; ++q)
@@ -168,7 +220,7 @@ __device__ __forceinline__ void ip_walk(const T (&rows)[NV][Elem<T>::E], int v0,
                 val[q][e] = right ? (A.o[K][q] + val[q][e]) : (val[q][e] + B.o[K][q]);
     }
 #pragma unroll
-    for (int l = 0; l < LOGRV; ++l) {
+    for (int l = 0; l < LOGV; ++l) {
         const int h = 1 << l;
 #pragma unroll
         for (int q = 0; q < RV; ++q) {

@@ -151,8 +151,10 @@ def test_operator_argument_errors(canon):
 def test_tile_geometry(canon):
     """Tile sizes the tests place their edge cases on: 4 waves x 64 lanes x
     16 vectors of 16 bytes for the 1-d scans, 8 vectors for double rows;
-    iterated_pairwise tiles of 64 / RV rows (register geometry) or of the
-    rows whose lane trees fit the LDS budget."""
+    iterated_pairwise tiles of the same 4096 E elements in the register
+    geometry (power-of-two L from E to 512 E: 64 / RV rows of wide rows,
+    4096 E / L rows of narrow ones) or of the rows whose lane trees fit the
+    LDS budget."""
     L = canon.lib()
     for pol, par in ((0, 0), (2, 1), (2, 16), (2, 256), (2, 65536), (1, 1)):
         assert L.canon_scan_tile_elems(pol, par, 8) == 8192
@@ -164,7 +166,11 @@ def test_tile_geometry(canon):
     assert L.canon_scan_tile_elems(1, 256, 4) == 64 * 256
     assert L.canon_scan_tile_elems(1, 3, 8) == 64 * 3         # LDS path, 64 rows
     assert L.canon_scan_tile_elems(1, 2048, 8) == 1 * 2048    # LDS path, 1 row
-    assert L.canon_scan_rows_tile_elems(1, 16, 8) == 64 * 16
+    assert L.canon_scan_tile_elems(1, 2, 4) == 64 * 2         # L < E: LDS path
+    for lanes in (2, 4, 8, 16, 32, 64):                        # narrow rows
+        assert L.canon_scan_tile_elems(1, lanes, 8) == 8192
+        assert L.canon_scan_tile_elems(1, 2 * lanes, 4) == 16384
+    assert L.canon_scan_rows_tile_elems(1, 16, 8) == 512 * 16
     assert L.canon_scan_tile_elems(7, 0, 8) == 0
     assert L.canon_scan_tile_elems(2, 12, 8) == 0
     assert L.canon_scan_tile_elems(0, 0, 2) == 0

@@ -60,7 +60,7 @@ def test_reduce(canon, dtype, op):
 @pytest.mark.parametrize("policy,param", [("pairwise", 0), ("block_dyadic", 2),
                                           ("block_dyadic", 16), ("block_dyadic", 256),
                                           ("block_dyadic", 8192), ("iterated_pairwise", 3),
-                                          ("iterated_pairwise", 128)])
+                                          ("iterated_pairwise", 16), ("iterated_pairwise", 128)])
 def test_scan(canon, dtype, op, policy, param):
     S = tile(dtype)
     x = data(op, 66 * S + 777, 82, dtype)

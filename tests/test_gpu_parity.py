@@ -368,6 +368,39 @@ def test_scan_iterated_pairwise_unaligned_register_geometry(canon, dtype, L):
                                                        "exclusive"), "exclusive")
 
 
+NARROW = ([(np.float64, L) for L in (2, 4, 8, 16, 32, 64)] +
+          [(np.float32, L) for L in (4, 8, 16, 32, 64, 128)])
+
+
+@pytest.mark.parametrize("dtype,L", NARROW)
+def test_scan_iterated_pairwise_narrow_rows(canon, dtype, L):
+    """Register geometry with rows narrower than a wave (L = E .. 32 E, a
+    wave holding 64 E / L row groups): past 64 tiles (node climbs to level
+    6 and up) with a ragged last row, a start off the 16-byte grid, in
+    place, the exclusive and include_initial kinds, and rows."""
+    S = scan_tile(dtype, "iterated_pairwise", L)
+    assert S == 4096 * (2 if dtype == np.float64 else 4)
+    n = 67 * S + L // 2 + 3
+    x = synth.generate(n + 1, "mixed_magnitude", 510 + L, dtype)
+    want = oracle.scan(x[:n], "iterated_pairwise", L)
+    assert_bit_exact(to_host(canon.scan(to_dev(x[:n]), "iterated_pairwise", L)), want, "aligned")
+    base = to_dev(x)
+    want1 = oracle.scan(x[1:], "iterated_pairwise", L)
+    assert_bit_exact(to_host(canon.scan(base[1:], "iterated_pairwise", L)), want1, "unaligned")
+    canon.scan(base[1:], "iterated_pairwise", L, out=base[1:])
+    assert_bit_exact(to_host(base[1:]), want1, "in place")
+    xd = to_dev(x[:n])
+    for kind in ("exclusive", "include_initial"):
+        got = to_host(canon.scan_with_init(xd, "iterated_pairwise", L, kind, 0.5))
+        assert_bit_exact(got, oracle.scan_with_init(x[:n], "iterated_pairwise", L, 0.5, kind),
+                         kind)
+    rows, cols, ld = 5, 2 * S + L + 1, 2 * S + 2 * L + 2
+    X = synth.generate(rows * ld, "mixed_magnitude", 520 + L, dtype).reshape(rows, ld)
+    got = to_host(canon.scan_rows(to_dev(X)[:, :cols], "iterated_pairwise", L))
+    for r in range(rows):
+        assert_bit_exact(got[r], oracle.scan(X[r, :cols], "iterated_pairwise", L), f"row {r}")
+
+
 # iterated_pairwise with L > 2048: the lanes of a row are cut into chunks of
 # 512 (their trees in LDS), the trees above the chunks come from the
 # workspace; tiles of 4 rows (double) or 8 rows (float).

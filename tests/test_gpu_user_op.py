@@ -104,8 +104,8 @@ def test_reduce(skew, canon, dtype):
 
 
 SCANS = [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16), ("block_dyadic", 256),
-         ("block_dyadic", 8192), ("iterated_pairwise", 3), ("iterated_pairwise", 128),
-         ("iterated_pairwise", 256)]
+         ("block_dyadic", 8192), ("iterated_pairwise", 3), ("iterated_pairwise", 16),
+         ("iterated_pairwise", 128), ("iterated_pairwise", 256)]
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
@@ -128,11 +128,12 @@ def test_scan(skew, canon, dtype, policy, param):
 # levels 3 and up): FullTile (pairwise; block_dyadic<2> in float),
 # SplitTile (block_dyadic<16>, and B of four tiles: one block over several
 # tiles), WideTile (block_dyadic<256>), the one-pass iterated_pairwise kernel
-# (L = 128 double, 256 both: pipelined and one tile per workgroup), the
-# three-kernel iterated_pairwise path (L = 3, 100).
+# (L = 128 double, 256 both: pipelined and one tile per workgroup; L = 16:
+# rows narrower than a wave), the three-kernel iterated_pairwise path
+# (L = 3, 100).
 LARGE_SCANS = [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16), ("block_dyadic", 256),
-               ("block_dyadic", 65536), ("iterated_pairwise", 128), ("iterated_pairwise", 256),
-               ("iterated_pairwise", 3), ("iterated_pairwise", 100)]
+               ("block_dyadic", 65536), ("iterated_pairwise", 16), ("iterated_pairwise", 128),
+               ("iterated_pairwise", 256), ("iterated_pairwise", 3), ("iterated_pairwise", 100)]
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
