@@ -679,8 +679,8 @@ def run_configs(torch, canon, synth, dev, reps=50, warmup=5):
     add("C4", "row scan block_dyadic<16>", "float64", Xn.size, 2 * Xn.nbytes,
         timed(lambda: canon.scan_rows(X, "block_dyadic", 16, out=Y)), ok, wit)
     del X, Y, rr
-    scan_cfg("C5", "scan_2e27_f64", (("iterated_pairwise", 128), ("block_dyadic", 16),
-                                     ("block_dyadic", 256)), False)
+    scan_cfg("C5", "scan_2e27_f64", (("iterated_pairwise", 128), ("iterated_pairwise", 16),
+                                     ("block_dyadic", 16), ("block_dyadic", 256)), False)
     scan_cfg("C5", "scan_2e28_f32", (("block_dyadic", 256),), False)
 
     def scan_init_cfg(cfg, name, cases):

@@ -305,7 +305,8 @@ canon_status_t canon_scan_noalloc_f64(const double* x, double* y, size_t n, int 
  *                                workspace size follows it
  *   CANON_SCHED_SPIN_LIMIT       polls of every bounded wait (single-pass
  *                                scans, the reduce's finish) before it gives
- *                                up and records the error word; for tests of
+ *                                up and records the error word (the scans'
+ *                                waits check it every 64 polls); for tests of
  *                                that path only: a small value makes waits
  *                                give up, and the output is then invalid
  *                                (default 2^20)

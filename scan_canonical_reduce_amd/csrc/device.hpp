@@ -395,25 +395,28 @@ __device__ __forceinline__ long spin_limit_of(const uint32_t* err)
     return v ? (long)v : kSpinLimit;
 }
 
-// Poll a published word until it is ready.  The wait is bounded: after
-// spin_limit_of(err) polls, or as soon as another wave has recorded an error, the
-// kernel's error word gets kErrSpin and -0.0 is returned, so that every wave
-// still runs to completion and the host can report the failure.
+// Poll a published word until it is ready.  The wait is bounded: after the
+// call's bound (spin_limit_of(err), at least 64 polls), or as soon as another
+// wave has recorded an error, the kernel's error word gets kErrSpin and -0.0
+// is returned, so that every wave still runs to completion and the host can
+// report the failure.  Both are checked every 64 polls only: the header words
+// share a cache line with the ticket counter, and loads of that line by every
+// short wait slowed the tickets of the whole grid.
 template <typename T>
 __device__ __forceinline__ T wait_word(uint64_t* slot, uint32_t* err)
 {
     const uint64_t nr = not_ready_word<T>();
     uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (w != nr) return unpack_word<T>(w);
-    const long limit = spin_limit_of(err);
-    long it = 0;
+    long it = 0, limit = kSpinLimit;
     while (w == nr) {
         ++it;
-        if (it > limit ||
-            ((it & 63) == 0 &&
-             __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-            __hip_atomic_fetch_or(err, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return neg_zero<T>();
+        if ((it & 63) == 0) {
+            if (it == 64) limit = spin_limit_of(err);
+            if (it > limit ||
+                __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                __hip_atomic_fetch_or(err, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return neg_zero<T>();
+            }
         }
         __builtin_amdgcn_s_sleep(2);
         w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

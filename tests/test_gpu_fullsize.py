@@ -123,3 +123,31 @@ def test_bench_step_scans_full_size(canon, policy, param):
     L = param if policy == "iterated_pairwise" else 1
     back = to_host(canon.reduce(xd, L, -0.0)).reshape(1)
     assert_bit_exact(to_host(y[-1:]), back, f"{policy} back == reduce")
+
+
+# Every register geometry of the one-pass iterated_pairwise kernel: narrow
+# rows (f64 L = 16, f32 L = 32), wide rows of 1, 2, 4 and 8 wave-wide vectors
+# (pipelined, and one tile per workgroup).  Its two forms (16-byte vector
+# loads and stores on an aligned copy, element loads and stores off the
+# 16-byte grid) are different kernels with different register use; on
+# 2^26 + 12345 elements they must agree on every element, and sampled
+# prefixes (literal form) and the back element (GPU reduce) pin the result.
+GEOMETRIES = ([(np.float64, L) for L in (16, 128, 256, 512, 1024)] +
+              [(np.float32, L) for L in (32, 256, 512, 1024, 2048)])
+
+
+@pytest.mark.parametrize("dtype,L", GEOMETRIES)
+def test_ip_register_geometries_aligned_and_unaligned(canon, dtype, L):
+    n = (1 << 26) + 12345
+    print(f"[fullsize] iterated_pairwise<{L}> {np.dtype(dtype).name} 2^26+12345, "
+          "aligned and unaligned", flush=True)
+    x = synth.generate(n + 1, "mixed_magnitude", 900 + L, dtype)
+    base = to_dev(x)
+    un = to_host(canon.scan(base[1:], "iterated_pairwise", L))
+    al = to_host(canon.scan(base[1:].clone(), "iterated_pairwise", L))
+    assert_bit_exact(un, al, "unaligned == aligned")
+    idx = _probes(n, k=0)
+    want = np.array([oracle.scan_prefix(x[1:], int(i), "iterated_pairwise", L) for i in idx])
+    assert_bit_exact(al[idx], want, "probes (literal)")
+    back = to_host(canon.reduce(base[1:], L, -0.0)).reshape(1)
+    assert_bit_exact(al[-1:], back, "scan back == reduce (GPU)")
