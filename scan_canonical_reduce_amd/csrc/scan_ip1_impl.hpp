@@ -12,11 +12,14 @@
 // workgroup waiting before it has published what others need:
 //   * each tile publishes its own per-lane totals (node (0, t)) as soon as
 //     its in-tile column scan is done (the tile's "front");
-//   * node (k+1, v) is formed by whichever of its two children finishes
-//     second: after publishing a child, the finishing tile counts it in the
-//     parent's arrival counter, and the tile that counts second reads the
-//     other child, adds (left child on the left) and publishes the parent,
-//     then tries the next level; a tile counting first stops there;
+//   * node (k+1, v) is formed by whichever of its two children arrives
+//     second: a tile counts itself in its level-1 parent's arrival counter
+//     when its loads are issued, and after publishing node (k, u), k >= 1,
+//     in that node's parent's counter; the tile that counts second reads
+//     the other child (waiting, if need be, for its words, which are
+//     published without waiting for this tile), adds (left child on the
+//     left) and publishes the parent, then tries the next level; a tile
+//     counting first stops there;
 //   * the tile's "back" then reads the nodes of its set bits, applies them,
 //     walks its rows' lane trees and stores.
 // Every node a tile waits for covers only tiles with smaller tickets, and
@@ -116,6 +119,7 @@ template <typename T, int LOGRV>
 struct Ip1Tile {
     T a[IpFast<T, LOGRV>::NV][Elem<T>::E];
     uint64_t item;
+    uint32_t before1;  // wave 3, lane 0: the level-1 arrival count before this tile's
 };
 
 template <typename T, int LOGRV>
@@ -147,6 +151,15 @@ __device__ __forceinline__ void ip1_load(Ip1Tile<T, LOGRV>& s, uint64_t item,
         ipf_load<T, LOGRV, false>(xs, c.cols, row0, c.w, c.lane, s.a);
     else
         ipf_load<T, LOGRV, true>(xs, c.cols, row0, c.w, c.lane, s.a);
+    // The tile's arrival at its level-1 parent is counted now, behind its
+    // loads: the count does not depend on the front, and its round trip
+    // then overlaps the loads' (a tile that counts second waits, in the
+    // climb, for its sibling's totals to be published, which they will be
+    // without waiting for this tile).
+    s.before1 = 0;
+    if (c.w == 3 && c.lane == 0 && 1 < c.lay->g.levels && (t >> 1) < c.sh->lvl.cnt[1])
+        s.before1 = __hip_atomic_fetch_add(ip1_counter(c.ws, *c.lay, c.sh->lvl, 1, seg, t >> 1),
+                                           1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Front: the lane prefixes inside the tile, the tile's totals published,
@@ -210,7 +223,9 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
             const uint64_t v = u >> 1;
             if (v >= c.sh->lvl.cnt[k + 1]) break;  // the parent covers tiles past the end
             uint32_t before = 0;
-            if (lane == 0)
+            if (k == 0)
+                before = s.before1;  // counted when the tile was loaded
+            else if (lane == 0)
                 before = __hip_atomic_fetch_add(ip1_counter(c.ws, lay, c.sh->lvl, k + 1, seg, v),
                                                 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             before = __builtin_amdgcn_readfirstlane(before);
