@@ -279,8 +279,8 @@ size_t canon_scan_rows_tile_elems(int policy, uint32_t param, size_t elem_size);
  * errors as canon_scan_f64, plus CANON_EUNSUPPORTED when the scan needs more
  * than the array, i.e. canon_scan_workspace_bytes(n, policy, param, 8) >
  * CANON_NOALLOC_SCRATCH_BYTES (pairwise and block_dyadic up to about 8.3e9
- * elements, iterated_pairwise<128> up to 2^23, iterated_pairwise<16> up to
- * about 3.3e7).  Every call on one
+ * elements, iterated_pairwise<128> up to about 3.3e7, iterated_pairwise<16>
+ * up to about 2.6e8).  Every call on one
  * device shares the array, which keeps the last call's contents: calls that
  * may overlap on one device (other streams, other host threads) race, and
  * the error word of canon_workspace_error is not available. */

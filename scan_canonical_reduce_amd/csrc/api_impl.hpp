@@ -209,10 +209,14 @@ inline bool is_ip(int policy, uint32_t param) { return policy == CANON_ITERATED_
 inline bool ip_single(const IpLayout& ip) { return ip.fast_logrv != kIpNoFast; }
 inline bool ip_fits(const IpLayout& ip) { return ip.nseg * ip.tps < (1ull << 31); }
 
-// Workspace of an iterated_pairwise scan: the largest of its possible plans
-// (16-byte aligned or not).
+// Workspace of an iterated_pairwise scan: the one-pass plan of the register
+// geometry when it applies (it runs at any alignment), else the largest of
+// the three-kernel plans (16-byte aligned or not).
 inline size_t ip_ws(uint64_t nseg, uint64_t cols, uint32_t L, size_t es)
 {
+    const IpLayout reg = make_ip_layout(nseg, cols, L, es, true);
+    if (ip_single(reg) && ip_fits(reg))
+        return round_up(make_ip_single_layout(reg).total_words * 8, kWsAlign);
     size_t need = 0;
     for (int al = 0; al < 2; ++al) {
         const IpLayout ip = make_ip_layout(nseg, cols, L, es, al != 0);

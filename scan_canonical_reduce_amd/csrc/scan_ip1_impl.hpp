@@ -1,5 +1,6 @@
 // Canonical scan, policy iterated_pairwise<L>, in one pass over the input
-// (gfx950, fast geometry: L = 64 * E * RV, 16-byte aligned rows).
+// (gfx950, register geometry: L = E * 2^j lanes, E <= L <= 512 E; element
+// loads and stores where rows are off the 16-byte grid).
 //
 // Expression and evaluation inside a tile: as in scan_ip.hip (canonical-
 // reduce README, P4229R0 "Summary"; P4016R0 "Key Design Points").  Tile t

@@ -53,7 +53,7 @@ struct IpFast {
 };
 
 // butterfly partner value of `v` held by lane ^ 2^K (VALU lane moves: the
-// row trees are a chain of six dependent exchanges per row)
+// row trees are a chain of log2 TPR dependent exchanges per row)
 template <int K, typename T>
 __device__ __forceinline__ T xor_lane(T v)
 {

@@ -61,6 +61,11 @@ def test_workspace_sizes(canon):
     assert L.canon_scan_workspace_bytes(1 << 20, 2, 3, 8) == 0  # B not a power of two
     assert L.canon_scan_workspace_bytes(0, 0, 0, 8) == 0
     assert L.canon_scan_workspace_bytes(1 << 20, 1, 128, 8) > 0       # iterated_pairwise nodes
+    # iterated_pairwise with power-of-two L from E to 512 E runs in one pass at
+    # any alignment: its workspace is that pass's (L node words per tile and
+    # level, f64 2^28: 32768 tiles), not the three-kernel plan's
+    assert 64 << 20 < L.canon_scan_workspace_bytes(1 << 28, 1, 128, 8) < 65 << 20
+    assert 8 << 20 < L.canon_scan_workspace_bytes(1 << 28, 1, 16, 8) < (8 << 20) + (1 << 18)
     assert L.canon_scan_rows_workspace_bytes(16, 4096, 2, 16, 8) == 0  # block_dyadic rows: none
     assert L.canon_scan_rows_workspace_bytes(16, 4096, 1, 16, 8) > 0
 
