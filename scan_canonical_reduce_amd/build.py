@@ -17,8 +17,8 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libcanon")
 
 SOURCES = [
     "api.cpp", "reduce.hip", "scan.hip", "scan_with_init.hip", "scan_wide.hip",
-    "scan_wide_init.hip", "scan_rows.hip", "scan_ip.hip", "scan_ip1.hip",
-    "scan_ip1_narrow_f64.hip", "scan_ip1_narrow_f32.hip",
+    "scan_wide_init.hip", "scan_lane.hip", "scan_lane_init.hip", "scan_rows.hip", "scan_ip.hip",
+    "scan_ip1.hip", "scan_ip1_narrow_f64.hip", "scan_ip1_narrow_f32.hip",
     "ops_mul_f64.hip", "ops_mul_f32.hip", "ops_min_f64.hip", "ops_min_f32.hip",
     "ops_max_f64.hip", "ops_max_f32.hip", "scan_noalloc.cpp",
 ]

@@ -23,6 +23,9 @@
                                                  hipStream_t);                                     \
     template hipError_t launch_wide<V, true>(const V*, V*, uint64_t, int, bool, uint64_t*,        \
                                              const ScanLayout&, const ScanOut<V>&, hipStream_t);   \
+    template hipError_t launch_lane_block<V, true>(const V*, V*, uint64_t, int, bool, uint64_t*,  \
+                                                   const ScanLayout&, const ScanOut<V>&,           \
+                                                   hipStream_t);                                   \
     template hipError_t launch_scan_rows<V, false, false>(const V*, uint64_t, V*, uint64_t,       \
                                                           uint64_t, uint64_t, bool, int, bool,     \
                                                           const ScanOut<V>*, hipStream_t);         \

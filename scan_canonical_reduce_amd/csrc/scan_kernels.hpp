@@ -397,7 +397,9 @@ struct BlockScan {
     }
 };
 
-// Block_dyadic with B >= E.  With n = qB + r, the value at a block's
+// Block_dyadic with B >= E (the block sizes that LaneBlockTile and WideTile
+// do not take: blocks larger than a wave's span, B >= tile, and float blocks
+// of one lane's vector).  With n = qB + r, the value at a block's
 // interior is C + W, C = PW(x[0..qB)) the pairwise value at the end of the
 // previous block, W the pairwise prefix inside the block; at a block end it
 // is the pairwise value there.  So the levels above b reduce to one pairwise
@@ -700,6 +702,138 @@ struct WideTile {
     }
 };
 
+// block_dyadic with blocks inside one vector row of a wave: B = E 2^Q,
+// 0 <= Q <= 5, so a block is the vectors of LPB = 2^Q consecutive lanes of
+// one row (64 / LPB blocks per row).  The tile network runs the levels <= b
+// (inside a vector and across the block's lanes): W, the pairwise prefix
+// inside the block, in every element, and the block's total at its last
+// lane.  Each lane then carries one value per vector row, cur[u], through the
+// pairwise scan of the block totals: across lane groups of 2 LPB .. 64 lanes,
+// across the thread's rows, across the 4 waves (one barrier), lower levels
+// first, each level adding the end of the lower half on the left, the same
+// for every lane of a block.  At a block's last lane cur[u] is then the
+// pairwise value of the tile's blocks up to that block.  The back adds the
+// tile-level nodes on the left of every cur[u] and of the value before the
+// wave; an element outputs the value at the end of the previous block + W,
+// a block end its own block's value.  No LDS pass over the block totals and
+// one barrier per tile besides the look-back's.
+template <typename T, bool ALIGNED, int LOGV, int Q, bool OUTX>
+struct LaneBlockTile {
+    using ST = ScanTile<T, 0, LOGV>;
+    static constexpr int E = ST::E;
+    static constexpr int V = ST::V;
+    static constexpr int LOG_S = ST::LOG_S;
+    static constexpr int LPB = 1 << Q;  // lanes per block
+    static_assert(Q >= 0 && Q <= 5, "blocks inside one vector row");
+    static constexpr int kMinWavesPerEu = 1;
+    struct State {
+        ST st;
+        T cur[V];  // per row u: at the block's last lane, the blocks' pairwise value up to it
+        T wpre;    // pairwise value of the tile's blocks before this wave (-0.0 for wave 0)
+    };
+
+    static __device__ __forceinline__ uint64_t g0(uint64_t t, const ScanCtx<T>& c)
+    {
+        return (t << LOG_S) + ((uint64_t)c.w << ST::LOG_WSPAN) + (uint64_t)c.lane * E;
+    }
+    static __device__ __forceinline__ void load(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        s.st.template load<ALIGNED>(c.x, c.n, g0(t, c));
+    }
+
+    static __device__ __forceinline__ T front(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        // levels <= b: W in every element
+        s.st.slot_levels();
+        if constexpr (Q > 0) s.st.template lane_level<0>(c.lane);
+        if constexpr (Q > 1) s.st.template lane_level<1>(c.lane);
+        if constexpr (Q > 2) s.st.template lane_level<2>(c.lane);
+        if constexpr (Q > 3) s.st.template lane_level<3>(c.lane);
+        if constexpr (Q > 4) s.st.template lane_level<4>(c.lane);
+#pragma unroll
+        for (int u = 0; u < V; ++u) s.cur[u] = s.st.v[u][E - 1];
+        // block levels across lane groups (sources: the last lanes of blocks)
+#define CANON_LB_LANE(K)                                                              \
+    if constexpr ((K) >= Q) {                                                         \
+        _Pragma("unroll") for (int u = 0; u < V; ++u)                                 \
+        {                                                                             \
+            const T src = from_lower_half_end<(1 << (K))>(s.cur[u]);                  \
+            s.cur[u] = (((c.lane >> (K)) & 1) ? src : neg_zero<T>()) + s.cur[u];      \
+        }                                                                             \
+    }
+        CANON_LB_LANE(0)
+        CANON_LB_LANE(1)
+        CANON_LB_LANE(2)
+        CANON_LB_LANE(3)
+        CANON_LB_LANE(4)
+        CANON_LB_LANE(5)
+#undef CANON_LB_LANE
+        // block levels across the thread's rows (sources: lane 63 of a row)
+#pragma unroll
+        for (int l = 0; l < LOGV; ++l) {
+            const int H = 1 << l;
+#pragma unroll
+            for (int u = 0; u < V; ++u)
+                if (u & H) s.cur[u] = readlane(s.cur[(u & ~(2 * H - 1)) + H - 1], 63) + s.cur[u];
+        }
+        const T wt = readlane(s.cur[V - 1], 63);  // complete tree of the wave
+        if (c.lane == 0) c.sh->tot[c.w] = wt;
+        __syncthreads();
+        const T t0 = c.sh->tot[0], t1 = c.sh->tot[1], t2 = c.sh->tot[2], t3 = c.sh->tot[3];
+        const T t01 = t0 + t1;
+        const T total = t01 + (t2 + t3);
+        if (threadIdx.x == 0) publish(c.ws + c.lay->tiles_off + t, total);
+        if (c.w & 1) {
+            const T v = (c.w & 2) ? t2 : t0;
+#pragma unroll
+            for (int u = 0; u < V; ++u) s.cur[u] = v + s.cur[u];
+        }
+        if (c.w & 2) {
+#pragma unroll
+            for (int u = 0; u < V; ++u) s.cur[u] = t01 + s.cur[u];
+        }
+        s.wpre = c.w == 0 ? neg_zero<T>() : c.w == 1 ? t0 : c.w == 2 ? t01 : t01 + t2;
+        return total;
+    }
+
+    static __device__ __forceinline__ void back(State& s, uint64_t t, const ScanCtx<T>& c)
+    {
+        const T* h = c.sh->lb.h;
+        T cw = s.wpre;
+        for (int k = 0; k < kMaxLevels && (t >> k) != 0; ++k)
+            if ((t >> k) & 1) {
+#pragma unroll
+                for (int u = 0; u < V; ++u) s.cur[u] = h[k] + s.cur[u];
+                cw = h[k] + cw;
+            }
+        const int first = c.lane & ~(LPB - 1);  // the block's first lane
+        const bool bend = (c.lane & (LPB - 1)) == LPB - 1;
+        // the value at the end of the previous block: the last lane of the
+        // block before in the row, else lane 63 of the row before, else cw
+        // (before the wave's first block); every lane takes part in the moves
+        auto fin = [&](int u, T(&o)[E]) {
+            const T inrow = shfl_idx(s.cur[u], first - 1);
+            const T prow = u > 0 ? readlane(s.cur[u > 0 ? u - 1 : 0], 63) : cw;
+            const T prev = first > 0 ? inrow : prow;
+#pragma unroll
+            for (int e = 0; e < E - 1; ++e) o[e] = prev + s.st.v[u][e];
+            o[E - 1] = bend ? s.cur[u] : prev + s.st.v[u][E - 1];
+        };
+        if constexpr (OUTX) {
+            // the element before the wave's first one ends the previous
+            // wave's last block (or the tile before): its value is cw
+            s.st.template emit_known<ALIGNED>(c.y, c.n, g0(t, c), c.init, c.kind, cw, c.lane, fin);
+        } else {
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                T o[E];
+                fin(u, o);
+                s.st.template put<ALIGNED>(c.y, c.n, g0(t, c), u, o);
+            }
+        }
+    }
+};
+
 // One pipeline step of a persistent workgroup: tile t is in `cur` with its
 // front done (total published).  Takes the next ticket and issues its loads
 // into `nxt`, reads t's look-back words afresh right behind them, runs the
@@ -812,6 +946,50 @@ template <typename T, bool OUTX>
 hipError_t launch_wide(const T* x, T* y, uint64_t n, int b_log, bool aligned, uint64_t* ws,
                        const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s);
 
+// The LaneBlockTile kernels, in their own translation units (scan_lane.hip,
+// scan_lane_init.hip): b_log from LOGE to LOGE + 5.  Blocks of one lane's
+// vector (b_log = LOGE) only where a vector holds two values: with four, the
+// six lane levels of the block scan on 16 rows spill (f32 B = 4 at 2^28:
+// 613 us against 452 us for SplitTile).
+template <typename T>
+constexpr bool kLaneOneLaneBlocks = Elem<T>::E == 2;
+template <typename T, bool OUTX>
+hipError_t launch_lane_block(const T* x, T* y, uint64_t n, int b_log, bool aligned, uint64_t* ws,
+                             const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s);
+
+template <typename T, bool OUTX>
+hipError_t launch_lane_block_impl(const T* x, T* y, uint64_t n, int b_log, bool aligned,
+                                  uint64_t* ws, const ScanLayout& lay, const ScanOut<T>& out,
+                                  hipStream_t s)
+{
+    constexpr int LOGV = scan_log_v<T>();
+#define CANON_LANE_CASE(QQ)                                                                      \
+    case QQ:                                                                                     \
+        if (aligned)                                                                             \
+            return launch_k<LaneBlockTile<T, true, LOGV, QQ, OUTX>>(x, y, n, b_log, ws, lay, 0,  \
+                                                                    out, s);                     \
+        return launch_k<LaneBlockTile<T, false, LOGV, QQ, OUTX>>(x, y, n, b_log, ws, lay, 0,     \
+                                                                 out, s);
+    switch (b_log - Elem<T>::LOGE) {
+        case 0:
+            if constexpr (kLaneOneLaneBlocks<T>) {
+                if (aligned)
+                    return launch_k<LaneBlockTile<T, true, LOGV, 0, OUTX>>(x, y, n, b_log, ws, lay,
+                                                                           0, out, s);
+                return launch_k<LaneBlockTile<T, false, LOGV, 0, OUTX>>(x, y, n, b_log, ws, lay, 0,
+                                                                        out, s);
+            }
+            return hipErrorInvalidValue;
+        CANON_LANE_CASE(1)
+        CANON_LANE_CASE(2)
+        CANON_LANE_CASE(3)
+        CANON_LANE_CASE(4)
+        CANON_LANE_CASE(5)
+        default: return hipErrorInvalidValue;
+    }
+#undef CANON_LANE_CASE
+}
+
 template <typename T, bool OUTX>
 hipError_t launch_wide_impl(const T* x, T* y, uint64_t n, int b_log, bool aligned, uint64_t* ws,
                             const ScanLayout& lay, const ScanOut<T>& out, hipStream_t s)
@@ -851,6 +1029,8 @@ static hipError_t launch_split(const T* x, T* y, uint64_t n, int b_log, bool ali
     constexpr int LOG_WSPAN = LOG_S - 2;
     if (b_log >= Elem<T>::LOGE + 6 && b_log <= LOG_WSPAN)
         return launch_wide<T, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
+    if (b_log < Elem<T>::LOGE + 6 && b_log >= Elem<T>::LOGE + (kLaneOneLaneBlocks<T> ? 0 : 1))
+        return launch_lane_block<T, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
     const int lm = LOG_S - b_log > 8 ? LOG_S - b_log - 8 : 0;
     if (lm <= 2) return launch_split_k<T, false, 2, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
     return launch_split_k<T, false, 4, OUTX>(x, y, n, b_log, aligned, ws, lay, out, s);
