@@ -126,14 +126,17 @@ def test_scan(skew, canon, dtype, policy, param):
 # Every kernel family past 64 tiles (the 64-tile group rebuild, climbs to
 # node levels 7 and 8, the right-spine composition, iterated_pairwise node
 # levels 3 and up): FullTile (pairwise; block_dyadic<2> in float),
-# SplitTile (block_dyadic<16>, and B of four tiles: one block over several
-# tiles), WideTile (block_dyadic<256>), the one-pass iterated_pairwise kernel
-# (L = 128 double, 256 both: pipelined and one tile per workgroup; L = 16:
-# rows narrower than a wave), the three-kernel iterated_pairwise path
-# (L = 3, 100).
-LARGE_SCANS = [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 16), ("block_dyadic", 256),
-               ("block_dyadic", 65536), ("iterated_pairwise", 16), ("iterated_pairwise", 128),
-               ("iterated_pairwise", 256), ("iterated_pairwise", 3), ("iterated_pairwise", 100)]
+# LaneBlockTile (blocks inside one vector row: block_dyadic<2> in double,
+# <4> in double, <16>), SplitTile (block_dyadic<4> in float, <4096> in
+# double: blocks larger than a wave's span, and B of four tiles: one block
+# over several tiles), WideTile (block_dyadic<256>), the one-pass
+# iterated_pairwise kernel (L = 128 double, 256 both: pipelined and one tile
+# per workgroup; L = 16: rows narrower than a wave), the three-kernel
+# iterated_pairwise path (L = 3, 100).
+LARGE_SCANS = [("pairwise", 0), ("block_dyadic", 2), ("block_dyadic", 4), ("block_dyadic", 16),
+               ("block_dyadic", 256), ("block_dyadic", 4096), ("block_dyadic", 65536),
+               ("iterated_pairwise", 16), ("iterated_pairwise", 128), ("iterated_pairwise", 256),
+               ("iterated_pairwise", 3), ("iterated_pairwise", 100)]
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
