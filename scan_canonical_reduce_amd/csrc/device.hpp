@@ -385,6 +385,64 @@ __device__ __forceinline__ void publish(uint64_t* slot, T v)
     __hip_atomic_store(slot, pack_word(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The words of values v[0 .. N) published to slot[0 .. N) (16-byte aligned,
+// N even) two at a time, each pair in one 16-byte store with the coherence of
+// a relaxed agent-scope atomic store (sc1: written through this XCD's L2 to
+// memory).  One store per pair, where a store per word would leave every
+// written line half-filled twice: the lanes of a wave then write whole lines.
+// An aligned 16-byte store never splits an 8-byte word, so a reader's 64-bit
+// load sees a word either not ready or whole.  A store of more than 8 bytes
+// must be followed by two wait states before a VALU instruction may write
+// its data registers (the compiler inserts them after its own stores, not
+// after one written in asm): the s_nop 1 in the same asm block.
+template <int N, typename T>
+__device__ __forceinline__ void publish_pairs(uint64_t* slot, const T (&v)[N])
+{
+    static_assert(N % 2 == 0, "pairs of words");
+    using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+        const uint64_t a = pack_word(v[i]), b = pack_word(v[i + 1]);
+        const u32x4 d = {(unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32)};
+        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1"
+                     :
+                     : "v"(slot + i), "v"(d)
+                     : "memory");
+    }
+}
+
+// Words slot[q][0 .. N) (each 16-byte aligned, N even) read two at a time,
+// each pair in one 16-byte load with the coherence of a relaxed agent-scope
+// atomic load (sc1: from memory, not this XCD's L2): the counterpart of
+// publish_pairs, so that the lanes of a wave read each line once.  Every load
+// is issued, then one wait for all of them; each result register is then
+// passed through an empty asm, so that nothing uses (or reuses) it before the
+// wait.  The loads are as ordered as the atomic loads they replace: relaxed.
+template <int Q, int N>
+__device__ __forceinline__ void load_pairs(const uint64_t* const (&slot)[Q], uint64_t (&w)[Q][N])
+{
+    static_assert(N % 2 == 0, "pairs of words");
+    using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+    u32x4 d[Q][N / 2];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i)
+            asm volatile("global_load_dwordx4 %0, %1, off sc1"
+                         : "=&v"(d[q][i])
+                         : "v"(slot[q] + 2 * i)
+                         : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            asm volatile("" : "+v"(d[q][i]));
+            w[q][2 * i] = ((uint64_t)d[q][i][1] << 32) | d[q][i][0];
+            w[q][2 * i + 1] = ((uint64_t)d[q][i][3] << 32) | d[q][i][2];
+        }
+}
+
 // The bound of a wait: header word 2 of the workspace whose error word is
 // `err` (its first 32 bits), written by the call's init kernel (0: the
 // default, kSpinLimit).

@@ -93,7 +93,8 @@ inline IpLayout make_ip_layout(uint64_t nseg, uint64_t cols, uint32_t L, size_t 
 // segment count), in 64-bit words from the workspace start:
 //   word 0: error word (low 32 bits); word 1: ticket counter (low 32 bits);
 //   [woff[k], +nseg * cnt[k] * L): node level k, one published word per lane
-//     (node (k, u) of segment s at woff[k] + (s * cnt[k] + u) * L);
+//     (node (k, u) of segment s at woff[k] + (s * cnt[k] + u) * L, its words
+//     in pairs of adjacent columns: IpFast::wcol);
 //   [cbase, ...): 32-bit arrival counters, level k >= 1 at coff[k] (in
 //     32-bit units from cbase): one per node, counting its finished children.
 struct IpSingleLayout {

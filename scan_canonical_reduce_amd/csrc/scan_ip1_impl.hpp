@@ -213,12 +213,16 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
         };
         T cur[RV][E];
 #pragma unroll
-        for (int q = 0; q < RV; ++q)
+        for (int q = 0; q < RV; ++q) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                cur[q][e] = a[(RW - 1) * RV + q][e];
-                if (last) publish(word(0, t, F::col(q, lane) + e), cur[q][e]);
-            }
+            for (int e = 0; e < E; ++e) cur[q][e] = a[(RW - 1) * RV + q][e];
+            if (last)
+#pragma unroll
+                for (int j = 0; j < F::NP; ++j) {
+                    const T pv[2] = {cur[q][2 * j], cur[q][2 * j + 1]};
+                    publish_pairs(word(0, t, F::wcol(q, j, lane)), pv);
+                }
+        }
         uint64_t u = t;
         for (int k = 0; k + 1 < lay.g.levels; ++k) {
             const uint64_t v = u >> 1;
@@ -232,23 +236,30 @@ __device__ __forceinline__ void ip1_front(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, 
             before = __builtin_amdgcn_readfirstlane(before);
             if (before == 0) break;  // the sibling completes the parent
             if (last) {
-                // the sibling's words: all reads issued, then each waited for
-                uint64_t sw[RV][E];
+                // the sibling's words: all reads issued, then waited for
+                const uint64_t* sp[RV * F::NP];
 #pragma unroll
                 for (int q = 0; q < RV; ++q)
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        sw[q][e] = __hip_atomic_load(word(k, u ^ 1, F::col(q, lane) + e),
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int j = 0; j < F::NP; ++j)
+                        sp[q * F::NP + j] = word(k, u ^ 1, F::wcol(q, j, lane));
+                uint64_t sw[RV * F::NP][2];
+                load_pairs(sp, sw);
 #pragma unroll
-                for (int q = 0; q < RV; ++q)
+                for (int q = 0; q < RV; ++q) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        const uint64_t col = F::col(q, lane) + e;
-                        const T sib = ready_or_wait<T>(sw[q][e], word(k, u ^ 1, col), c.err);
+                        const uint64_t col = F::wcol(q, e / 2, lane) + (e & 1);
+                        const T sib = ready_or_wait<T>(sw[q * F::NP + e / 2][e & 1],
+                                                       word(k, u ^ 1, col), c.err);
                         cur[q][e] = (u & 1) ? sib + cur[q][e] : cur[q][e] + sib;
-                        publish(word(k + 1, v, col), cur[q][e]);
                     }
+#pragma unroll
+                    for (int j = 0; j < F::NP; ++j) {
+                        const T pv[2] = {cur[q][2 * j], cur[q][2 * j + 1]};
+                        publish_pairs(word(k + 1, v, F::wcol(q, j, lane)), pv);
+                    }
+                }
             }
             u = v;
         }
@@ -282,7 +293,8 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         return ip1_word(c.ws, c.sh->lvl, lay.g.L, k, seg, (t >> k) - 1, (uint64_t)col);
     };
     // The node words of up to NB set bits at a time, spread over the reading
-    // threads (word idx of a batch: node idx / L, lane idx % L), every read
+    // threads (word idx of a batch: node idx / L, word idx % L of the node in
+    // its published order, staged in that order), every read
     // issued before any is waited for, then staged in LDS.
     T b[RV][E];
 #pragma unroll
@@ -319,8 +331,15 @@ __device__ __forceinline__ void ip1_back(Ip1Tile<T, LOGRV>& s, const Ip1Ctx<T, L
         for (int m = 0; m < nb; ++m) {
 #pragma unroll
             for (int q = 0; q < RV; ++q) {
+                // the node's words are staged in their published order
                 T hv[E];
-                lds_load_vec(&c.sh->h[m * F::L + F::col(q, lane)], hv);
+                if constexpr (F::NP == 1) {
+                    lds_load_vec(&c.sh->h[m * F::L + F::wcol(q, 0, lane)], hv);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        hv[e] = c.sh->h[m * F::L + F::wcol(q, e / 2, lane) + (e & 1)];
+                }
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
 #pragma unroll

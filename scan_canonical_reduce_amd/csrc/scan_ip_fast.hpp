@@ -50,6 +50,15 @@ struct IpFast {
     {
         return ((uint64_t)w * G + group(lane)) * RW + r;
     }
+    // Index inside a published node (L words, one a column) of the word of
+    // value 2j of vector q of this thread's row; value 2j+1's word follows
+    // it.  Pair-major, so that one 16-byte store or load per pair covers
+    // whole lines across the lanes; with two values a vector it is col.
+    static constexpr int NP = E / 2;  // pairs a vector
+    __device__ static uint64_t wcol(int q, int j, int lane)
+    {
+        return (((uint64_t)q * NP + j) * TPR + sub(lane)) * 2;
+    }
 };
 
 // butterfly partner value of `v` held by lane ^ 2^K (VALU lane moves: the
