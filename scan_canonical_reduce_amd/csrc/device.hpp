@@ -104,6 +104,15 @@ template <typename T> __device__ __forceinline__ T neg_zero() { return Absent<T>
 // Keeps a value in a VGPR at this point (an empty asm operand): the compiler
 // may not move the operations that produce it past here.
 template <typename T> __device__ __forceinline__ void pin_reg(T& x) { asm volatile("" : "+v"(x)); }
+// A copy of the per-lane value v that the compiler cannot relate to v: the
+// addresses of a tile's stores derived from it are computed where they are
+// used, instead of being kept live from the tile's loads (one 64-bit address
+// per vector of the thread).
+template <typename T> __device__ __forceinline__ T fresh_copy(T v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
 template <typename B, class Op> __device__ __forceinline__ void pin_reg(OpVal<B, Op>& x)
 {
     asm volatile("" : "+v"(x.v));

@@ -54,11 +54,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_rows(const T* x, uint64_t
                         else pc = s_stack[k] + pc;
                     }
                 }
+            // the stores' offset as a fresh copy: otherwise the compiler keeps
+            // the address of every vector from its load to its store (f64
+            // block_dyadic: 104 VGPRs and 4 waves per SIMD, against 90 and 5)
+            const uint64_t gs = fresh_copy(g0);
             if constexpr (OUTX)
-                st.template emit<ALIGNED>(yr, cols, g0, init, kind, pc + pw, s_wend, w, lane,
+                st.template emit<ALIGNED>(yr, cols, gs, init, kind, pc + pw, s_wend, w, lane,
                                           [&](int u, T(&o)[ST::E]) { st.final_vec(u, o); });
             else
-                st.template store<ALIGNED>(yr, cols, g0);
+                st.template store<ALIGNED>(yr, cols, gs);
             __syncthreads();  // everyone has read s_tot and s_stack
             if (threadIdx.x == 0) {
                 T acc = tile_total;
